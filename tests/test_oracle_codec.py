@@ -1,0 +1,224 @@
+"""Pins of the oracle's INT2 codec and rounding helpers (CPU only).
+
+Each test ties the oracle to something outside itself: a library conversion,
+a hand-derived example, exact rational arithmetic, brute force over the four
+codes, or a property any correct min/max quantiser has.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec
+
+
+def _bf16(x):
+    return codec.bf16_to_f32((np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16))
+
+
+# ------------------------------------------------------------- rounding ----
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(200000).astype(np.float32) * np.float32(100)
+    # force exact ties (low half 0x8000) on both even and odd kept patterns
+    u = x.view(np.uint32).copy()
+    u[:5000] = (u[:5000] & 0xFFFF0000) | 0x8000
+    x = u.view(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(codec.f32_to_bf16_rne(x), ref)
+
+
+def test_bf16_rne_known_values():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even pattern is 1.0 (0x3F80)
+    assert codec.f32_to_bf16_rne(np.float32(1 + 2 ** -8))[()] == 0x3F80
+    # 1 + 3*2^-8 is a tie between 1+2^-7 (odd) and 1+2^-6 (even): 0x3F82
+    assert codec.f32_to_bf16_rne(np.float32(1 + 3 * 2 ** -8))[()] == 0x3F82
+    assert codec.f32_to_bf16_rne(np.float32(-2.0))[()] == 0xC000
+
+
+def test_fp16_matches_torch_and_known_values():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(100000) * 10,
+                        rng.standard_normal(20000) * 1e-6,        # subnormal range
+                        rng.uniform(-60000, 60000, 20000)]).astype(np.float32)
+    ref = torch.from_numpy(x).half().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(codec.f32_to_f16(x).view(np.uint16), ref)
+    known = {1.0 / 3.0: 0x3555, 2.0 ** -24: 0x0001, 65504.0: 0x7BFF, -1.5: 0xBE00, 0.0: 0x0000}
+    for v, bits in known.items():
+        assert codec.f32_to_f16(np.float32(v)).view(np.uint16)[()] == bits
+
+
+# ------------------------------------------------------------ quantiser ----
+def test_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "int2_worked_example.json")))
+    x = np.array(g["values"], np.float32)
+    c, s16, m16 = codec.quantize_groups(x)
+    assert s16.view(np.uint16)[()] == g["scale_fp16_bits"]
+    assert m16.view(np.uint16)[()] == g["min_fp16_bits"]
+    assert c.tolist() == g["codes"]
+    assert c.tolist() != g["codes_if_ties_round_away_from_zero"]
+
+
+def test_constant_group():
+    x = np.full(32, _bf16(0.7)[()], np.float32)
+    c, s16, m16 = codec.quantize_groups(x)
+    assert s16.astype(np.float32) == 0 and s16.view(np.uint16) == 0
+    assert m16 == np.float16(x[0])
+    assert not c.any()
+
+
+def test_signed_zero_is_canonical():
+    x = np.zeros(32, np.float32)
+    x[::2] = -0.0
+    c, s16, m16 = codec.quantize_groups(x)
+    assert s16.view(np.uint16) == 0 and m16.view(np.uint16) == 0 and not c.any()
+    x = np.full(32, -0.0, np.float32)
+    c, s16, m16 = codec.quantize_groups(x)
+    assert s16.view(np.uint16) == 0 and m16.view(np.uint16) == 0
+
+
+def _groups(rng, n, scale=1.0, offset=0.0):
+    return _bf16(rng.standard_normal((n, 32)) * scale + offset)
+
+
+@pytest.mark.parametrize("scale,offset", [(1.0, 0.0), (10.0, 0.0), (1e-3, 5.0), (300.0, -1e3)])
+def test_extremes_and_range(scale, offset):
+    rng = np.random.default_rng(2)
+    x = _groups(rng, 20000, scale, offset)
+    c, s16, m16 = codec.quantize_groups(x)
+    assert c.max() <= 3
+    ok = s16.astype(np.float32) > 0
+    rows = np.arange(len(x))
+    assert (c[rows, x.argmin(1)][ok] == 0).all()
+    assert (c[rows, x.argmax(1)][ok] == 3).all()
+
+
+@pytest.mark.parametrize("scale,offset", [(1.0, 0.0), (8.0, 0.0), (0.01, 3.0), (50.0, 200.0)])
+def test_error_bound(scale, offset):
+    """|x - (c*s + m)| <= s/2 plus the fp16 rounding of s and m (exact arithmetic)."""
+    rng = np.random.default_rng(3)
+    x = _groups(rng, 20000, scale, offset).astype(np.float64)
+    c, s16, m16 = codec.quantize_groups(x.astype(np.float32))
+    s = s16.astype(np.float64)
+    m = m16.astype(np.float64)
+    s_exact = (x.max(1) - x.min(1)) / 3
+    deq = c * s[:, None] + m[:, None]
+    slack = 3 * np.abs(s - s_exact) + np.abs(m - x.min(1)) + 1e-6 * np.abs(x).max(1)
+    assert (np.abs(x - deq).max(1) <= s / 2 + slack).all()
+
+
+def test_codes_are_nearest_grid_point():
+    """Away from ties, each code is the argmin over 0..3 of |x - (m + c*s)|
+    on the stored fp16 grid (exact rational distances)."""
+    rng = np.random.default_rng(4)
+    x = _groups(rng, 3000, 2.0, 0.3)
+    c, s16, m16 = codec.quantize_groups(x)
+    checked = 0
+    for g in range(len(x)):
+        s = Fraction(float(s16[g]))
+        m = Fraction(float(m16[g]))
+        if s == 0:
+            continue
+        for i in range(32):
+            xi = Fraction(float(x[g, i]))
+            d = [abs(xi - (m + k * s)) for k in range(4)]
+            best = min(range(4), key=lambda k: d[k])
+            second = sorted(d)[1]
+            if second - d[best] > s / 1000:
+                assert c[g, i] == best
+                checked += 1
+    assert checked > 90000
+
+
+def test_grouping_orientation():
+    """K groups run over tokens of one channel, V groups over channels of one token."""
+    w, d = 64, 64
+    t = np.arange(w)[:, None]
+    ch = np.arange(d)[None, :]
+    # channel d of K spans [0, 31*(d+1)/64] inside every 32-token group
+    k = _bf16(((t % 32) * (ch + 1) / 64.0).astype(np.float32))
+    # token t of V spans [0, 31*(t+1)/64] inside every 32-channel group
+    v = _bf16(((ch % 32) * (t + 1) / 64.0).astype(np.float32))
+    to_bits = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+    e = codec.quantize_window(to_bits(k), to_bits(v))
+    assert e["Ks"].shape == (w // 32, d) and e["Vs"].shape == (w, d // 32)
+    for j in range(w // 32):
+        for dd in range(d):
+            top = float(k[32 * j + 31, dd])
+            assert e["Ks"][j, dd] == np.float16(np.float32(top) / np.float32(3))
+            assert e["Km"][j, dd] == 0
+    for tt in range(w):
+        for j in range(d // 32):
+            top = float(v[tt, 32 * j + 31])
+            assert e["Vs"][tt, j] == np.float16(np.float32(top) / np.float32(3))
+    # codes of the ramp: position i of a group maps to round(3*i/31)
+    expect = np.rint(np.arange(32) * 3 / 31.0)
+    assert np.array_equal(e["Kc"][:32, 5], expect)
+    assert np.array_equal(e["Vc"][7, 32:64], expect)
+
+
+def test_pack_roundtrip_and_bit_order():
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 4, (128, 128)).astype(np.uint8)
+    p = codec.pack_codes(c)
+    assert p.shape == (128, 32)
+    assert np.array_equal(codec.unpack_codes(p), c)
+    one = np.zeros((1, 4), np.uint8)
+    one[0] = [1, 2, 3, 0]
+    assert codec.pack_codes(one)[0, 0] == 0b00111001
+
+
+def test_entry_bytes_roundtrip_and_size():
+    rng = np.random.default_rng(6)
+    kb = (rng.standard_normal((128, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb = (rng.standard_normal((128, 128)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    e = codec.quantize_window(kb, vb)
+    raw = codec.entry_bytes(e)
+    assert len(raw) == codec.entry_nbytes(128, 128) == 12288
+    # 3 bits per element including the fp16 scale and min per 32 values
+    assert len(raw) * 8 == 3 * 2 * 128 * 128
+    e2 = codec.entry_from_bytes(raw, 128, 128)
+    for key in e:
+        assert np.array_equal(np.asarray(e[key]).view(np.uint8), np.asarray(e2[key]).view(np.uint8))
+
+
+def test_promote_sum_is_exact_in_float64():
+    """c*s + m with fp16 s, m and c <= 3 is exact in float64, so one cast to
+    float32 is a single rounding (what a fused multiply-add gives)."""
+    rng = np.random.default_rng(7)
+    s = rng.choice(np.concatenate([rng.standard_normal(5000) * 1e-5, rng.standard_normal(5000) * 1e3]),
+                   20000).astype(np.float16)
+    m = rng.choice(np.concatenate([rng.standard_normal(5000) * 1e4, rng.standard_normal(5000) * 1e-6]),
+                   20000).astype(np.float16)
+    c = rng.integers(0, 4, 20000)
+    got = c * s.astype(np.float64) + m.astype(np.float64)
+    for i in range(0, 20000, 7):
+        assert Fraction(float(got[i])) == c[i] * Fraction(float(s[i])) + Fraction(float(m[i]))
+
+
+def test_promote_bits_match_torch_rounding():
+    rng = np.random.default_rng(8)
+    kb = (rng.standard_normal((64, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb = (rng.standard_normal((64, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    e = codec.quantize_window(kb, vb)
+    pk, pv = codec.promote_bits(e)
+    k, v = codec.dequant_window_f64(e)
+    ref = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(pk, ref(k)) and np.array_equal(pv, ref(v))
+
+
+@pytest.mark.parametrize("scale,offset", [(1.0, 0.0), (8.0, 0.0), (1e-3, 0.0), (100.0, 5e3)])
+def test_requantize_idempotent(scale, offset):
+    """Requantising a promoted window returns the ledger's codes, scales, mins."""
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        kf = (rng.standard_normal((128, 128)) * scale + offset).astype(np.float32)
+        vf = (rng.standard_normal((128, 128)) * scale + offset).astype(np.float32)
+        kb = (kf.view(np.uint32) >> 16).astype(np.uint16)
+        vb = (vf.view(np.uint32) >> 16).astype(np.uint16)
+        e = codec.quantize_window(kb, vb)
+        e2 = codec.quantize_window(*codec.promote_bits(e))
+        assert codec.entry_bytes(e) == codec.entry_bytes(e2)
