@@ -1,0 +1,219 @@
+/*
+ * kvtier.h - C ABI of the window-tiered KV-cache decode path for MI355X (gfx950).
+ *
+ * The method (QEvict technical summary, gist.science paper 2608.05326,
+ * "Methodologie: QEvict" and "Kernmechanismen"): the cached history of each
+ * (sequence, layer) segment is cut into windows of consecutive tokens; every
+ * window sits in one of three tiers -
+ *   F  full precision (bf16 here),
+ *   Q  recoverable INT2, backed by a write-once quantisation ledger,
+ *   E  evicted, for good -
+ * and windows move between tiers under a byte budget by their cumulative
+ * attention score.  One decode step attends over F and Q windows and emits the
+ * attention mass each window receives.
+ *
+ * Conventions for every call below
+ *   - Pointers are DEVICE pointers unless marked [host].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue work and return without synchronising, except
+ *     kv_pool_create (no sync either, but it validates), kv_pool_check and
+ *     kv_last_error.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns KV_EINVAL (or KV_ENOMEM for a too-small buffer) and
+ *     enqueues nothing.  A failed launch returns KV_EDEVICE.
+ *   - Conditions only the device can see (a demotion of a window that is not
+ *     bf16, a pool out of slots, ...) set bits of the pool's device error word,
+ *     skip the offending item and leave the state consistent; kv_pool_check
+ *     reports them as KV_ESTATE.
+ *   - No C++ exception crosses this ABI.  The library never allocates device
+ *     memory: the caller owns the arena and every buffer passed in.
+ *   - One pool is used from one stream at a time; calls on one pool must not
+ *     overlap.
+ */
+#ifndef KVTIER_H
+#define KVTIER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kv_pool kv_pool;  /* opaque host handle owned by the library */
+typedef int32_t kv_status;
+
+enum {
+  KV_OK = 0,
+  KV_EINVAL = 1,   /* invalid argument or configuration */
+  KV_ENOMEM = 2,   /* a caller buffer is smaller than required */
+  KV_EBUDGET = 3,  /* budget fractions outside [0, 1] */
+  KV_ESTATE = 4,   /* device-side state error (see kv_pool_check) */
+  KV_EDEVICE = 5   /* HIP runtime error */
+};
+
+/* Window tiers as stored in the page table. */
+enum { KV_TIER_E = 0, KV_TIER_Q = 1, KV_TIER_F = 2 };
+
+/* Device error word bits (kv_pool_check). */
+enum {
+  KV_ERR_DEMOTE_STATE = 1,     /* demote item not a full bf16 window */
+  KV_ERR_PROMOTE_STATE = 2,    /* promote item not INT2 with a ledger entry */
+  KV_ERR_NO_BF16_SLOT = 4,     /* no free bf16 slot in the segment */
+  KV_ERR_NO_LEDGER_SLOT = 8,   /* no free ledger slot in the segment */
+  KV_ERR_APPEND_STATE = 16,    /* append into a window that is not bf16 */
+  KV_ERR_ITEM_RANGE = 32,      /* item window index out of range */
+  KV_ERR_READ_MISSING = 64,    /* kv_read_* of a window without that copy */
+  KV_ERR_CAPACITY = 128        /* append beyond max_windows */
+};
+
+/* Pool geometry [host].  A segment is one (sequence b, layer l) pair; segment
+ * index = l * batch + b.  Limits: q_heads % kv_heads == 0 with group size
+ * q_heads / kv_heads in {1, 2, 4, 7, 8}; head_dim in {64, 128}; window a
+ * multiple of 32 in [32, 256]; 1 <= max_windows <= 4096; bf16_slots <= 16383
+ * and ledger_slots <= 32767 per segment; n_recent >= 0. */
+typedef struct {
+  int32_t batch, layers, q_heads, kv_heads;
+  int32_t head_dim;
+  int32_t window;        /* tokens per window */
+  int32_t max_windows;   /* windows per segment, including growth by decode */
+  int32_t n_recent;      /* newest windows that always stay bf16 */
+  int32_t bf16_slots;    /* bf16 window slots per segment */
+  int32_t ledger_slots;  /* INT2 ledger slots per segment */
+} kv_pool_config;
+
+/* Arena regions (kv_pool_region).  All regions are 256-byte aligned.
+ *  KV_REGION_BF16    bf16 window slots: [segment][bf16_slot][kv_head] blocks of
+ *                    2*W*D bf16 values (K then V, each [W][D] row-major).
+ *  KV_REGION_LEDGER  INT2 ledger slots: [segment][ledger_slot][kv_head] entries
+ *                    of 3*W*D/4 bytes: Kc [W][D/4], Vc [W][D/4] (code of
+ *                    (t, d) in byte d/4, bits 2*(d%4)), Ks, Km fp16 [W/32][D],
+ *                    Vs, Vm fp16 [W][D/32].
+ *  KV_REGION_PAGES   uint32 [segment][max_windows] page-table entries:
+ *                    bits 0-1 tier, bit 2 has-ledger, bits 3-16 bf16 slot,
+ *                    bits 17-31 ledger slot.
+ *  KV_REGION_SCORES  float [segment][max_windows] cumulative scores.
+ *  KV_REGION_TOKENS  int32 [segment] tokens cached.
+ *  KV_REGION_WORK    library scratch (transition work lists, counters).
+ *  KV_REGION_ERR     int32 device error word. */
+enum {
+  KV_REGION_BF16 = 0, KV_REGION_LEDGER = 1, KV_REGION_PAGES = 2, KV_REGION_SCORES = 3,
+  KV_REGION_TOKENS = 4, KV_REGION_WORK = 5, KV_REGION_ERR = 6, KV_REGION_COUNT = 7
+};
+
+/* Bytes of the device arena a pool of this geometry needs; 0 if `cfg` is
+ * invalid (kv_last_error says why). [host, pure] */
+size_t kv_pool_arena_bytes(const kv_pool_config* cfg);
+
+/* Bytes of one INT2 ledger entry (one window, one kv head): 3*W*D/4, i.e. 2-bit
+ * codes plus an fp16 scale and min per 32 values = 3 bits per value. [host] */
+size_t kv_ledger_entry_bytes(int32_t window, int32_t head_dim);
+
+/* Create a pool over a caller-owned device arena of at least
+ * kv_pool_arena_bytes(cfg) bytes, 256-byte aligned.  Enqueues the clearing of
+ * the metadata regions (every window evicted, no tokens, zero scores, zero
+ * error word) on `stream`.  *out receives the handle. */
+kv_status kv_pool_create(const kv_pool_config* cfg, void* arena, size_t arena_bytes,
+                         void* stream, kv_pool** out);
+
+/* Release the host handle (the arena stays the caller's). NULL is a no-op. */
+kv_status kv_pool_destroy(kv_pool* pool);
+
+/* Byte offset and size of a region inside the arena. [host] */
+kv_status kv_pool_region(const kv_pool* pool, int32_t which, size_t* offset, size_t* bytes);
+
+/* Load a prefilled context into `layer`: k, v bf16 [batch][kv_heads][tokens][D].
+ * Every window of every sequence becomes a bf16 window (window w in bf16
+ * slot w), tokens = `tokens`, scores = prior (float [batch][ceil(tokens/W)],
+ * or zeros when NULL).  Needs ceil(tokens/W) <= min(max_windows, bf16_slots). */
+kv_status kv_prefill(kv_pool* pool, int32_t layer, const void* k, const void* v,
+                     int32_t tokens, const float* prior, void* stream);
+
+/* Demote windows from bf16 to INT2 ("Kernmechanismen", demotion; write-once
+ * ledger).  items: int32 [batch][stride] window indices of `layer`, counts:
+ * int32 [batch] items per sequence (device, so a router's output can be passed
+ * straight in).  A window without a ledger entry is quantised now into the
+ * lowest free ledger slot (per 32-value groups: K per channel over 32 tokens,
+ * V per token over 32 channels; fp16 scale = (max-min)/3 and min; codes
+ * round-half-even((x - min)/scale) in float32, clamped to 0..3); a window that
+ * already has one keeps it unchanged.  Its bf16 slot is freed.  Items are
+ * processed in order per sequence. */
+kv_status kv_demote_quantize(kv_pool* pool, int32_t layer, const int32_t* items,
+                             int32_t stride, const int32_t* counts, void* stream);
+
+/* Promote windows from INT2 back to bf16 ("Kernmechanismen", promotion): the
+ * ledger entry is dequantised, bf16_rne(fmaf(code, scale, min)), into the
+ * lowest free bf16 slot; the ledger entry is kept.  Same item format as
+ * kv_demote_quantize.  Enqueue demotions first: a promotion can reuse a slot
+ * a demotion frees. */
+kv_status kv_promote_dequantize(kv_pool* pool, int32_t layer, const int32_t* items,
+                                int32_t stride, const int32_t* counts, void* stream);
+
+/* Workspace bytes kv_tiered_decode_attn needs for this pool. [host] */
+size_t kv_attn_workspace_bytes(const kv_pool* pool);
+
+/* One decode step of grouped-query attention for every sequence of `layer`
+ * over its bf16 and INT2 windows; evicted windows take no part (the softmax
+ * normaliser runs over the remaining tokens).  Query head h reads kv head
+ * h / (q_heads / kv_heads).
+ *   q      bf16 [batch][q_heads][D]
+ *   k_new, v_new  bf16 [batch][kv_heads][D], the token this step appends (it
+ *          is attended and then stored in the newest window, opening a new
+ *          bf16 window when the last one is full); both NULL = no append.
+ *   out    float [batch][q_heads][D]
+ *   mass   float [batch][q_heads][max_windows] or NULL: the softmax probability
+ *          summed over each window's tokens (0 for evicted windows; entries at
+ *          or past the window count are not written).
+ *   workspace  >= kv_attn_workspace_bytes(pool) bytes, 256-byte aligned; its
+ *          contents need not be preserved between calls. */
+kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q,
+                                const void* k_new, const void* v_new,
+                                float* out, float* mass,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cumulative scoring and routing of `layer` ("Kernmechanismen", cumulative
+ * scoring; "Methodologie: QEvict", three tiers under a fixed budget).
+ *   mass   float [batch][q_heads][max_windows] from kv_tiered_decode_attn, or
+ *          NULL: S[w] += sum over heads of mass[h][w] for live windows.
+ *   do_route != 0: route every window.  With n windows, R = n_recent:
+ *            n_hi = min(n, max(R, floor(hi_frac * n)))
+ *            n_lo = max(0, min(n - n_hi, floor((budget_frac * n - n_hi) * 16 / 3)))
+ *          (double precision, in this order); the R newest windows are bf16;
+ *          the other live windows ranked by (S descending, index ascending):
+ *          the first n_hi - R stay/become bf16, the next n_lo INT2, the rest
+ *          are evicted now.  Demotions and promotions are written as lists for
+ *          kv_demote_quantize / kv_promote_dequantize:
+ *   transitions  int32 [3][batch][max_windows]: demote, promote, evict lists
+ *          (ascending window order)
+ *   counts int32 [4][batch]: demotions, promotions, evictions, demotions that
+ *          will quantise (no ledger entry yet). */
+kv_status kv_score_route(kv_pool* pool, int32_t layer, const float* mass, int32_t do_route,
+                         double budget_frac, double hi_frac,
+                         int32_t* transitions, int32_t* counts, void* stream);
+
+/* Copy window `window` of sequence b, layer l, in the canonical layouts:
+ * kv_read_ledger writes kv_heads ledger entries (KV_REGION_LEDGER entry
+ * format) to dst; kv_read_window writes bf16 K then V [kv_heads][2][W][D].
+ * A window without that copy sets KV_ERR_READ_MISSING and writes zeros. */
+kv_status kv_read_ledger(kv_pool* pool, int32_t layer, int32_t b, int32_t window,
+                         void* dst, void* stream);
+kv_status kv_read_window(kv_pool* pool, int32_t layer, int32_t b, int32_t window,
+                         void* dst, void* stream);
+
+/* The router's tier counts for a segment of n windows (the formula of
+ * kv_score_route, evaluated on the host in the same double-precision order).
+ * [host, pure] */
+kv_status kv_tier_counts(int32_t n, int32_t n_recent, double budget_frac, double hi_frac,
+                         int32_t* n_hi, int32_t* n_lo);
+
+/* Synchronise `stream`, read and clear the device error word.  Returns KV_OK or
+ * KV_ESTATE (kv_last_error lists the bits); *bits (may be NULL) gets them. */
+kv_status kv_pool_check(kv_pool* pool, void* stream, int32_t* bits);
+
+/* Message of the last failing call on this thread ("" if none). [host] */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVTIER_H */

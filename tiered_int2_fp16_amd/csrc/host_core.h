@@ -1,0 +1,55 @@
+// Host-side geometry of a window-tiered KV pool: validation, arena regions,
+// workspace sizing.  Pure C++17 (no HIP), so it builds and tests on any host.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "kvtier.h"
+
+namespace kvtier {
+
+constexpr int kTile = 32;            // tokens per attention tile = INT2 group length
+constexpr int kMaxWindows = 4096;    // page-table entries per segment (LDS bound)
+constexpr int kMaxBf16Slots = 16383; // 14-bit slot field
+constexpr int kMaxLedgerSlots = 32767;  // 15-bit slot field
+constexpr int kAttnThreads = 256;    // 4 wave64 per attention workgroup
+constexpr int kAttnWaves = kAttnThreads / 64;
+
+struct Geometry {
+  kv_pool_config cfg{};
+  int group = 0;              // q heads per kv head
+  int segments = 0;           // layers * batch
+  size_t bf16_block = 0;      // bytes of one (slot, kv head) bf16 block: K+V
+  size_t entry = 0;           // bytes of one (slot, kv head) ledger entry
+  size_t off[KV_REGION_COUNT]{};
+  size_t size[KV_REGION_COUNT]{};
+  size_t total = 0;
+  // KV_REGION_WORK sub-layout (int32 offsets into the region)
+  size_t work_items = 0;      // int4 [batch][max_windows]: window, src, dst, flag
+  size_t work_counts = 0;     // int  [batch]
+  size_t attn_counters = 0;   // int  [batch][kv_heads], zero at rest
+  size_t seg_counters = 0;    // int  [batch], zero at rest
+};
+
+// Validate `cfg` and fill `g`.  On failure returns false with a message.
+bool geometry_init(const kv_pool_config& cfg, Geometry* g, std::string* err);
+
+// Attention split-K factor: workgroups per (sequence, kv head).
+int attn_splits(const Geometry& g, int compute_units);
+
+struct AttnWorkspace {
+  size_t partials = 0;   // float [batch][kv_heads][splits][group*(D+2)]
+  size_t tile_mass = 0;  // float [batch][kv_heads][max_windows*W/32][group][2]
+  size_t total = 0;
+};
+AttnWorkspace attn_workspace(const Geometry& g, int splits);
+
+// Tier counts of a segment with n windows (the router's formula; double
+// precision, evaluated in the documented order).
+void tier_counts(int n, int n_recent, double budget_frac, double hi_frac, int* n_hi, int* n_lo);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace kvtier

@@ -1,0 +1,37 @@
+// Host launchers of the gfx950 kernels (one translation unit per kernel family).
+// Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace kvtier {
+
+hipError_t launch_prefill(const PoolView& pv, int layer, const uint16_t* k, const uint16_t* v,
+                          int tokens, const float* prior, hipStream_t s);
+hipError_t launch_demote(const PoolView& pv, int layer, const int32_t* items, int stride,
+                         const int32_t* counts, hipStream_t s);
+hipError_t launch_promote(const PoolView& pv, int layer, const int32_t* items, int stride,
+                          const int32_t* counts, hipStream_t s);
+hipError_t launch_read(const PoolView& pv, int layer, int b, int window, bool ledger, void* dst,
+                       hipStream_t s);
+
+struct AttnArgs {
+  int layer;
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  float* out;
+  float* mass;
+  float* partials;
+  float* tile_mass;
+  int splits;
+};
+hipError_t launch_attn(const PoolView& pv, const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, int do_route,
+                              double budget_frac, double hi_frac, int32_t* transitions,
+                              int32_t* counts, hipStream_t s);
+
+}  // namespace kvtier

@@ -1,0 +1,163 @@
+// Cumulative scoring and the byte-budget router for gfx950.
+//
+// QEvict technical summary: window importance is the attention score
+// accumulated over time ("Kernmechanismen", cumulative scoring); windows are
+// routed among full precision, recoverable INT2 and evicted within a fixed
+// byte budget ("Methodologie: QEvict"; "Kernbijdragen" item 2); evicted
+// windows are gone for good.
+//
+// Readings where the pages are silent: the R newest windows always stay bf16;
+// tier counts come from the budget as
+//   n_hi = min(n, max(R, floor(phi*n))),
+//   n_lo = max(0, min(n - n_hi, floor((beta*n - n_hi)*16/3)))
+// in double precision in that order (16/3 = bf16 bytes over INT2 bytes of a
+// window); ranking is score descending, then window index ascending.
+#include "launch.h"
+
+namespace kvtier {
+
+// S[w] += sum over the layer's query heads of mass[h][w], for live windows.
+__global__ __launch_bounds__(256) void score_kernel(PoolView pv, int layer, const float* mass) {
+  const int b = blockIdx.y, seg = layer * pv.B + b;
+  const int w = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = windows_of(pv.tokens[seg], pv.W);
+  if (w >= n) return;
+  if (pe_tier(pv.pages[size_t(seg) * pv.maxw + w]) == TIER_E) return;
+  float acc = 0.f;
+  const float* m = mass + size_t(b) * pv.Hq * pv.maxw + w;
+  for (int h = 0; h < pv.Hq; ++h) acc += m[size_t(h) * pv.maxw];
+  pv.scores[size_t(seg) * pv.maxw + w] += acc;
+}
+
+// Tier counts, IEEE double in the documented order (explicit roundings: no
+// contraction into fused multiply-adds).
+__device__ inline void device_tier_counts(int n, int R, double beta, double phi, int* hi, int* lo) {
+  const double a = __dmul_rn(phi, double(n));
+  int h = int(floor(a));
+  h = h > R ? h : R;
+  h = h < n ? h : n;
+  const double x = __ddiv_rn(__dmul_rn(__dsub_rn(__dmul_rn(beta, double(n)), double(h)), 16.0), 3.0);
+  int l = int(floor(x));
+  l = l < n - h ? l : n - h;
+  l = l > 0 ? l : 0;
+  *hi = h;
+  *lo = l;
+}
+
+// One workgroup per sequence: rank the eligible windows by counting, assign
+// tiers, emit the transition lists in ascending window order, apply evictions.
+__global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, double beta, double phi,
+                                                     int32_t* transitions, int32_t* counts) {
+  extern __shared__ uint32_t smem[];
+  const int b = blockIdx.x, seg = layer * pv.B + b;
+  const int maxw = pv.maxw;
+  uint32_t* pages = smem;                                    // [maxw]
+  float* S = reinterpret_cast<float*>(smem + maxw);          // [maxw]
+  uint8_t* newt = reinterpret_cast<uint8_t*>(smem + 2 * maxw);  // [maxw]
+  __shared__ int wave_tot[16][4];
+  __shared__ int base[4];
+  const int len = pv.tokens[seg];
+  const int n = windows_of(len, pv.W);
+  const int fr = n - pv.R > 0 ? n - pv.R : 0;  // first recent window
+  int n_hi, n_lo;
+  device_tier_counts(n, pv.R, beta, phi, &n_hi, &n_lo);
+  int nf = n_hi - (n - fr);
+  nf = nf > 0 ? nf : 0;
+  uint32_t* gp = pv.pages + size_t(seg) * maxw;
+  const float* gs = pv.scores + size_t(seg) * maxw;
+  for (int w = threadIdx.x; w < n; w += blockDim.x) {
+    pages[w] = gp[w];
+    S[w] = gs[w];
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < n; w += blockDim.x) {
+    const uint32_t e = pages[w];
+    const int t = pe_tier(e);
+    int nt = t;
+    if (t != TIER_E) {
+      if (w >= fr) {
+        nt = TIER_F;
+      } else {
+        const float sw = S[w];
+        int rank = 0;
+        for (int x = 0; x < fr; ++x) {
+          if (pe_tier(pages[x]) == TIER_E) continue;
+          const float sx = S[x];
+          rank += (sx > sw) || (sx == sw && x < w);
+        }
+        nt = rank < nf ? TIER_F : (rank < nf + n_lo ? TIER_Q : TIER_E);
+      }
+    }
+    newt[w] = uint8_t(nt);
+  }
+  __syncthreads();
+  // Ordered compaction: each thread owns a contiguous run of windows.
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int w0 = threadIdx.x * per, w1 = min(n, w0 + per);
+  int c[4] = {0, 0, 0, 0};  // demote, promote, evict, first quantisation
+  for (int w = w0; w < w1; ++w) {
+    const int t = pe_tier(pages[w]), nt = newt[w];
+    c[0] += (t == TIER_F && nt == TIER_Q);
+    c[1] += (t == TIER_Q && nt == TIER_F);
+    c[2] += (t != TIER_E && nt == TIER_E);
+    c[3] += (t == TIER_F && nt == TIER_Q && !pe_has_ledger(pages[w]));
+  }
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int pre[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int x = c[k];
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    pre[k] = x - c[k];
+    if (lane == 63) wave_tot[wid][k] = x;
+  }
+  __syncthreads();
+  const int nw = (blockDim.x + 63) / 64;
+  if (threadIdx.x < 4) {
+    int tot = 0;
+    for (int i = 0; i < nw; ++i) tot += wave_tot[i][threadIdx.x];
+    base[threadIdx.x] = tot;
+    if (counts) counts[threadIdx.x * pv.B + b] = tot;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    for (int i = 0; i < wid; ++i) pre[k] += wave_tot[i][k];
+  __syncthreads();
+  if (transitions) {
+    int32_t* dl = transitions + (size_t(0) * pv.B + b) * maxw;
+    int32_t* pl = transitions + (size_t(1) * pv.B + b) * maxw;
+    int32_t* el = transitions + (size_t(2) * pv.B + b) * maxw;
+    for (int w = w0; w < w1; ++w) {
+      const int t = pe_tier(pages[w]), nt = newt[w];
+      if (t == TIER_F && nt == TIER_Q) dl[pre[0]++] = w;
+      if (t == TIER_Q && nt == TIER_F) pl[pre[1]++] = w;
+      if (t != TIER_E && nt == TIER_E) el[pre[2]++] = w;
+    }
+  }
+  // evictions take effect now: both copies are released
+  for (int w = threadIdx.x; w < n; w += blockDim.x)
+    if (pe_tier(pages[w]) != TIER_E && newt[w] == TIER_E) gp[w] = 0u;
+}
+
+hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, int do_route,
+                              double beta, double phi, int32_t* transitions, int32_t* counts,
+                              hipStream_t s) {
+  if (mass) {
+    hipLaunchKernelGGL(score_kernel, dim3((pv.maxw + 255) / 256, pv.B), dim3(256), 0, s, pv, layer,
+                       mass);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (do_route) {
+    const size_t shm = size_t(pv.maxw) * 9;
+    hipLaunchKernelGGL(route_kernel, dim3(pv.B), dim3(1024), shm, s, pv, layer, beta, phi, transitions,
+                       counts);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvtier
