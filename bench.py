@@ -1,0 +1,257 @@
+"""Benchmark of the tiered decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the Llama-3.1-8B attention shape at 32K context (batch 1, 32 query /
+8 kv heads, head_dim 128, windows of 128 tokens, 20 % byte budget with 10 % of
+windows in bf16: 25 bf16 / 139 INT2 / 92 evicted windows), synthetic seeded
+data.  One step = one decode step over the tiered cache: the attention kernel
+(with per-window mass), the cumulative score update, and every 16th step of a
+pool a routing event (router, demotions into the write-once ledger,
+promotions).  Steps rotate over enough pool replicas (each its own arena) that
+every step reads its windows from HBM, not from the 256 MB Infinity Cache.
+
+The timed region replays a HIP graph of exactly K steps between two device
+synchronisations.  The attention kernel's own duration is then taken over the
+same K steps run eagerly with dispatch timing events (hipExtLaunchKernel).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from workload import CONFIGS, kv_history, query, score_prior  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+ROUTE_EVERY = 16
+
+
+def attn_bytes(c, n_f, n_q, n_windows):
+    """Algorithmic bytes of one attention launch: every bf16 window's K and V
+    (4*W*D per kv head), every INT2 window's codes + fp16 scale/min (3*W*D/4),
+    the query, the output, the window masses and the page table."""
+    wd = c.window * c.head_dim
+    kv = c.batch * c.kv_heads * (n_f * 4 * wd + n_q * 3 * wd // 4)
+    io = c.batch * c.q_heads * c.head_dim * (2 + 4) + c.batch * c.q_heads * n_windows * 4
+    return kv + io + c.batch * n_windows * 4
+
+
+def score_bytes(c, n_windows):
+    return c.batch * c.q_heads * n_windows * 4 + c.batch * n_windows * (8 + 4)
+
+
+def route_bytes(c, n_windows, first_quant, promotions):
+    wd = c.window * c.head_dim
+    move = c.kv_heads * (4 * wd + 3 * wd // 4)
+    return c.batch * n_windows * (4 + 4) + (first_quant + promotions) * move
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "tiered_int2_fp16_amd", "csrc"))):
+        h.update(open(os.path.join(ROOT, "tiered_int2_fp16_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_hash):
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "attn_llama8b_32k_traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(c, seconds):
+    """The oracle (plain numpy float64) timed on the host on the same workload:
+    one sequence's decode steps (tiered attention + window mass + score update)
+    until about `seconds` of work."""
+    from oracle.pool import Segment
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    k, v = kv_history(c, 0, 0)
+    prior = score_prior(c, 0, 0).astype(np.float64)
+    seg = Segment(c.kv_heads, c.window, c.head_dim, c.n_recent)
+    seg.prefill(k, v, prior=prior)
+    seg.route(c.budget_frac, c.hi_frac)
+    n_f, n_q = seg.tier.count(2), seg.tier.count(1)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        q = query(c, 0, steps)
+        _, mass = seg.attend(q[0])
+        seg.add_scores(mass)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_step = attn_bytes(c, n_f, n_q, seg.n) + score_bytes(c, seg.n)
+    return {"value": round(per_step * steps / el / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{steps} decode steps of the same 32K Llama-3.1-8B-shaped workload "
+                      f"(attention with window mass + score update, batch 1, 8 kv heads) in "
+                      f"{el:.1f} s; {steps / el:.3f} steps/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--replicas", type=int, default=24)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the tiered decode path here is single-GPU "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiered_int2_fp16_amd import binding as B
+
+    c = CONFIGS["llama8b_32k"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    n = c.n_windows
+    R = max(1, args.replicas)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    k, v = kv_history(c, 0, 0)
+    prior = score_prior(c, 0, 0)
+    K = torch.from_numpy(k.view(np.int16)[None]).to(dev)
+    V = torch.from_numpy(v.view(np.int16)[None]).to(dev)
+    P = torch.from_numpy(prior[None]).to(dev)
+    nq = 16
+    Q = [torch.from_numpy(query(c, 0, s).view(np.int16)).to(dev) for s in range(nq)]
+    cfg = B.make_config(c.batch, c.layers, c.q_heads, c.kv_heads, c.head_dim, c.window, n,
+                        c.n_recent, n, n)
+    pools, outs, masses, trs, cnts = [], [], [], [], []
+    for r in range(R):
+        p = B.Pool(cfg, dev)
+        p.prefill(0, K, V, c.context, P)
+        tr = torch.zeros(3, c.batch, n, dtype=torch.int32, device=dev)
+        cn = torch.zeros(4, c.batch, dtype=torch.int32, device=dev)
+        p.score_route(0, None, 1, c.budget_frac, c.hi_frac, tr, cn)
+        p.apply_route(0, tr, cn)
+        pools.append(p)
+        outs.append(torch.empty(c.batch, c.q_heads, c.head_dim, dtype=torch.float32, device=dev))
+        masses.append(torch.zeros(c.batch, c.q_heads, n, dtype=torch.float32, device=dev))
+        trs.append(tr)
+        cnts.append(cn)
+    del K, V
+    torch.cuda.synchronize()
+    pages = pools[0].pages(0)[0].cpu().numpy() & 3
+    n_f, n_q = int((pages == 2).sum()), int((pages == 1).sum())
+    assert all(p.check() == 0 for p in pools)
+    log(f"{R} replicas ready: {n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows")
+    local = [0] * R
+    route_log = []  # (replica, counts tensor snapshot index)
+
+    def step(i, record=None):
+        r = i % R
+        p = pools[r]
+        p.attn(0, Q[i % nq], out=outs[r], mass=masses[r])
+        do_route = (local[r] % ROUTE_EVERY) == ROUTE_EVERY - 1
+        p.score_route(0, masses[r], int(do_route), c.budget_frac, c.hi_frac, trs[r], cnts[r])
+        if do_route:
+            p.apply_route(0, trs[r], cnts[r])
+            if record is not None:
+                record.append(r)
+        local[r] += 1
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed
+    K_steps = args.steps
+    routed = []
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    local_before = list(local)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(K_steps):
+                step(args.warmup + i, routed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t_timed = time.perf_counter() - t0
+    # demotions that quantised and promotions, from the counts each routing
+    # event left (a replica routes at most once in a timed region of <= 16*R steps)
+    fq = sum(int(cnts[r][3].sum()) for r in routed)
+    pr = sum(int(cnts[r][1].sum()) for r in routed)
+    assert all(p.check() == 0 for p in pools)
+
+    # ---------------------------------------------- attention kernel duration
+    for p in pools:
+        B.kv_attn_profile(p.h, K_steps // R + 2)
+    for i in range(K_steps):
+        step(args.warmup + K_steps + i)
+    durs = []
+    for p in pools:
+        durs += B.kv_attn_timings(p.h)
+        B.kv_attn_profile(p.h, 0)
+    attn_ms = float(np.mean(durs))
+
+    per_attn = attn_bytes(c, n_f, n_q, n)
+    total_bytes = K_steps * (per_attn + score_bytes(c, n)) + \
+        len(routed) * route_bytes(c, n, 0, 0) + route_bytes(c, 0, fq, pr)
+    ms_per_step = 1e3 * t_timed / K_steps
+    value = total_bytes / t_timed / 1e9
+    achieved = per_attn / (attn_ms * 1e-3) / 1e9
+    khash = kernel_source_hash()
+    result = {
+        "metric": "tiered decode-attn effective HBM GB/s (% of peak) + decode steps/s at 32K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+int2",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_32k: Llama-3.1-8B attention shape, 32K context, one decode "
+                               "step per pool, batch 1, 32 q / 8 kv heads, head_dim 128, window 128, "
+                               "20% byte budget (25 bf16 / 139 INT2 / 92 evicted windows), route "
+                               "every 16 steps",
+                   "global_batch": c.batch, "seq_len": c.context, "parallelism": "none (1 GPU)",
+                   "replicas": R, "timed_region": "HIP graph replay of exactly K steps"},
+        "decode_steps_per_s": round(K_steps / t_timed, 1),
+        "percent_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "attn_kernel_us": round(attn_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(khash)},
+        "kernel_source_hash": khash,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

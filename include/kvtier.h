@@ -171,6 +171,17 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q,
                                 float* out, float* mass,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernel timing of kv_tiered_decode_attn (a profiling aid).  capacity > 0
+ * makes each later attention dispatch carry its own start/stop events
+ * (hipExtLaunchKernel), for up to `capacity` dispatches between reads;
+ * capacity 0 turns timing off.  Creates HIP events, never device memory. */
+kv_status kv_attn_profile(kv_pool* pool, int32_t capacity);
+
+/* Synchronise the device, copy the durations (milliseconds) of the attention
+ * dispatches timed since the last call into ms [host, cap entries] and their
+ * number into *n [host]; restart the count. */
+kv_status kv_attn_timings(kv_pool* pool, float* ms, int32_t cap, int32_t* n);
+
 /* Cumulative scoring and routing of `layer` ("Kernmechanismen", cumulative
  * scoring; "Methodologie: QEvict", three tiers under a fixed budget).
  *   mass   float [batch][q_heads][max_windows] from kv_tiered_decode_attn, or

@@ -28,6 +28,7 @@ EXPORTS = [
     "kv_pool_region", "kv_prefill", "kv_demote_quantize", "kv_promote_dequantize",
     "kv_attn_workspace_bytes", "kv_tiered_decode_attn", "kv_score_route", "kv_read_ledger",
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
+    "kv_attn_profile", "kv_attn_timings",
 ]
 
 
@@ -69,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "kv_tier_counts": (I32, [I32, I32, D, D, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "kv_pool_check": (I32, [P, P, ctypes.POINTER(I32)]),
         "kv_last_error": (ctypes.c_char_p, []),
+        "kv_attn_profile": (I32, [P, I32]),
+        "kv_attn_timings": (I32, [P, ctypes.POINTER(ctypes.c_float), I32, ctypes.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -181,6 +184,17 @@ def kv_pool_check(h, stream=None) -> int:
     if st not in (KV_OK, KV_ESTATE):
         _ck(st)
     return bits.value
+
+
+def kv_attn_profile(h, capacity: int):
+    _ck(LIB.kv_attn_profile(h, capacity))
+
+
+def kv_attn_timings(h, cap: int = 1 << 16):
+    buf = (ctypes.c_float * cap)()
+    n = ctypes.c_int32()
+    _ck(LIB.kv_attn_timings(h, buf, cap, ctypes.byref(n)))
+    return [buf[i] for i in range(n.value)]
 
 
 # ------------------------------------------------------- tensor ownership ---

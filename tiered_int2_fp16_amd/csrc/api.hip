@@ -5,6 +5,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "host_core.h"
 #include "kvtier.h"
@@ -18,6 +19,12 @@ struct kv_pool {
   size_t arena_bytes = 0;
   int splits = 1;
   int device = 0;
+  std::vector<hipEvent_t> ev_start, ev_stop;  // attention dispatch timing
+  int ev_used = 0;
+  ~kv_pool() {
+    for (hipEvent_t e : ev_start) hipEventDestroy(e);
+    for (hipEvent_t e : ev_stop) hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -224,8 +231,53 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q, con
   a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace));
   a.tile_mass = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.partials);
   a.splits = pool->splits;
+  a.ev_start = a.ev_stop = nullptr;
+  if (!pool->ev_start.empty() && pool->ev_used < int(pool->ev_start.size())) {
+    a.ev_start = pool->ev_start[pool->ev_used];
+    a.ev_stop = pool->ev_stop[pool->ev_used];
+    ++pool->ev_used;
+  }
   hipError_t e = launch_attn(view(pool), a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KV_OK : hip_fail(e, "attention launch");
+}
+
+kv_status kv_attn_profile(kv_pool* pool, int32_t capacity) {
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  if (capacity < 0 || capacity > (1 << 20)) return fail(KV_EINVAL, "capacity out of range");
+  kv_status st = set_device(pool);
+  if (st) return st;
+  for (hipEvent_t e : pool->ev_start) hipEventDestroy(e);
+  for (hipEvent_t e : pool->ev_stop) hipEventDestroy(e);
+  pool->ev_start.clear();
+  pool->ev_stop.clear();
+  pool->ev_used = 0;
+  for (int i = 0; i < capacity; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    pool->ev_start.push_back(a);
+    pool->ev_stop.push_back(b);
+  }
+  return KV_OK;
+}
+
+kv_status kv_attn_timings(kv_pool* pool, float* ms, int32_t cap, int32_t* n) {
+  if (!pool || !n || (cap > 0 && !ms)) return fail(KV_EINVAL, "bad arguments");
+  kv_status st = set_device(pool);
+  if (st) return st;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  const int cnt = pool->ev_used < cap ? pool->ev_used : cap;
+  for (int i = 0; i < cnt; ++i) {
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, pool->ev_start[i], pool->ev_stop[i]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    ms[i] = t;
+  }
+  *n = cnt;
+  pool->ev_used = 0;
+  return KV_OK;
 }
 
 kv_status kv_score_route(kv_pool* pool, int32_t layer, const float* mass, int32_t do_route,

@@ -22,6 +22,7 @@
 // and stored in the newest window afterwards; the page table and token count
 // are rewritten by the last workgroup of the sequence, after every workgroup of
 // that sequence has read them.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "host_core.h"
@@ -467,7 +468,12 @@ __global__ __launch_bounds__(256) void attn_kernel(PoolView pv, AttnArgs a) {
 template <int D, int G>
 static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream_t s) {
   const size_t shm = size_t(pv.maxw + 2) * 4 + size_t(pv.maxw + 1) * 4 + size_t((pv.nb + 31) / 32) * 4;
-  hipLaunchKernelGGL((attn_kernel<D, G>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pv, a);
+  if (a.ev_start || a.ev_stop) {
+    hipExtLaunchKernelGGL((attn_kernel<D, G>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
+                          a.ev_start, a.ev_stop, 0u, pv, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<D, G>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pv, a);
+  }
   return hipGetLastError();
 }
 

@@ -27,6 +27,8 @@ struct AttnArgs {
   float* partials;
   float* tile_mass;
   int splits;
+  hipEvent_t ev_start;  // optional dispatch timing events (may be null)
+  hipEvent_t ev_stop;
 };
 hipError_t launch_attn(const PoolView& pv, const AttnArgs& a, hipStream_t s);
 
