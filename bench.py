@@ -5,10 +5,10 @@
 Workload: the Llama-3.1-8B attention shape at 32K context (batch 1, 32 query /
 8 kv heads, head_dim 128, windows of 128 tokens, 20 % byte budget with 10 % of
 windows in bf16: 25 bf16 / 139 INT2 / 92 evicted windows), synthetic seeded
-data.  One step = one decode step over the tiered cache: the attention kernel
-(with per-window mass), the cumulative score update, and every 16th step of a
-pool a routing event (router, demotions into the write-once ledger,
-promotions).  Steps rotate over enough pool replicas (each its own arena) that
+data.  One step = one decode step over the tiered cache (kv_decode_step: the
+attention kernel and its combine kernel, which writes the per-window mass and
+adds it to the cumulative scores), and every 16th step of a pool a routing
+event (router, demotions into the write-once ledger, promotions).  Steps rotate over enough pool replicas (each its own arena) that
 every step reads its windows from HBM, not from the 256 MB Infinity Cache.
 
 The timed region replays a HIP graph of exactly K steps between two device
@@ -168,10 +168,10 @@ def main():
     def step(i, record=None):
         r = i % R
         p = pools[r]
-        p.attn(0, Q[i % nq], out=outs[r], mass=masses[r])
+        p.attn(0, Q[i % nq], out=outs[r], mass=masses[r], scores=True)   # kv_decode_step
         do_route = (local[r] % ROUTE_EVERY) == ROUTE_EVERY - 1
-        p.score_route(0, masses[r], int(do_route), c.budget_frac, c.hi_frac, trs[r], cnts[r])
         if do_route:
+            p.score_route(0, None, 1, c.budget_frac, c.hi_frac, trs[r], cnts[r])
             p.apply_route(0, trs[r], cnts[r])
             if record is not None:
                 record.append(r)

@@ -70,7 +70,8 @@ enum {
 /* Pool geometry [host].  A segment is one (sequence b, layer l) pair; segment
  * index = l * batch + b.  Limits: q_heads % kv_heads == 0 with group size
  * q_heads / kv_heads in {1, 2, 4, 7, 8}; head_dim in {64, 128}; window a
- * multiple of 32 in [32, 256]; 1 <= max_windows <= 4096; bf16_slots <= 16383
+ * multiple of 32 in [32, 256]; 1 <= max_windows <= 4096 with
+ * max_windows * window / 32 <= 8192; bf16_slots <= 16383
  * and ledger_slots <= 32767 per segment; n_recent >= 0. */
 typedef struct {
   int32_t batch, layers, q_heads, kv_heads;
@@ -84,11 +85,14 @@ typedef struct {
 
 /* Arena regions (kv_pool_region).  All regions are 256-byte aligned.
  *  KV_REGION_BF16    bf16 window slots: [segment][bf16_slot][kv_head] blocks of
- *                    2*W*D bf16 values (K then V, each [W][D] row-major).
+ *                    2*W*D bf16 values in 32-token tiles laid out for the
+ *                    matrix cores (K part, then V part of each tile; the
+ *                    placement is internal - kv_read_window gives [W][D]).
  *  KV_REGION_LEDGER  INT2 ledger slots: [segment][ledger_slot][kv_head] entries
- *                    of 3*W*D/4 bytes: Kc [W][D/4], Vc [W][D/4] (code of
- *                    (t, d) in byte d/4, bits 2*(d%4)), Ks, Km fp16 [W/32][D],
- *                    Vs, Vm fp16 [W][D/32].
+ *                    of 3*W*D/4 bytes in 32-token tiles (2-bit K and V codes,
+ *                    fp16 K scale/min per channel, fp16 V scale/min per token
+ *                    and 32-channel group; placement internal - kv_read_ledger
+ *                    gives the canonical layout below).
  *  KV_REGION_PAGES   uint32 [segment][max_windows] page-table entries:
  *                    bits 0-1 tier, bit 2 has-ledger, bits 3-16 bf16 slot,
  *                    bits 17-31 ledger slot.
@@ -160,7 +164,7 @@ size_t kv_attn_workspace_bytes(const kv_pool* pool);
  *   k_new, v_new  bf16 [batch][kv_heads][D], the token this step appends (it
  *          is attended and then stored in the newest window, opening a new
  *          bf16 window when the last one is full); both NULL = no append.
- *   out    float [batch][q_heads][D]
+ *   out    float [batch][q_heads][D], 16-byte aligned
  *   mass   float [batch][q_heads][max_windows] or NULL: the softmax probability
  *          summed over each window's tokens (0 for evicted windows; entries at
  *          or past the window count are not written).
@@ -171,7 +175,17 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q,
                                 float* out, float* mass,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Kernel timing of kv_tiered_decode_attn (a profiling aid).  capacity > 0
+/* One decode step: kv_tiered_decode_attn, with the cumulative score update of
+ * kv_score_route (S[w] += sum over the layer's query heads of mass[h][w],
+ * heads in order, for live windows) fused into its combining kernel.  Same
+ * arguments; mass may be NULL (the scores are still updated).  S ends up
+ * bit-identical to kv_tiered_decode_attn followed by kv_score_route. */
+kv_status kv_decode_step(kv_pool* pool, int32_t layer, const void* q,
+                         const void* k_new, const void* v_new,
+                         float* out, float* mass,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel timing of kv_tiered_decode_attn and kv_decode_step (a profiling aid).  capacity > 0
  * makes each later attention dispatch carry its own start/stop events
  * (hipExtLaunchKernel), for up to `capacity` dispatches between reads;
  * capacity 0 turns timing off.  Creates HIP events, never device memory. */
@@ -203,8 +217,10 @@ kv_status kv_score_route(kv_pool* pool, int32_t layer, const float* mass, int32_
                          int32_t* transitions, int32_t* counts, void* stream);
 
 /* Copy window `window` of sequence b, layer l, in the canonical layouts:
- * kv_read_ledger writes kv_heads ledger entries (KV_REGION_LEDGER entry
- * format) to dst; kv_read_window writes bf16 K then V [kv_heads][2][W][D].
+ * kv_read_ledger writes kv_heads ledger entries of 3*W*D/4 bytes to dst, each
+ * Kc [W][D/4], Vc [W][D/4] (code of (t, d) in byte d/4, bits 2*(d%4)), Ks, Km
+ * fp16 [W/32][D], Vs, Vm fp16 [W][D/32]; kv_read_window writes bf16 K then V
+ * [kv_heads][2][W][D].
  * A window without that copy sets KV_ERR_READ_MISSING and writes zeros. */
 kv_status kv_read_ledger(kv_pool* pool, int32_t layer, int32_t b, int32_t window,
                          void* dst, void* stream);

@@ -139,3 +139,21 @@ def test_llama_128k_loop_sampled():
         if (s + 1) % c.route_every == 0:
             p.route(0, c.budget_frac, c.hi_frac)
             p.check_state(0, ledger_sample=12, window_sample=4, rng=np.random.default_rng(3))
+
+
+def test_decode_step_fuses_the_score_update_bit_exactly():
+    """kv_decode_step == kv_tiered_decode_attn + kv_score_route, bit for bit."""
+    from workload import query
+    c = CONFIGS["llama8b_32k"]
+    a, b = Pair(c, seqs=[]), Pair(c, seqs=[])
+    for p in (a, b):
+        p.load(0)
+        p.route(0, c.budget_frac, c.hi_frac)
+    for s in range(3):
+        q = dev(query(c, 0, s))
+        oa, ma = a.pool.attn(0, q)
+        a.pool.score_route(0, ma, 0)
+        ob, mb = b.pool.attn(0, q, scores=True)
+        assert torch.equal(oa, ob) and torch.equal(ma, mb)
+        assert torch.equal(a.pool.scores(0), b.pool.scores(0))
+    assert a.pool.check() == 0 and b.pool.check() == 0

@@ -28,7 +28,7 @@ EXPORTS = [
     "kv_pool_region", "kv_prefill", "kv_demote_quantize", "kv_promote_dequantize",
     "kv_attn_workspace_bytes", "kv_tiered_decode_attn", "kv_score_route", "kv_read_ledger",
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
-    "kv_attn_profile", "kv_attn_timings",
+    "kv_attn_profile", "kv_attn_timings", "kv_decode_step",
 ]
 
 
@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "kv_promote_dequantize": (I32, [P, I32, P, I32, P, P]),
         "kv_attn_workspace_bytes": (SZ, [P]),
         "kv_tiered_decode_attn": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
+        "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_score_route": (I32, [P, I32, P, I32, D, D, P, P, P]),
         "kv_read_ledger": (I32, [P, I32, I32, I32, P, P]),
         "kv_read_window": (I32, [P, I32, I32, I32, P, P]),
@@ -162,6 +163,11 @@ def kv_attn_workspace_bytes(h) -> int:
 def kv_tiered_decode_attn(h, layer, q, out, mass, workspace, k_new=None, v_new=None, stream=None):
     _ck(LIB.kv_tiered_decode_attn(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(mass),
                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def kv_decode_step(h, layer, q, out, mass, workspace, k_new=None, v_new=None, stream=None):
+    _ck(LIB.kv_decode_step(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(mass),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def kv_score_route(h, layer, mass, do_route, budget_frac, hi_frac, transitions=None, counts=None,
@@ -272,7 +278,8 @@ class Pool:
         self._items(items, counts)
         kv_promote_dequantize(self.h, layer, items, counts)
 
-    def attn(self, layer, q, k_new=None, v_new=None, out=None, mass=None, want_mass=True):
+    def attn(self, layer, q, k_new=None, v_new=None, out=None, mass=None, want_mass=True, scores=False):
+        """kv_tiered_decode_attn, or kv_decode_step when `scores` (fused score update)."""
         c = self.cfg
         if out is None:
             out = torch.empty(c.batch, c.q_heads, c.head_dim, dtype=torch.float32, device=self.device)
@@ -283,7 +290,8 @@ class Pool:
         self._need(v_new, (c.batch, c.kv_heads, c.head_dim), _BF16, "v_new")
         self._need(out, (c.batch, c.q_heads, c.head_dim), (torch.float32,), "out")
         self._need(mass, (c.batch, c.q_heads, c.max_windows), (torch.float32,), "mass")
-        kv_tiered_decode_attn(self.h, layer, q, out, mass, self.workspace, k_new, v_new)
+        fn = kv_decode_step if scores else kv_tiered_decode_attn
+        fn(self.h, layer, q, out, mass, self.workspace, k_new, v_new)
         return out, mass
 
     def score_route(self, layer, mass, do_route, budget_frac=0.0, hi_frac=0.0, transitions=None,

@@ -205,15 +205,16 @@ size_t kv_attn_workspace_bytes(const kv_pool* pool) {
   return attn_workspace(pool->g, pool->splits).total;
 }
 
-kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q, const void* k_new,
-                                const void* v_new, float* out, float* mass, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+static kv_status attention(kv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                           const void* v_new, float* out, float* mass, void* workspace,
+                           size_t workspace_bytes, int acc_scores, void* stream) {
   kv_status st = check_pool_layer(pool, layer);
   if (st) return st;
   if (!q || !out) return fail(KV_EINVAL, "q and out must not be NULL");
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(KV_EINVAL, "k_new and v_new go together");
   if (!aligned(q, 16) || (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))))
     return fail(KV_EINVAL, "q, k_new, v_new must be 16-byte aligned");
+  if (!aligned(out, 16)) return fail(KV_EINVAL, "out must be 16-byte aligned");
   const AttnWorkspace ws = attn_workspace(pool->g, pool->splits);
   if (!workspace) return fail(KV_EINVAL, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(KV_EINVAL, "workspace must be 256-byte aligned");
@@ -221,6 +222,7 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q, con
     return fail(KV_ENOMEM, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                                std::to_string(ws.total));
   if ((st = set_device(pool))) return st;
+  char* wsb = static_cast<char*>(workspace);
   AttnArgs a;
   a.layer = layer;
   a.q = static_cast<const uint16_t*>(q);
@@ -228,9 +230,11 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q, con
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.out = out;
   a.mass = mass;
-  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace));
-  a.tile_mass = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.partials);
+  a.partials = reinterpret_cast<float*>(wsb);
+  a.tile_mass = reinterpret_cast<float*>(wsb + ws.partials);
+  a.app_info = reinterpret_cast<int32_t*>(wsb + ws.partials + ws.tile_mass);
   a.splits = pool->splits;
+  a.acc_scores = acc_scores;
   a.ev_start = a.ev_stop = nullptr;
   if (!pool->ev_start.empty() && pool->ev_used < int(pool->ev_start.size())) {
     a.ev_start = pool->ev_start[pool->ev_used];
@@ -239,6 +243,18 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q, con
   }
   hipError_t e = launch_attn(view(pool), a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KV_OK : hip_fail(e, "attention launch");
+}
+
+kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                                const void* v_new, float* out, float* mass, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return attention(pool, layer, q, k_new, v_new, out, mass, workspace, workspace_bytes, 0, stream);
+}
+
+kv_status kv_decode_step(kv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                         const void* v_new, float* out, float* mass, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attention(pool, layer, q, k_new, v_new, out, mass, workspace, workspace_bytes, 1, stream);
 }
 
 kv_status kv_attn_profile(kv_pool* pool, int32_t capacity) {

@@ -41,20 +41,6 @@ struct PoolView {
   }
 };
 
-// Canonical ledger entry layout (byte offsets within one entry).
-struct EntryLayout {
-  int kc, vc, ks, km, vs, vm, bytes;
-  __host__ __device__ EntryLayout(int W, int D) {
-    kc = 0;
-    vc = W * D / 4;
-    ks = W * D / 2;
-    km = ks + (W / 32) * D * 2;
-    vs = km + (W / 32) * D * 2;
-    vm = vs + W * (D / 32) * 2;
-    bytes = vm + W * (D / 32) * 2;
-  }
-};
-
 __device__ inline void set_err(int32_t* err, int bits) {
   __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

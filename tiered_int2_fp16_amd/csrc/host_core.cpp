@@ -24,6 +24,8 @@ bool geometry_init(const kv_pool_config& c, Geometry* g, std::string* err) {
   if (c.max_windows < 1 || c.max_windows > kMaxWindows)
     return bad(err, "max_windows must be in [1, 4096]");
   if (c.n_recent < 0) return bad(err, "n_recent must be >= 0");
+  if (c.max_windows * (c.window / kTile) > kMaxTiles)
+    return bad(err, "max_windows * window / 32 must be <= 8192 (tiles per segment)");
   if (c.bf16_slots < 1 || c.bf16_slots > kMaxBf16Slots)
     return bad(err, "bf16_slots must be in [1, 16383]");
   if (c.ledger_slots < 0 || c.ledger_slots > kMaxLedgerSlots)
@@ -77,9 +79,11 @@ AttnWorkspace attn_workspace(const Geometry& g, int splits) {
   const kv_pool_config& c = g.cfg;
   AttnWorkspace w;
   const size_t pairs = size_t(c.batch) * c.kv_heads;
-  w.partials = align256(pairs * splits * g.group * (c.head_dim + 2) * 4);
-  w.tile_mass = align256(pairs * c.max_windows * (c.window / kTile) * g.group * 2 * 4);
-  w.total = w.partials + w.tile_mass;
+  const size_t per = (size_t(g.group) * (c.head_dim + 2) + 3) & ~size_t(3);
+  w.partials = align256(pairs * splits * per * 4);
+  w.tile_mass = align256(pairs * (size_t(c.max_windows) * (c.window / kTile) + 1) * g.group * 2 * 4);
+  w.app_info = align256(size_t(c.batch) * 8 * 4);
+  w.total = w.partials + w.tile_mass + w.app_info;
   return w;
 }
 

@@ -12,6 +12,7 @@ namespace kvtier {
 
 constexpr int kTile = 32;            // tokens per attention tile = INT2 group length
 constexpr int kMaxWindows = 4096;    // page-table entries per segment (LDS bound)
+constexpr int kMaxTiles = 8192;      // 32-token tiles per segment (LDS bound)
 constexpr int kMaxBf16Slots = 16383; // 14-bit slot field
 constexpr int kMaxLedgerSlots = 32767;  // 15-bit slot field
 constexpr int kAttnThreads = 256;    // 4 wave64 per attention workgroup
@@ -40,8 +41,9 @@ bool geometry_init(const kv_pool_config& cfg, Geometry* g, std::string* err);
 int attn_splits(const Geometry& g, int compute_units);
 
 struct AttnWorkspace {
-  size_t partials = 0;   // float [batch][kv_heads][splits][group*(D+2)]
-  size_t tile_mass = 0;  // float [batch][kv_heads][max_windows*W/32][group][2]
+  size_t partials = 0;   // float [batch][kv_heads][splits][P]: o [G][D], max [G], sum [G], P % 4 == 0
+  size_t tile_mass = 0;  // float [batch][kv_heads][max_windows*W/32 + 1][group][2]
+  size_t app_info = 0;   // int [batch][8]: append decision of the step
   size_t total = 0;
 };
 AttnWorkspace attn_workspace(const Geometry& g, int splits);

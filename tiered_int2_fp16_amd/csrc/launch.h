@@ -26,7 +26,9 @@ struct AttnArgs {
   float* mass;
   float* partials;
   float* tile_mass;
+  int32_t* app_info;    // [batch][8] append decision of this step (workspace)
   int splits;
+  int acc_scores;       // combine also adds the window masses to the scores
   hipEvent_t ev_start;  // optional dispatch timing events (may be null)
   hipEvent_t ev_stop;
 };

@@ -23,9 +23,19 @@ __global__ __launch_bounds__(256) void score_kernel(PoolView pv, int layer, cons
   const int n = windows_of(pv.tokens[seg], pv.W);
   if (w >= n) return;
   if (pe_tier(pv.pages[size_t(seg) * pv.maxw + w]) == TIER_E) return;
+  // heads summed in order (the fused decode-step combine adds them the same way);
+  // loads issued eight at a time
   float acc = 0.f;
   const float* m = mass + size_t(b) * pv.Hq * pv.maxw + w;
-  for (int h = 0; h < pv.Hq; ++h) acc += m[size_t(h) * pv.maxw];
+  int h = 0;
+  for (; h + 8 <= pv.Hq; h += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = m[size_t(h + j) * pv.maxw];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+  }
+  for (; h < pv.Hq; ++h) acc += m[size_t(h) * pv.maxw];
   pv.scores[size_t(seg) * pv.maxw + w] += acc;
 }
 

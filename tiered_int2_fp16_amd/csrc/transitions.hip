@@ -11,28 +11,43 @@
 // validates the items in order, assigns the lowest free slot and rewrites the
 // page table; a data kernel then moves the bytes of every planned item.
 #include "launch.h"
+#include "layout.h"
 
 namespace kvtier {
 
 // ------------------------------------------------------------------ prefill
+// One workgroup per (window, kv head, sequence): the window's tokens, read in
+// the caller's [token][dim] order, are written in the tile layout of layout.h.
 __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, const uint16_t* k,
                                                       const uint16_t* v, int T, const float* prior) {
   const int w = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int seg = layer * pv.B + b;
   const int D = pv.D, W = pv.W, n = windows_of(T, W);
-  uint16_t* dk = pv.block(seg, w, kvh);
-  uint16_t* dv = dk + size_t(W) * D;
+  uint16_t* blk = pv.block(seg, w, kvh);
   const size_t src = (size_t(b) * pv.Hkv + kvh) * size_t(T) * D;
-  const int vec = D / 8;
-  for (int idx = threadIdx.x; idx < W * vec; idx += blockDim.x) {
-    const int t = idx / vec, c = idx % vec, pos = w * W + t;
-    uint4 a = make_uint4(0, 0, 0, 0), bb = make_uint4(0, 0, 0, 0);
-    if (pos < T) {
-      a = *reinterpret_cast<const uint4*>(k + src + size_t(pos) * D + 8 * c);
-      bb = *reinterpret_cast<const uint4*>(v + src + size_t(pos) * D + 8 * c);
+  const int per_tile = 4 * D;  // 16-byte chunks per part per tile
+  for (int idx = threadIdx.x; idx < (W / 32) * 2 * per_tile; idx += blockDim.x) {
+    const int tile = idx / (2 * per_tile), rem = idx % (2 * per_tile);
+    const bool is_v = rem >= per_tile;
+    const int c = is_v ? rem - per_tile : rem;
+    const int cmb = c >> 6, lane = c & 63;
+    uint32_t word[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int t, d;
+        if (is_v) layout::v_chunk_elem(cmb, lane, 2 * e2 + h, &t, &d);
+        else layout::k_chunk_elem(cmb, lane, 2 * e2 + h, D, &t, &d);
+        const int pos = w * W + tile * 32 + t;
+        const uint16_t x = pos < T ? (is_v ? v : k)[src + size_t(pos) * D + d] : uint16_t(0);
+        pair |= uint32_t(x) << (16 * h);
+      }
+      word[e2] = pair;
     }
-    *reinterpret_cast<uint4*>(dk + size_t(t) * D + 8 * c) = a;
-    *reinterpret_cast<uint4*>(dv + size_t(t) * D + 8 * c) = bb;
+    *reinterpret_cast<uint4*>(blk + size_t(tile) * 64 * D + (is_v ? 32 * D : 0) + size_t(c) * 8) =
+        make_uint4(word[0], word[1], word[2], word[3]);
   }
   if (kvh == 0 && threadIdx.x == 0) {
     pv.pages[size_t(seg) * pv.maxw + w] = pe_make(TIER_F, false, w, 0);
@@ -191,10 +206,14 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
   for (int w = threadIdx.x; w < maxw; w += blockDim.x) gp[w] = pages[w];
 }
 
+// Demote data kernel: for each planned (item, kv head), quantise every 32-token
+// tile of the bf16 window into its ledger entry.  A tile's K groups are its
+// channels (32 tokens each), its V groups each token's 32-channel blocks.
 __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer, int cap) {
-  __shared__ uint8_t codes[256 * 128];
+  __shared__ float xs[2][32][129];          // K, V of one tile, canonical [token][dim]
+  __shared__ uint8_t cs[2][32][128];        // their codes
   const int kvh = blockIdx.y, W = pv.W, D = pv.D;
-  const EntryLayout L(W, D);
+  const layout::LedgerTile LT(D);
   const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items);
   for (int k = blockIdx.x; k < pv.B * cap; k += gridDim.x) {
     const int b = k / cap, i = k % cap;
@@ -202,68 +221,68 @@ __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer, i
     const WorkItem it = work[size_t(b) * pv.maxw + i];
     if (it.flag != 1) continue;
     const int seg = layer * pv.B + b;
-    const uint16_t* K = pv.block(seg, it.src, kvh);
-    const uint16_t* V = K + size_t(W) * D;
+    const uint16_t* blk = pv.block(seg, it.src, kvh);
     uint8_t* E = pv.entry(seg, it.dst, kvh);
-    uint16_t* ks = reinterpret_cast<uint16_t*>(E + L.ks);
-    uint16_t* km = reinterpret_cast<uint16_t*>(E + L.km);
-    uint16_t* vs = reinterpret_cast<uint16_t*>(E + L.vs);
-    uint16_t* vm = reinterpret_cast<uint16_t*>(E + L.vm);
-    // K: one group per (32-token block j, channel d)
-    for (int g = threadIdx.x; g < (W / 32) * D; g += blockDim.x) {
-      const int j = g / D, d = g % D;
-      float x[32];
-      uint8_t c[32];
+    for (int tile = 0; tile < W / 32; ++tile) {
+      const uint16_t* tb = blk + size_t(tile) * 64 * D;
+      uint8_t* et = E + size_t(tile) * LT.bytes;
+      for (int x = threadIdx.x; x < 32 * D; x += blockDim.x) {
+        const int t = x / D, d = x % D;
+        xs[0][t][d] = bf16_to_f32(tb[layout::bf16_k_offset(t, d, D)]);
+        xs[1][t][d] = bf16_to_f32(tb[layout::bf16_v_offset(t, d, D)]);
+      }
+      __syncthreads();
+      uint16_t* ks = reinterpret_cast<uint16_t*>(et + LT.ks);
+      uint16_t* km = reinterpret_cast<uint16_t*>(et + LT.km);
+      uint16_t* vs = reinterpret_cast<uint16_t*>(et + LT.vs);
+      uint16_t* vm = reinterpret_cast<uint16_t*>(et + LT.vm);
+      for (int g = threadIdx.x; g < D + D; g += blockDim.x) {
+        float x[32];
+        uint8_t c[32];
+        if (g < D) {                       // K group: channel g over the tile's 32 tokens
 #pragma unroll
-      for (int t = 0; t < 32; ++t) x[t] = bf16_to_f32(K[size_t(32 * j + t) * D + d]);
-      quant_group(x, c, ks + j * D + d, km + j * D + d);
+          for (int t = 0; t < 32; ++t) x[t] = xs[0][t][g];
+          quant_group(x, c, ks + g, km + g);
 #pragma unroll
-      for (int t = 0; t < 32; ++t) codes[(32 * j + t) * D + d] = c[t];
-    }
-    __syncthreads();
-    for (int p = threadIdx.x; p < W * D / 16; p += blockDim.x) {
-      uint32_t word = 0;
+          for (int t = 0; t < 32; ++t) cs[0][t][g] = c[t];
+        } else {                           // V group: token t, channels 32j..32j+31
+          const int t = (g - D) / (D / 32), j = (g - D) % (D / 32);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) word |= uint32_t(codes[16 * p + e]) << (2 * e);
-      reinterpret_cast<uint32_t*>(E + L.kc)[p] = word;
-    }
-    __syncthreads();
-    // V: one group per (token t, 32-channel block jj)
-    const int vg = D / 32;
-    for (int g = threadIdx.x; g < W * vg; g += blockDim.x) {
-      const int t = g / vg, jj = g % vg;
-      float x[32];
-      uint8_t c[32];
-      const uint4* src = reinterpret_cast<const uint4*>(V + size_t(t) * D + 32 * jj);
+          for (int e = 0; e < 32; ++e) x[e] = xs[1][t][32 * j + e];
+          quant_group(x, c, vs + j * 32 + t, vm + j * 32 + t);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 u = src[q];
-        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[8 * q + 2 * r] = __uint_as_float(ww[r] << 16);
-          x[8 * q + 2 * r + 1] = __uint_as_float(ww[r] & 0xFFFF0000u);
+          for (int e = 0; e < 32; ++e) cs[1][t][32 * j + e] = c[e];
         }
       }
-      quant_group(x, c, vs + t * vg + jj, vm + t * vg + jj);
+      __syncthreads();
+      // pack: one 32-bit code word per thread step (64 lanes x D/32 words per part)
+      const int words = 64 * (D / 32);
+      for (int x = threadIdx.x; x < 2 * words; x += blockDim.x) {
+        const bool is_v = x >= words;
+        const int q = is_v ? x - words : x;
+        const int lane = q / (D / 32), w = q % (D / 32);
+        uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) codes[t * D + 32 * jj + e] = c[e];
+        for (int f = 0; f < 16; ++f) {
+          int cmb, e, t, d;
+          layout::field_elem(w, f, &cmb, &e);
+          if (is_v) layout::v_chunk_elem(cmb, lane, e, &t, &d);
+          else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
+          word |= uint32_t(cs[is_v][t][d]) << (2 * f);
+        }
+        reinterpret_cast<uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + w] = word;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int p = threadIdx.x; p < W * D / 16; p += blockDim.x) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) word |= uint32_t(codes[16 * p + e]) << (2 * e);
-      reinterpret_cast<uint32_t*>(E + L.vc)[p] = word;
-    }
-    __syncthreads();
   }
 }
 
-// Promote: bf16_rne(fmaf(c, s, m)) for every value of the window.
+// Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of the window.
+// A ledger chunk (lane, cmb) and the bf16 chunk (cmb, lane) hold the same 8
+// values, so each thread step turns one code half-word into one 16-byte chunk.
 __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, int cap) {
   const int kvh = blockIdx.y, W = pv.W, D = pv.D;
-  const EntryLayout L(W, D);
+  const layout::LedgerTile LT(D);
   const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items);
   for (int k = blockIdx.x; k < pv.B * cap; k += gridDim.x) {
     const int b = k / cap, i = k % cap;
@@ -272,36 +291,46 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, in
     if (it.flag != 1) continue;
     const int seg = layer * pv.B + b;
     const uint8_t* E = pv.entry(seg, it.src, kvh);
-    uint16_t* K = pv.block(seg, it.dst, kvh);
-    uint16_t* V = K + size_t(W) * D;
-    const uint16_t* ks = reinterpret_cast<const uint16_t*>(E + L.ks);
-    const uint16_t* km = reinterpret_cast<const uint16_t*>(E + L.km);
-    const uint16_t* vs = reinterpret_cast<const uint16_t*>(E + L.vs);
-    const uint16_t* vm = reinterpret_cast<const uint16_t*>(E + L.vm);
-    // 8 consecutive values (16 B of bf16, one 16-bit code word) per thread step
-    for (int idx = threadIdx.x; idx < W * D / 8; idx += blockDim.x) {
-      const int t = idx / (D / 8), d0 = 8 * (idx % (D / 8));
-      const uint32_t kw = reinterpret_cast<const uint16_t*>(E + L.kc)[idx];
-      const uint32_t vw = reinterpret_cast<const uint16_t*>(E + L.vc)[idx];
-      const float vsc = float(__builtin_bit_cast(_Float16, vs[t * (D / 32) + d0 / 32]));
-      const float vmn = float(__builtin_bit_cast(_Float16, vm[t * (D / 32) + d0 / 32]));
-      uint32_t ko[4], vo[4];
+    uint16_t* blk = pv.block(seg, it.dst, kvh);
+    const int per_tile = 4 * D;    // chunks per part per tile
+    for (int idx = threadIdx.x; idx < (W / 32) * 2 * per_tile; idx += blockDim.x) {
+      const int tile = idx / (2 * per_tile), rem = idx % (2 * per_tile);
+      const bool is_v = rem >= per_tile;
+      const int c = is_v ? rem - per_tile : rem;
+      const int cmb = c >> 6, lane = c & 63;
+      const uint8_t* et = E + size_t(tile) * LT.bytes;
+      const uint32_t word =
+          reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + (cmb >> 1)];
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(et + LT.ks);
+      const uint16_t* km = reinterpret_cast<const uint16_t*>(et + LT.km);
+      const uint16_t* vs = reinterpret_cast<const uint16_t*>(et + LT.vs);
+      const uint16_t* vm = reinterpret_cast<const uint16_t*>(et + LT.vm);
+      uint32_t out[4];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float kk[2], vv[2];
+      for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t pair = 0;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int d = d0 + e + h;
-          const float s = float(__builtin_bit_cast(_Float16, ks[(t / 32) * D + d]));
-          const float m = float(__builtin_bit_cast(_Float16, km[(t / 32) * D + d]));
-          kk[h] = __builtin_fmaf(float((kw >> (2 * (e + h))) & 3u), s, m);
-          vv[h] = __builtin_fmaf(float((vw >> (2 * (e + h))) & 3u), vsc, vmn);
+          const int e = 2 * e2 + h;
+          const int f = e2 + 4 * (cmb & 1) + 8 * h;
+          const float code = float((word >> (2 * f)) & 3u);
+          int t, d;
+          float s, m;
+          if (is_v) {
+            layout::v_chunk_elem(cmb, lane, e, &t, &d);
+            s = float(__builtin_bit_cast(_Float16, vs[(d >> 5) * 32 + t]));
+            m = float(__builtin_bit_cast(_Float16, vm[(d >> 5) * 32 + t]));
+          } else {
+            layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
+            s = float(__builtin_bit_cast(_Float16, ks[d]));
+            m = float(__builtin_bit_cast(_Float16, km[d]));
+          }
+          pair |= uint32_t(f32_to_bf16_rne(__builtin_fmaf(code, s, m))) << (16 * h);
         }
-        ko[e / 2] = uint32_t(f32_to_bf16_rne(kk[0])) | (uint32_t(f32_to_bf16_rne(kk[1])) << 16);
-        vo[e / 2] = uint32_t(f32_to_bf16_rne(vv[0])) | (uint32_t(f32_to_bf16_rne(vv[1])) << 16);
+        out[e2] = pair;
       }
-      *reinterpret_cast<uint4*>(K + size_t(t) * D + d0) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
-      *reinterpret_cast<uint4*>(V + size_t(t) * D + d0) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+      *reinterpret_cast<uint4*>(blk + size_t(tile) * 64 * D + (is_v ? 32 * D : 0) + size_t(c) * 8) =
+          make_uint4(out[0], out[1], out[2], out[3]);
     }
   }
 }
@@ -336,21 +365,63 @@ hipError_t launch_promote(const PoolView& pv, int layer, const int32_t* items, i
 }
 
 // ---------------------------------------------------------------- read-back
+// Canonical copies for inspection: bf16 K then V [kv_head][2][W][D]; ledger
+// entries as Kc, Vc [W][D/4] (code of (t, d) in byte d/4, bits 2*(d%4)), Ks,
+// Km fp16 [W/32][D], Vs, Vm fp16 [W][D/32].
 __global__ __launch_bounds__(256) void read_kernel(PoolView pv, int layer, int b, int w, int ledger,
                                                    uint8_t* dst) {
-  const int seg = layer * pv.B + b;
+  const int seg = layer * pv.B + b, W = pv.W, D = pv.D;
   const uint32_t e = (w >= 0 && w < pv.maxw) ? pv.pages[size_t(seg) * pv.maxw + w] : 0u;
-  const size_t per = ledger ? size_t(3 * pv.W * pv.D / 4) : size_t(4 * pv.W * pv.D);
   const bool ok = ledger ? (pe_tier(e) != TIER_E && pe_has_ledger(e)) : (pe_tier(e) == TIER_F);
   if (!ok && threadIdx.x == 0) set_err(pv.err, KV_ERR_READ_MISSING);
+  const layout::LedgerTile LT(D);
   for (int kvh = 0; kvh < pv.Hkv; ++kvh) {
-    const uint8_t* src = ok ? (ledger ? pv.entry(seg, pe_lslot(e), kvh)
-                                      : reinterpret_cast<const uint8_t*>(pv.block(seg, pe_bslot(e), kvh)))
-                            : nullptr;
-    for (size_t i = threadIdx.x; i < per / 16; i += blockDim.x) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (ok) x = reinterpret_cast<const uint4*>(src)[i];
-      reinterpret_cast<uint4*>(dst + kvh * per)[i] = x;
+    if (!ledger) {
+      uint16_t* out = reinterpret_cast<uint16_t*>(dst) + size_t(kvh) * 2 * W * D;
+      const uint16_t* blk = ok ? pv.block(seg, pe_bslot(e), kvh) : nullptr;
+      for (int x = threadIdx.x; x < W * D; x += blockDim.x) {
+        const int t = x / D, d = x % D;
+        out[x] = ok ? blk[layout::bf16_window_k(t, d, D)] : uint16_t(0);
+        out[W * D + x] = ok ? blk[layout::bf16_window_v(t, d, D)] : uint16_t(0);
+      }
+    } else {
+      uint8_t* out = dst + size_t(kvh) * (3 * W * D / 4);
+      const uint8_t* E = ok ? pv.entry(seg, pe_lslot(e), kvh) : nullptr;
+      uint8_t* kc = out;
+      uint8_t* vc = out + W * D / 4;
+      uint16_t* ks = reinterpret_cast<uint16_t*>(out + W * D / 2);
+      uint16_t* km = ks + (W / 32) * D;
+      uint16_t* vs = km + (W / 32) * D;
+      uint16_t* vm = vs + W * (D / 32);
+      for (int x = threadIdx.x; x < W * D / 4; x += blockDim.x) {
+        const int t = x / (D / 4), d0 = 4 * (x % (D / 4));
+        uint32_t kb = 0, vb = 0;
+        if (ok) {
+          const uint8_t* et = E + size_t(t / 32) * LT.bytes;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            int wb, bit;
+            layout::k_code_pos(t % 32, d0 + q, D, &wb, &bit);
+            kb |= ((*reinterpret_cast<const uint32_t*>(et + LT.kc + wb) >> bit) & 3u) << (2 * q);
+            layout::v_code_pos(t % 32, d0 + q, D, &wb, &bit);
+            vb |= ((*reinterpret_cast<const uint32_t*>(et + LT.vc + wb) >> bit) & 3u) << (2 * q);
+          }
+        }
+        kc[x] = uint8_t(kb);
+        vc[x] = uint8_t(vb);
+      }
+      for (int x = threadIdx.x; x < (W / 32) * D; x += blockDim.x) {
+        const int tile = x / D, d = x % D;
+        const uint8_t* et = ok ? E + size_t(tile) * LT.bytes : nullptr;
+        ks[x] = ok ? reinterpret_cast<const uint16_t*>(et + LT.ks)[d] : uint16_t(0);
+        km[x] = ok ? reinterpret_cast<const uint16_t*>(et + LT.km)[d] : uint16_t(0);
+      }
+      for (int x = threadIdx.x; x < W * (D / 32); x += blockDim.x) {
+        const int t = x / (D / 32), j = x % (D / 32);
+        const uint8_t* et = ok ? E + size_t(t / 32) * LT.bytes : nullptr;
+        vs[x] = ok ? reinterpret_cast<const uint16_t*>(et + LT.vs)[j * 32 + t % 32] : uint16_t(0);
+        vm[x] = ok ? reinterpret_cast<const uint16_t*>(et + LT.vm)[j * 32 + t % 32] : uint16_t(0);
+      }
     }
   }
 }
