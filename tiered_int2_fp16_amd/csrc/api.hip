@@ -230,10 +230,13 @@ static kv_status attention(kv_pool* pool, int32_t layer, const void* q, const vo
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.out = out;
   a.mass = mass;
-  a.partials = reinterpret_cast<float*>(wsb);
-  a.tile_mass = reinterpret_cast<float*>(wsb + ws.partials);
-  a.app_info = reinterpret_cast<int32_t*>(wsb + ws.partials + ws.tile_mass);
+  a.partials = reinterpret_cast<float*>(wsb + ws.partials);
+  a.ml = reinterpret_cast<float2*>(wsb + ws.ml);
+  a.tile_mass = reinterpret_cast<float2*>(wsb + ws.tile_mass);
+  a.app_mass = reinterpret_cast<float2*>(wsb + ws.app_mass);
+  a.app_info = reinterpret_cast<int32_t*>(wsb + ws.app_info);
   a.splits = pool->splits;
+  a.plan_words = (pool->g.cfg.max_windows + 255) & ~255;
   a.acc_scores = acc_scores;
   a.ev_start = a.ev_stop = nullptr;
   if (!pool->ev_start.empty() && pool->ev_used < int(pool->ev_start.size())) {

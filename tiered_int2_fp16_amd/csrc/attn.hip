@@ -60,7 +60,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGMax = 8;     // query heads per kv head supported
 constexpr int kWq = 5;       // weight of an INT2 tile (a bf16 tile weighs 16)
 constexpr int kMaxSplits = 64;
-constexpr int kMassWindows = 64;   // windows per mass block of the combine kernel
+constexpr int kMassWindows = 32;   // windows per mass block of the combine kernel
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -90,22 +90,39 @@ __device__ inline f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Exclusive scan of one int per thread over a 256-thread block.
-__device__ inline int block_excl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) tmp[wid] = x;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < wid; ++i) base += tmp[i];
-  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-  __syncthreads();
-  return base + x - v;
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
+// 16-lane rows, then row broadcasts across them).
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled).  Lanes whose
+// offset is out of range read zeros and touch no memory; bytes == 0 makes a
+// whole load a no-op.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// Wait for every outstanding vector memory operation (s_waitcnt vmcnt(0),
+// other counters left alone).
+__device__ inline void drain_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return uint32_t(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+// A buffer offset, or (when !valid) one past any resource here: that lane
+// reads zeros and touches no memory.
+__device__ inline int boff(bool valid, int off) { return valid ? off : int(0x80000000u); }
+__device__ inline float2 as_f2(uint2 u) { return make_float2(__uint_as_float(u.x), __uint_as_float(u.y)); }
+__device__ inline uint2 load8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
 // Eight INT2 codes of one operand chunk -> fp16 (1 + c/4).  Word X holds the
@@ -175,29 +192,28 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   constexpr int CW = D / 32;   // 32-bit code words per lane per part
   constexpr int kList = 64;    // tile entries a wave lists at a time
   constexpr int kQGroup = 4;   // INT2 tiles loaded together
-  extern __shared__ uint32_t s_used[];   // [(nb + 31) / 32] bf16 slot bitmap (append only)
+  extern __shared__ uint32_t s_dyn[];    // plan (page entries, tile prefixes), slot bitmap
   __shared__ float s_wm[kAttnWaves][kGMax], s_wl[kAttnWaves][kGMax];
   __shared__ float s_wo[kAttnWaves][kGMax][D];
   __shared__ float s_wb[kAttnWaves][kGMax][4];
   __shared__ __attribute__((aligned(16))) uint8_t s_scb[kAttnWaves][8 * D];  // INT2 tile scales
-  __shared__ __attribute__((aligned(16))) _Float16 s_bq[kAttnWaves][2][kGMax * D];  // 4sq hi, lo
-  __shared__ float s_cst[kAttnWaves][kGMax];                                   // tile constants
   __shared__ uint32_t s_list[kAttnWaves][kList];                               // a wave's tiles
+  __shared__ float2 s_rec[kAttnWaves][kList][kGMax];                           // their raw masses
+  __shared__ int s_gt[kMaxWindows / 64];                                       // tiles per 64 windows
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int g = lane >> 4, hn = lane & 15;   // lane = (column block g, head hn)
   const int W = pv.W, maxw = pv.maxw, TPW = W / 32, G = pv.G;
   const int seg = a.layer * pv.B + b;
   const int S = a.splits;
 
   // ------------------------------------------------------------ the query
-  // issued first: it does not depend on the plan
+  // issued first: it does not depend on the plan.  Lane (g, hn) holds channels
+  // 32kk + 8g .. 32kk + 8g + 7 of head hn: the B operand of the QK products.
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e / sqrtf(float(D));
-  bf16x8 qb[KK];    // q (bf16) for the bf16 tiles
-  constexpr int kRounds = (kGMax * (D / 8) + 63) / 64;
-  f16x8 qc[kRounds];  // 4*q in the compact (head, 8-channel chunk) layout
+  bf16x8 qb[KK];    // q (bf16)
   {
     const uint16_t* qp = a.q + (size_t(b) * pv.Hq + size_t(kvh) * G + hn) * D + 8 * g;
 #pragma unroll
@@ -206,44 +222,57 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       if (hn < G) u = *reinterpret_cast<const uint4*>(qp + 32 * kk);
       qb[kk] = as_bf16x8(u);
     }
+  }
+
+  // ------------------------------------------------ tile plan (workgroup)
+  // The page table goes to LDS once per workgroup: thread t takes windows
+  // t, t + 256, ...; their entries are loaded before the token count is known.
+  // s_ex[w] holds the live tiles before window w within its 64-window group
+  // (bf16 tiles in the low 16 bits, INT2 tiles in the high 16 bits) and
+  // s_gt[r] the total of group r; one barrier, then each wave reads the plan.
+  uint32_t* s_pe = s_dyn;                                        // [roundup(maxw, 256)]
+  int* s_ex = reinterpret_cast<int*>(s_dyn + a.plan_words);      // [roundup(maxw, 256)]
+  uint32_t* s_used = s_dyn + 2 * a.plan_words;                   // bf16 slot bitmap (append)
+  const int len_old = pv.tokens[seg];
+  const uint32_t* gp = pv.pages + size_t(seg) * maxw;
+  const int n_old = windows_of(len_old, W);
+  auto tiles_of = [&](uint32_t e, int w) -> int {
+    if (w >= n_old) return 0;
+    const int t = pe_tier(e);
+    const int vt = (min(W, len_old - w * W) + 31) / 32;
+    return t == TIER_F ? vt : (t == TIER_Q ? (vt << 16) : 0);
+  };
+  {
+    const auto pt = tile_rsrc(gp, maxw * 4);   // lanes past the table read 0
+    const int JR = a.plan_words / 256;
+    for (int j0 = 0; j0 < JR; j0 += 4) {
+      uint32_t e4[4];
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int it = 64 * r + lane, h = it / (D / 8), c8 = it % (D / 8);
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (h < G) u = *reinterpret_cast<const uint4*>(a.q + (size_t(b) * pv.Hq + size_t(kvh) * G + h) * D + 8 * c8);
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      for (int j = 0; j < 4; ++j) e4[j] = load4(pt, (256 * (j0 + j) + tid) * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qc[r][2 * e] = (_Float16)(4.f * __uint_as_float(w4[e] << 16));
-        qc[r][2 * e + 1] = (_Float16)(4.f * __uint_as_float(w4[e] & 0xFFFF0000u));
+      for (int j = 0; j < 4; ++j) {
+        if (j0 + j < JR) {
+          const int w = 256 * (j0 + j) + tid;
+          const int c = tiles_of(e4[j], w);
+          const int incl = wave_incl_scan(c);
+          s_pe[w] = e4[j];
+          s_ex[w] = incl - c;
+          if (lane == 63) s_gt[w >> 6] = incl;
+        }
       }
     }
   }
-
-  // ------------------------------------------------ wave-local tile plan
-  // Every wave reads the page table and prefix-sums the live tiles itself
-  // (bf16 tiles in the low 16 bits, INT2 tiles in the high 16 bits): no
-  // workgroup barrier before the first tile load.
-  const int len_old = pv.tokens[seg];
-  const int n_old = windows_of(len_old, W);
-  const uint32_t* gp = pv.pages + size_t(seg) * maxw;
-  const int per = (n_old + 63) / 64;
-  const int wl0 = min(n_old, lane * per), wl1 = min(n_old, wl0 + per);
-  int cnt = 0;
-  for (int w = wl0; w < wl1; ++w) {
-    const int t = pe_tier(gp[w]);
-    const int vt = (min(W, len_old - w * W) + 31) / 32;
-    cnt += t == TIER_F ? vt : (t == TIER_Q ? (vt << 16) : 0);
+  __syncthreads();
+  const int NG = (n_old + 63) / 64;   // 64-window groups (<= 64)
+  int gbase;                           // lane r: live tiles before group r
+  int tot;
+  {
+    const int t = lane < NG ? s_gt[lane] : 0;
+    const int incl = wave_incl_scan(t);
+    gbase = incl - t;
+    tot = __builtin_amdgcn_readlane(incl, 63);
   }
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  const int tot = uniform(__shfl(incl, 63, 64));
   const int NF = tot & 0xFFFF, NQ = tot >> 16;
-  const int excl = incl - cnt;
   const long U = 16L * NF + long(kWq) * NQ;
   const long nwaves = long(S) * kAttnWaves;
   const long widx = long(split) * kAttnWaves + wid;
@@ -253,17 +282,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   const int q_beg = int(min(long(NQ), cdiv(u0 - 16L * NF, kWq)));
   const int q_end = int(min(long(NQ), cdiv(u1 - 16L * NF, kWq)));
   uint32_t* list = s_list[wid];
-  // lanes write the entries of tiles [lo, hi) of tier `tier` that sit in their windows
+  // the wave lists the tiles [lo, hi) of tier `tier`: lane l takes window
+  // 64r + l of each group r whose tiles of that tier meet the range
   auto build_list = [&](int tier, int lo, int hi) {
-    int ti = tier == TIER_F ? (excl & 0xFFFF) : (excl >> 16);
-    for (int w = wl0; w < wl1 && ti < hi; ++w) {
-      const uint32_t e = gp[w];
+    const int sh = tier == TIER_F ? 0 : 16;
+    for (int r = 0; r < NG; ++r) {
+      const int b0 = (__builtin_amdgcn_readlane(gbase, r) >> sh) & 0xFFFF;
+      const int b1 = r + 1 < NG ? (__builtin_amdgcn_readlane(gbase, r + 1) >> sh) & 0xFFFF
+                                : ((tot >> sh) & 0xFFFF);
+      if (b1 <= lo || b0 >= hi) continue;
+      const int w = 64 * r + lane;
+      if (w >= n_old) continue;
+      const uint32_t e = s_pe[w];
       if (pe_tier(e) != tier) continue;
+      int ti = b0 + ((s_ex[w] >> sh) & 0xFFFF);
       const int vt = (min(W, len_old - w * W) + 31) / 32;
       const int sl = tier == TIER_F ? pe_bslot(e) : pe_lslot(e);
       for (int k = 0; k < vt; ++k, ++ti)
         if (ti >= lo && ti < hi) list[ti - lo] = te_make(sl, w, k);
     }
+    __builtin_amdgcn_wave_barrier();
   };
 
   // ------------------------------------------------- the append decision
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   int app_ok = 0, app_slot = 0, app_row = 0, app_new = 0;
   if (a.k_new != nullptr && split == 0 && wid == 0) {
     if (len_old % W != 0) {
-      const uint32_t e = gp[n_old - 1];
+      const uint32_t e = s_pe[n_old - 1];
       app_ok = pe_tier(e) == TIER_F;
       app_slot = pe_bslot(e);
       app_row = len_old % W;
@@ -281,11 +319,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       // a new window opens: the lowest bf16 slot no live bf16 window holds
       const int words = (pv.nb + 31) / 32;
       for (int i = lane; i < words; i += 64) s_used[i] = 0u;
+      __builtin_amdgcn_wave_barrier();
       for (int w = lane; w < n_old; w += 64) {
-        const uint32_t e = gp[w];
+        const uint32_t e = s_pe[w];
         if (pe_tier(e) == TIER_F && pe_bslot(e) < pv.nb)
           atomicOr(&s_used[pe_bslot(e) >> 5], 1u << (pe_bslot(e) & 31));
       }
+      __builtin_amdgcn_wave_barrier();
       int slot = 0x7FFFFFFF;
       for (int i = lane; i < words; i += 64) {
         const uint32_t x = ~s_used[i];
@@ -323,9 +363,25 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st.o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.ob = f32x4{0.f, 0.f, 0.f, 0.f};
-  float2* tmass = reinterpret_cast<float2*>(a.tile_mass) +
-                  (size_t(b) * pv.Hkv + kvh) * (size_t(maxw) * TPW + 1) * G;
-  const bool rec_mass = a.mass != nullptr && g == 0 && hn < G;
+  // raw tile masses of this kv head's query heads: row h holds tile w*TPW + k
+  float2* tmass = a.tile_mass + (size_t(b) * pv.Hq + size_t(kvh) * G) * maxw * TPW;
+  // tile masses feed the window masses and the fused score update
+  const bool want_mass = a.mass != nullptr || a.acc_scores != 0;
+  const bool rec_mass = want_mass && g == 0 && hn < G;
+  float2(*rec)[kGMax] = s_rec[wid];
+  // the raw masses of a listed chunk of nt tiles go out after the chunk: no
+  // global store inside the tile loops, where it would hold up the next
+  // tile's loads
+  auto flush_masses = [&](int nt) {
+    if (!want_mass) return;
+    __builtin_amdgcn_wave_barrier();
+    for (int idx = lane; idx < nt * G; idx += 64) {
+      const int h = idx / nt, t = idx - h * nt;
+      const uint32_t e = list[t];
+      tmass[size_t(h) * maxw * TPW + te_win(e) * TPW + te_tile(e)] = rec[t][h];
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
 
   // ------------------------------------------- the appended token (VALU)
   if (app_ok) {
@@ -355,25 +411,31 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       st.o[nb][2] = fmaf(p0, __uint_as_float(u.y << 16), st.o[nb][2]);
       st.o[nb][3] = fmaf(p0, __uint_as_float(u.y & 0xFFFF0000u), st.o[nb][3]);
     }
-    if (rec_mass) tmass[size_t(maxw) * TPW * G + hn] = make_float2(rs, st.m_run);
+    if (rec_mass) a.app_mass[size_t(b) * pv.Hq + size_t(kvh) * G + hn] = make_float2(rs, st.m_run);
   }
 
   // ---------------------------------------------------------- bf16 tiles
+  // Loads go through a buffer resource spanning one tile; a prefetch past the
+  // last tile gets an empty resource and reads zeros without touching memory,
+  // so the loop has no branch around a load and every tile waits only for
+  // its own loads.
   {
+    constexpr int kTileBytes = 64 * D * 2;
     struct FB {
       uint4 k[NB];
       uint4 v[NB];
     };
-    auto load_f = [&](FB& fb, uint32_t e) {
+    auto load_f = [&](FB& fb, int i, int nt) {
+      const uint32_t e = uniform(int(list[min(i, nt - 1)]));
       const uint16_t* base = pv.block(seg, te_slot(e), kvh) + size_t(te_tile(e)) * 64 * D;
-      const uint4* kp = reinterpret_cast<const uint4*>(base);
-      const uint4* vp = reinterpret_cast<const uint4*>(base + 32 * D);
+      const auto rs = tile_rsrc(base, i < nt ? kTileBytes : 0);
 #pragma unroll
-      for (int c = 0; c < NB; ++c) fb.k[c] = kp[c * 64 + lane];
+      for (int c = 0; c < NB; ++c) fb.k[c] = load16(rs, (c * 64 + lane) * 16);
 #pragma unroll
-      for (int c = 0; c < NB; ++c) fb.v[c] = vp[c * 64 + lane];
+      for (int c = 0; c < NB; ++c) fb.v[c] = load16(rs, 32 * D * 2 + (c * 64 + lane) * 16);
     };
-    auto compute_f = [&](FB& fb, uint32_t e) {
+    auto compute_f = [&](FB& fb, int t) {
+      const uint32_t e = uniform(int(list[t]));
       const int w = te_win(e), k = te_tile(e);
       const int valid = min(32, len_old - w * W - 32 * k);
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -412,56 +474,65 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
         st.o[nb] = mfma_bf16(as_bf16x8(fb.v[nb]), ph, st.o[nb]);
         st.o[nb] = mfma_bf16(as_bf16x8(fb.v[nb]), pl, st.o[nb]);
       }
-      if (rec_mass) tmass[(size_t(w) * TPW + k) * G + hn] = make_float2(rs, st.m_run);
+      if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
     };
     for (int cb = f_beg; cb < f_end; cb += kList) {
       const int ce = min(f_end, cb + kList), nt = ce - cb;
       build_list(TIER_F, cb, ce);
+      // two tiles in flight; a buffer is refilled as soon as its tile is
+      // consumed (sched_barrier keeps the loads ahead of the next tile's math)
       FB A, Bf;
-      int i = 0;
-      load_f(A, uniform(int(list[0])));
-      while (i < nt) {
-        if (i + 1 < nt) load_f(Bf, uniform(int(list[i + 1])));
-        compute_f(A, uniform(int(list[i])));
-        if (++i >= nt) break;
-        if (i + 1 < nt) load_f(A, uniform(int(list[i + 1])));
-        compute_f(Bf, uniform(int(list[i])));
-        ++i;
+      load_f(A, 0, nt);
+      load_f(Bf, 1, nt);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < nt; i += 2) {
+        compute_f(A, i);
+        if (i + 1 >= nt) break;
+        load_f(A, i + 2, nt);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_f(Bf, i + 1);
+        load_f(Bf, i + 3, nt);   // (empty past the end: one path back to the loop head)
+        __builtin_amdgcn_sched_barrier(0);
       }
+      drain_loads();   // the last (empty) prefetch: nothing pending into the next chunk
+      flush_masses(nt);
     }
   }
 
   // ---------------------------------------------------------- INT2 tiles
   {
+    f16x8 q4[KK];     // 4q in fp16, formed here so it never shares registers with the bf16 buffers
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(4.f * float(qb[kk][e]));
     const layout::LedgerTile LT(D);
     struct QB {
       uint32_t kc[CW], vc[CW], sc[CW];
     };
-    auto load_words = [&](const uint8_t* p, uint32_t (&w)[CW]) {
+    auto load_words = [&](__amdgpu_buffer_rsrc_t rs, int off, uint32_t (&w)[CW]) {
       if constexpr (CW == 4) {
-        const uint4 u = reinterpret_cast<const uint4*>(p)[lane];
+        const uint4 u = load16(rs, off + lane * 16);
         w[0] = u.x;
         w[1] = u.y;
         w[2] = u.z;
         w[3] = u.w;
       } else {
-        const uint2 u = reinterpret_cast<const uint2*>(p)[lane];
+        const uint2 u = load8(rs, off + lane * 8);
         w[0] = u.x;
         w[1] = u.y;
       }
     };
-    auto load_q = [&](QB& qq, uint32_t e) {
+    auto load_q = [&](QB& qq, int i, int nt) {
+      const uint32_t e = uniform(int(list[min(i, nt - 1)]));
       const uint8_t* t = pv.entry(seg, te_slot(e), kvh) + size_t(te_tile(e)) * LT.bytes;
-      load_words(t + LT.kc, qq.kc);
-      load_words(t + LT.vc, qq.vc);
-      load_words(t + LT.ks, qq.sc);
+      const auto rs = tile_rsrc(t, i < nt ? LT.bytes : 0);
+      load_words(rs, LT.kc, qq.kc);
+      load_words(rs, LT.vc, qq.vc);
+      load_words(rs, LT.ks, qq.sc);
     };
     uint8_t* scb = s_scb[wid];
-    f16x8* bh = reinterpret_cast<f16x8*>(s_bq[wid][0]);
-    f16x8* bl = reinterpret_cast<f16x8*>(s_bq[wid][1]);
-    float* cst = s_cst[wid];
-    auto compute_q = [&](QB& qq, uint32_t e) {
-      const int w = te_win(e), k = te_tile(e);
+    auto compute_q = [&](QB& qq, int t) {
       // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer
       if constexpr (CW == 4)
         reinterpret_cast<uint4*>(scb)[lane] = make_uint4(qq.sc[0], qq.sc[1], qq.sc[2], qq.sc[3]);
@@ -471,34 +542,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       const f16x8* km = reinterpret_cast<const f16x8*>(scb + 2 * D);      // [D]
       const f16x8* vs = reinterpret_cast<const f16x8*>(scb + 4 * D);      // [D/32][32]
       const f16x8* vm = reinterpret_cast<const f16x8*>(scb + 6 * D);
-      // 4 s q split into fp16 high + low parts, and the tile constant
-      // sum_d q (m - 4 s) in fp32, once per (head, dim) in a compact lane
-      // layout: item (h, c8) = head h, channels 8*c8..8*c8+7.
-#pragma unroll
-      for (int r = 0; r < kRounds; ++r) {
-        const int it = 64 * r + lane, h = it / (D / 8), c8 = it % (D / 8);
-        if (h < G) {
-          const f16x8 s8 = ks[c8], m8 = km[c8];
-          // 4 s q: fp16 product plus its exact fp16 residual (fma TwoProduct)
-          const f16x8 hi8 = qc[r] * s8;
-          const f16x8 lo8 = __builtin_elementwise_fma(qc[r], s8, -hi8);
-          float cp = 0.f;
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2)
-            cp = fmaf(float(qc[r][e2]), fmaf(float(m8[e2]), 0.25f, -float(s8[e2])), cp);
-          bh[h * (D / 8) + c8] = hi8;
-          bl[h * (D / 8) + c8] = lo8;
-#pragma unroll
-          for (int off = 1; off < D / 8; off <<= 1) cp += __shfl_xor(cp, off, 64);
-          if (c8 == 0) cst[h] = cp;
-        }
-      }
-      const int hh = hn < G ? hn : G - 1;
+      // Each lane forms its own B operand: 4 s q as an fp16 product plus its
+      // exact fp16 residual (fma TwoProduct), and its share of the tile
+      // constant sum_d q (m - 4 s) in fp32, completed across the 4 lane groups.
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      float cp = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const f16x8 qh = bh[hh * (D / 8) + 4 * kk + g];
-        const f16x8 ql = bl[hh * (D / 8) + 4 * kk + g];
+        const f16x8 s8 = ks[4 * kk + g], m8 = km[4 * kk + g];
+        const f16x8 qh = q4[kk] * s8;
+        const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2)
+          cp = fmaf(float(q4[kk][e2]), fmaf(float(m8[e2]), 0.25f, -float(s8[e2])), cp);
         const int c0 = kk, c1 = KK + kk;                               // chunks of blk 0 / 1
         const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1]) : decode_codes<0>(qq.kc[c0 >> 1]);
         const f16x8 a1 = (c1 & 1) ? decode_codes<1>(qq.kc[c1 >> 1]) : decode_codes<0>(qq.kc[c1 >> 1]);
@@ -507,7 +563,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
         s1 = mfma_f16(a1, qh, s1);
         s1 = mfma_f16(a1, ql, s1);
       }
-      const float bias0 = cst[hh];
+      // the MFMA result lanes (g, hn) hold head hn, as the B operand lanes do
+      const float bias0 = sum_rows(cp);
       float z[8], p[8], rs;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -542,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
           st.o[nb] = mfma_f16(av, pl, st.o[nb]);
         }
       }
-      if (rec_mass) tmass[(size_t(w) * TPW + k) * G + hn] = make_float2(rs, st.m_run);
+      if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
     };
     for (int cb = q_beg; cb < q_end; cb += kList) {
       const int ce = min(q_end, cb + kList), nt = ce - cb;
@@ -552,25 +609,27 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       QB A[kQGroup], Bq[kQGroup];
       auto load_group = [&](QB (&grp)[kQGroup], int i0) {
 #pragma unroll
-        for (int j = 0; j < kQGroup; ++j)
-          if (i0 + j < nt) load_q(grp[j], uniform(int(list[i0 + j])));
+        for (int j = 0; j < kQGroup; ++j) load_q(grp[j], i0 + j, nt);
       };
       auto compute_group = [&](QB (&grp)[kQGroup], int i0) {
 #pragma unroll
         for (int j = 0; j < kQGroup; ++j)
-          if (i0 + j < nt) compute_q(grp[j], uniform(int(list[i0 + j])));
+          if (i0 + j < nt) compute_q(grp[j], i0 + j);
       };
-      int i = 0;
       load_group(A, 0);
-      while (i < nt) {
-        if (i + kQGroup < nt) load_group(Bq, i + kQGroup);
+      load_group(Bq, kQGroup);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < nt; i += 2 * kQGroup) {
         compute_group(A, i);
-        i += kQGroup;
-        if (i >= nt) break;
-        if (i + kQGroup < nt) load_group(A, i + kQGroup);
-        compute_group(Bq, i);
-        i += kQGroup;
+        if (i + kQGroup >= nt) break;
+        load_group(A, i + 2 * kQGroup);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_group(Bq, i + kQGroup);
+        load_group(Bq, i + 3 * kQGroup);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      drain_loads();
+      flush_masses(nt);
     }
   }
 
@@ -588,101 +647,127 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     }
   }
   __syncthreads();
-  // partial of this workgroup: o [G][D], then max [G], then sum [G]
-  const int P = (G * (D + 2) + 3) & ~3;
-  float* part = a.partials + ((size_t(b) * pv.Hkv + kvh) * S + split) * P;
-  for (int idx = tid; idx < G * (D + 2); idx += 256) {
-    const int h = idx < G * D ? idx / D : (idx - G * D) % G;
+  // partial of this workgroup: o [G][D]; (max, sum) of each head to ml
+  float* part = a.partials + ((size_t(b) * pv.Hkv + kvh) * S + split) * G * D;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, s_wm[v][h]);
     float acc = 0.f;
-    if (idx >= G * D && idx < G * D + G) {
-      acc = M;
-    } else {
 #pragma unroll
-      for (int v = 0; v < kAttnWaves; ++v) {
-        const float sc = s_wm[v][h] == -INFINITY ? 0.f : fast_exp2(s_wm[v][h] - M);
-        if (idx >= G * D) {
-          acc += sc * s_wl[v][h];
-        } else {
-          const int d = idx % D;
-          acc += sc * (s_wo[v][h][d] + s_wb[v][h][d >> 5]);
-        }
-      }
+    for (int v = 0; v < kAttnWaves; ++v) {
+      const float sc = s_wm[v][h] == -INFINITY ? 0.f : fast_exp2(s_wm[v][h] - M);
+      acc += sc * (s_wo[v][h][d] + s_wb[v][h][d >> 5]);
     }
     part[idx] = acc;
+  }
+  if (tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, s_wm[v][tid]);
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < kAttnWaves; ++v)
+      L += s_wm[v][tid] == -INFINITY ? 0.f : fast_exp2(s_wm[v][tid] - M) * s_wl[v][tid];
+    a.ml[(size_t(b) * pv.Hq + size_t(kvh) * G + tid) * S + split] = make_float2(M, L);
   }
 }
 
 // --------------------------------------------------------------------------
-// Combine: blocks x < Hkv produce the output of kv head x of sequence y (and
-// store an appended token's K/V); blocks x >= Hkv normalise the window masses
-// of 256 windows for every query head, optionally adding them to the
-// cumulative scores.
+// Combine.  Blocks x < Hkv * (D / 32) produce 32 output channels of every
+// query head of kv head x / (D / 32) (the first block of a kv head also stores
+// an appended token's K/V); blocks beyond normalise the window masses of 32
+// windows for every query head, optionally adding them to the cumulative
+// scores.  Every block issues all of its loads before its first barrier.
+
+// x combined over the 32 lanes of its half-wave: DPP within each 16-lane row
+// (xor 1, xor 2, half-row mirror, row mirror), then the row pair.
+template <typename Op>
+__device__ inline float half_reduce(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Max and normaliser of one query head over the splits: lane c of a 32-lane
+// half-wave takes splits c and c + 32 (raw m, l pairs of the workgroups).
+__device__ inline float2 head_mz(float m0, float l0, float m1, float l1) {
+  const float M = half_reduce(fmaxf(m0, m1), [](float u, float v) { return fmaxf(u, v); });
+  float z = 0.f;
+  if (m0 != -INFINITY) z = l0 * fast_exp2(m0 - M);
+  if (m1 != -INFINITY) z = fmaf(l1, fast_exp2(m1 - M), z);
+  z = half_reduce(z, [](float u, float v) { return u + v; });
+  return make_float2(M, z);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, int acc_scores) {
-  __shared__ float s_scale[kMaxSplits * kGMax];
+  constexpr int kSlice = 32, NO = D / kSlice;
+  __shared__ float s_m[kMaxSplits * kGMax];
+  __shared__ float s_hm[kGMax], s_hz[kGMax];
   __shared__ float4 s_acc[256];
-  __shared__ float s_pm[256], s_pz[256];
-  extern __shared__ float s_mz[];            // mass blocks: max, normaliser [Hq], masses [64][Hq]
+  __shared__ int s_lv[kMassWindows];
+  extern __shared__ float s_dynf[];   // mass blocks: M, 1/Z [Hq], masses [kMassWindows][Hq], appended [Hq]
   const int b = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
   const int G = pv.G, Hkv = pv.Hkv, Hq = pv.Hq, S = a.splits, W = pv.W, maxw = pv.maxw;
   const int TPW = W / 32, seg = a.layer * pv.B + b;
-  const int P = (G * (D + 2) + 3) & ~3;
   const int32_t* info = a.app_info + 8 * b;
   const int app = info[0], slot = info[1], row = info[2], newwin = info[3], len_old = info[4];
   const int len = len_old + (app ? 1 : 0);
   const int n_old = windows_of(len_old, W), n_win = windows_of(len, W);
+  const int c32 = tid & 31, r8 = tid >> 5;   // (split lane, row of 32 threads)
 
-  if (x < Hkv) {
-    const int kvh = x;
-    const float* parts = a.partials + (size_t(b) * Hkv + kvh) * S * P;
-    float* s_lsum = reinterpret_cast<float*>(s_acc);
-    for (int i = tid; i < S * G; i += 256) {
-      s_scale[i] = parts[size_t(i / G) * P + G * D + i % G];
-      s_lsum[i] = parts[size_t(i / G) * P + G * D + G + i % G];
-    }
-    __syncthreads();
-    if (tid < G) {
-      float M = -INFINITY, Z = 0.f;
-      for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_scale[sp * G + tid]);
-      for (int sp = 0; sp < S; ++sp) {
-        const float ms = s_scale[sp * G + tid];
-        const float sc = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        s_scale[sp * G + tid] = sc;
-        Z += sc * s_lsum[sp * G + tid];
-      }
-      s_pz[tid] = Z;
-    }
-    __syncthreads();
-    __syncthreads();
-    const int items = G * D / 4, groups = 256 / items;
+  if (x < Hkv * NO) {
+    // -------------------------------------------------------- output slice
+    const int kvh = x / NO, sl = x % NO;
+    const auto rp = tile_rsrc(a.partials + (size_t(b) * Hkv + kvh) * S * G * D, S * G * D * 4);
+    const auto rml = tile_rsrc(a.ml + (size_t(b) * Hq + size_t(kvh) * G) * S, G * S * 8);
+    const int items = G * (kSlice / 4);   // (head, 4 channels)
+    const int groups = 256 / items;       // split groups, >= 4
     const int it = tid % items, grp = tid / items;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (grp < groups) {
-      const int h = (4 * it) / D;
-      const float4* po = reinterpret_cast<const float4*>(parts) + it;
-      // all of this thread's partial outputs in flight at once, 16 at a time
-      for (int sp0 = grp; sp0 < S; sp0 += 16 * groups) {
-        float4 v4[16];
+    const int h = it / (kSlice / 4);
+    const int d = sl * kSlice + 4 * (it % (kSlice / 4));
+    const bool act = grp < groups;
+    constexpr int kPer = kMaxSplits / 4;
+    float4 v4[kPer];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int sp = sp0 + j * groups;
-          v4[j] = sp < S ? po[size_t(sp) * (P / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int sp = sp0 + j * groups;
-          const float sc = sp < S ? s_scale[sp * G + h] : 0.f;
-          acc.x = fmaf(sc, v4[j].x, acc.x);
-          acc.y = fmaf(sc, v4[j].y, acc.y);
-          acc.z = fmaf(sc, v4[j].z, acc.z);
-          acc.w = fmaf(sc, v4[j].w, acc.w);
-        }
-      }
-      s_acc[grp * items + it] = acc;
+    for (int j = 0; j < kPer; ++j) {
+      const int sp = grp + j * groups;
+      const uint4 u = load16(rp, boff(act && sp < S, ((sp * G + h) * D + d) * 4));
+      v4[j] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     }
+    // row r8 (< G) reduces head r8: splits c32 and c32 + 32
+    const bool v0 = r8 < G && c32 < S, v1 = r8 < G && c32 + 32 < S;
+    const float2 u0 = as_f2(load8(rml, boff(v0, (r8 * S + c32) * 8)));
+    const float2 u1 = as_f2(load8(rml, boff(v1, (r8 * S + c32 + 32) * 8)));
+    const float m0 = v0 ? u0.x : -INFINITY, l0 = u0.y, m1 = v1 ? u1.x : -INFINITY, l1 = u1.y;
+    if (v0) s_m[c32 * G + r8] = m0;
+    if (v1) s_m[(c32 + 32) * G + r8] = m1;
+    const float2 mz = head_mz(m0, l0, m1, l1);
+    if (r8 < G && c32 == 0) {
+      s_hm[r8] = mz.x;
+      s_hz[r8] = mz.y;
+    }
+    __syncthreads();
+    const float M = s_hm[h];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int sp = grp + j * groups;
+      if (act && sp < S) {
+        const float ms = s_m[sp * G + h];
+        const float sc = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+        acc.x = fmaf(sc, v4[j].x, acc.x);
+        acc.y = fmaf(sc, v4[j].y, acc.y);
+        acc.z = fmaf(sc, v4[j].z, acc.z);
+        acc.w = fmaf(sc, v4[j].w, acc.w);
+      }
+    }
+    if (act) s_acc[tid] = acc;
     __syncthreads();
     if (tid < items) {
       float4 t4 = s_acc[tid];
@@ -690,17 +775,16 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
         const float4 u = s_acc[q2 * items + tid];
         t4.x += u.x; t4.y += u.y; t4.z += u.z; t4.w += u.w;
       }
-      const int h = (4 * tid) / D, d = (4 * tid) % D;
-      const float Z = s_pz[h], iz = Z > 0.f ? 1.f / Z : 0.f;
+      const float Z = s_hz[h], iz = Z > 0.f ? 1.f / Z : 0.f;
       *reinterpret_cast<float4*>(a.out + (size_t(b) * Hq + size_t(kvh) * G + h) * D + d) =
           make_float4(t4.x * iz, t4.y * iz, t4.z * iz, t4.w * iz);
     }
-    if (app) {
+    if (app && sl == 0) {
       // the appended token joins its window (no kernel of this step reads it)
       uint16_t* dst = pv.block(seg, slot, kvh);
-      for (int d = tid; d < D; d += 256) {
-        dst[layout::bf16_window_k(row, d, D)] = a.k_new[(size_t(b) * Hkv + kvh) * D + d];
-        dst[layout::bf16_window_v(row, d, D)] = a.v_new[(size_t(b) * Hkv + kvh) * D + d];
+      for (int dd = tid; dd < D; dd += 256) {
+        dst[layout::bf16_window_k(row, dd, D)] = a.k_new[(size_t(b) * Hkv + kvh) * D + dd];
+        dst[layout::bf16_window_v(row, dd, D)] = a.v_new[(size_t(b) * Hkv + kvh) * D + dd];
       }
       if (kvh == 0 && tid == 0) {
         if (newwin) pv.pages[size_t(seg) * maxw + n_old] = pe_make(TIER_F, false, slot, 0);
@@ -711,111 +795,123 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   }
 
   // ---------------------------------------------------------- window masses
-  // 64 windows per block; thread (window wl, head lane hq) takes heads hq, hq+4, ...
   if (!a.mass && !acc_scores) return;
-  const int w0 = (x - Hkv) * kMassWindows;
+  const int w0 = (x - Hkv * NO) * kMassWindows;
   if (w0 >= n_win) return;
-  float* s_M = s_mz;             // [Hq]
-  float* s_Zh = s_mz + Hq;       // [Hq]
-  float* s_mv = s_mz + 2 * Hq;   // [kMassWindows][Hq]
-  // per-head max and normaliser over all splits: threads (h, c) scan splits c, c + C, ...
-  const int hs = min(Hq, 256), C = max(1, 256 / Hq);
-  for (int h0 = 0; h0 < Hq; h0 += 256) {
-    const int h = h0 + tid % hs, c = tid / hs;
-    float M = -INFINITY, Z = 0.f;
-    if (h < Hq && c < C) {
-      const int kvh = h / G, hl = h % G;
-      const float* parts = a.partials + (size_t(b) * Hkv + kvh) * S * P + G * D;
-#pragma unroll 8
-      for (int sp = c; sp < S; sp += C) {
-        const float ms = parts[size_t(sp) * P + hl], ls = parts[size_t(sp) * P + G + hl];
-        if (ms != -INFINITY) {
-          const float mn = fmaxf(M, ms);
-          Z = Z * exp2f(M - mn) + ls * exp2f(ms - mn);
-          M = mn;
-        }
-      }
-    }
-    s_pm[tid] = M;
-    s_pz[tid] = Z;
-    __syncthreads();
-    if (tid < min(Hq - h0, 256)) {
-      float Mh = -INFINITY, Zh = 0.f;
-      for (int cc = 0; cc < C; ++cc) {
-        const float ms = s_pm[cc * hs + tid], zs = s_pz[cc * hs + tid];
-        if (ms == -INFINITY) continue;
-        const float mn = fmaxf(Mh, ms);
-        Zh = Zh * exp2f(Mh - mn) + zs * exp2f(ms - mn);
-        Mh = mn;
-      }
-      s_M[h0 + tid] = Mh;
-      s_Zh[h0 + tid] = Zh;
-    }
-    __syncthreads();
-  }
-  const int wl = tid % kMassWindows, hq = tid / kMassWindows;
+  float* s_M = s_dynf;             // [Hq]
+  float* s_Zh = s_dynf + Hq;       // [Hq] 1 / normaliser
+  float* s_mv = s_dynf + 2 * Hq;   // [kMassWindows][Hq]
+  // thread (head sub-row hs, window wl, tile k): heads hs, hs + HP, ...; the
+  // TPW tiles of a window sit in adjacent lanes, so each load instruction
+  // reads consecutive records of one head
+  const int HT = kMassWindows * TPW, HP = 256 / HT;   // threads per head, heads per pass
+  const int hs = tid / HT, wl = (tid % HT) / TPW, k = tid % TPW;
   const int w = w0 + wl;
   const bool in = w < n_win;
+  constexpr int kBatch = 16;
+  const int passes = (Hq + HP - 1) / HP;
+  const auto rtm = tile_rsrc(a.tile_mass + size_t(b) * Hq * maxw * TPW, Hq * maxw * TPW * 8);
+  const auto rml = tile_rsrc(a.ml + size_t(b) * Hq * S, Hq * S * 8);
+  const auto rpg = tile_rsrc(pv.pages + size_t(seg) * maxw, maxw * 4);
+  const auto rsc = tile_rsrc(pv.scores + size_t(seg) * maxw, maxw * 4);
+  float2* s_app = reinterpret_cast<float2*>(s_dynf + (2 + kMassWindows) * Hq);   // [Hq]
+  // the window the appended token joins adds that token's record
+  const bool vwin = app && w == len_old / W;
+  // t[p]: tile record of head (p0 + p) * HP + hs
+  auto tile_masses = [&](int p0, float2 (&t)[kBatch]) {
+#pragma unroll
+    for (int p = 0; p < kBatch; ++p) {
+      const int h = (p0 + p) * HP + hs;
+      const bool hv = p0 + p < passes && h < Hq;
+      t[p] = as_f2(load8(rtm, boff(hv && w < maxw, ((h * maxw + w) * TPW + k) * 8)));
+    }
+  };
+  // loads of the first batch in flight together: tile masses, the page entry,
+  // the score, the appended token's records and the (m, l) pairs of the
+  // per-head reductions
+  float2 t1[kBatch];
+  tile_masses(0, t1);
+  if (app) {
+    const auto rap = tile_rsrc(a.app_mass + size_t(b) * Hq, Hq * 8);
+    for (int h = tid; h < Hq; h += 256) s_app[h] = as_f2(load8(rap, h * 8));
+  }
+  const uint32_t pe = load4(rpg, boff(in && w < n_old, w * 4));
+  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tid < kMassWindows && w0 + tid < maxw, (w0 + tid) * 4)));
+  for (int h0 = 0; h0 < Hq; h0 += 32) {
+    float2 mr[4][2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int h = h0 + p * 8 + r8;
+      const bool v0 = h < Hq && c32 < S, v1 = h < Hq && c32 + 32 < S;
+      mr[p][0] = as_f2(load8(rml, boff(v0, (h * S + c32) * 8)));
+      mr[p][1] = as_f2(load8(rml, boff(v1, (h * S + c32 + 32) * 8)));
+      if (!v0) mr[p][0].x = -INFINITY;
+      if (!v1) mr[p][1].x = -INFINITY;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int h = h0 + p * 8 + r8;
+      const float2 mz = head_mz(mr[p][0].x, mr[p][0].y, mr[p][1].x, mr[p][1].y);
+      if (h < Hq && c32 == 0) {
+        s_M[h] = mz.x;
+        s_Zh[h] = mz.y > 0.f ? 1.f / mz.y : 0.f;   // reciprocal of the normaliser
+      }
+    }
+  }
+  __syncthreads();
   bool live = false;
   int vt = 0;
   if (in) {
     if (w < n_old) {
-      live = pe_tier(pv.pages[size_t(seg) * maxw + w]) != TIER_E;
+      live = pe_tier(pe) != TIER_E;
       vt = (min(W, len_old - w * W) + 31) / 32;
     } else {
       live = true;   // the window the appended token opened
     }
   }
-  const bool vwin = app && w == len_old / W;
-  // tile masses of 4 heads (all their tiles) in flight at once
-  constexpr int HL = 256 / kMassWindows;   // head lanes per window
-  const float2* tm0 = reinterpret_cast<const float2*>(a.tile_mass);
-  for (int h0 = hq; h0 < Hq; h0 += 4 * HL) {
-    float2 t[4][8];
+  auto masses = [&](int p0, const float2 (&t)[kBatch]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = h0 + j * HL;
-      const int kvh = h / G, hl = h % G;
-      const float2* tm = tm0 + (size_t(b) * Hkv + kvh) * (size_t(maxw) * TPW + 1) * G;
-      const bool on = in && live && h < Hq;
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        t[j][k] = (on && k < vt) ? tm[(size_t(w) * TPW + k) * G + hl] : make_float2(0.f, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = h0 + j * HL;
-      if (h >= Hq) break;
-      float mv = 0.f;
-      if (in && live) {
-        const float M = s_M[h], Z = s_Zh[h];
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k < vt) acc += t[j][k].x * exp2f(t[j][k].y - M);
-        if (vwin) {
-          const int kvh = h / G, hl = h % G;
-          const float2 tv = tm0[(size_t(b) * Hkv + kvh) * (size_t(maxw) * TPW + 1) * G +
-                                size_t(maxw) * TPW * G + hl];
-          acc += tv.x * exp2f(tv.y - M);
-        }
-        mv = Z > 0.f ? acc / Z : 0.f;
+    for (int p = 0; p < kBatch; ++p) {
+      if (p0 + p >= passes) break;
+      const int h = (p0 + p) * HP + hs;
+      const bool hv = h < Hq;
+      const float M = hv ? s_M[h] : 0.f;
+      float acc = (hv && live && k < vt) ? t[p].x * fast_exp2(t[p].y - M) : 0.f;
+      // sum over the window's TPW adjacent lanes
+      if (TPW >= 2) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0xB1, 0xF, 0xF, false));
+      if (TPW >= 4) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x4E, 0xF, 0xF, false));
+      if (TPW >= 8) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x141, 0xF, 0xF, false));
+      if (hv && k == 0) {
+        if (vwin) acc += s_app[h].x * fast_exp2(s_app[h].y - M);
+        s_mv[wl * Hq + h] = (in && live) ? acc * s_Zh[h] : 0.f;
       }
-      if (in && a.mass) a.mass[(size_t(b) * Hq + h) * maxw + w] = mv;
-      s_mv[wl * Hq + h] = mv;
+    }
+  };
+  masses(0, t1);
+  for (int p0 = kBatch; p0 < passes; p0 += kBatch) {
+    float2 t2[kBatch];
+    tile_masses(p0, t2);
+    masses(p0, t2);
+  }
+  if (hs == 0 && k == 0) s_lv[wl] = in && live;
+  __syncthreads();
+  // masses out in window order (32 consecutive windows per head)
+  if (a.mass) {
+    for (int idx = tid; idx < Hq * kMassWindows; idx += 256) {
+      const int h = idx / kMassWindows, ww = idx % kMassWindows;
+      if (w0 + ww < n_win) a.mass[(size_t(b) * Hq + h) * maxw + w0 + ww] = s_mv[ww * Hq + h];
     }
   }
-  __syncthreads();
-  if (acc_scores && hq == 0 && in && live) {
+  if (acc_scores && tid < kMassWindows && s_lv[tid]) {
     float ssum = 0.f;
-    for (int h = 0; h < Hq; ++h) ssum += s_mv[wl * Hq + h];   // heads in order
-    pv.scores[size_t(seg) * maxw + w] += ssum;
+    for (int h = 0; h < Hq; ++h) ssum += s_mv[tid * Hq + h];   // heads in order
+    pv.scores[size_t(seg) * maxw + w0 + tid] = s_old + ssum;
   }
 }
 
 template <int D>
 static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream_t s) {
-  const size_t shm = size_t((pv.nb + 31) / 32) * 4;
+  const size_t shm = (2 * size_t(a.plan_words) + (pv.nb + 31) / 32) * 4;
   if (a.ev_start || a.ev_stop) {
     hipExtLaunchKernelGGL((attn_kernel<D>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
                           a.ev_start, a.ev_stop, 0u, pv, a);
@@ -825,8 +921,8 @@ static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int mass_blocks = (a.mass || a.acc_scores) ? (pv.maxw + kMassWindows - 1) / kMassWindows : 0;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(pv.Hkv + mass_blocks, pv.B), dim3(256),
-                     size_t(2 + kMassWindows) * pv.Hq * 4, s, pv, a, a.acc_scores);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(pv.Hkv * (D / 32) + mass_blocks, pv.B), dim3(256),
+                     size_t(4 + kMassWindows) * pv.Hq * 4, s, pv, a, a.acc_scores);
   return hipGetLastError();
 }
 

@@ -79,11 +79,14 @@ AttnWorkspace attn_workspace(const Geometry& g, int splits) {
   const kv_pool_config& c = g.cfg;
   AttnWorkspace w;
   const size_t pairs = size_t(c.batch) * c.kv_heads;
-  const size_t per = (size_t(g.group) * (c.head_dim + 2) + 3) & ~size_t(3);
-  w.partials = align256(pairs * splits * per * 4);
-  w.tile_mass = align256(pairs * (size_t(c.max_windows) * (c.window / kTile) + 1) * g.group * 2 * 4);
-  w.app_info = align256(size_t(c.batch) * 8 * 4);
-  w.total = w.partials + w.tile_mass + w.app_info;
+  const size_t qrows = size_t(c.batch) * c.q_heads;
+  size_t off = 0;
+  w.partials = off;  off += align256(pairs * splits * g.group * c.head_dim * 4);
+  w.ml = off;        off += align256(qrows * splits * 8);
+  w.tile_mass = off; off += align256(qrows * size_t(c.max_windows) * (c.window / kTile) * 8);
+  w.app_mass = off;  off += align256(qrows * 8);
+  w.app_info = off;  off += align256(size_t(c.batch) * 8 * 4);
+  w.total = off;
   return w;
 }
 

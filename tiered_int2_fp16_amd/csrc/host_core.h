@@ -40,9 +40,12 @@ bool geometry_init(const kv_pool_config& cfg, Geometry* g, std::string* err);
 // Attention split-K factor: workgroups per (sequence, kv head).
 int attn_splits(const Geometry& g, int compute_units);
 
+// Byte offsets of the attention workspace regions (each 256-byte aligned).
 struct AttnWorkspace {
-  size_t partials = 0;   // float [batch][kv_heads][splits][P]: o [G][D], max [G], sum [G], P % 4 == 0
-  size_t tile_mass = 0;  // float [batch][kv_heads][max_windows*W/32 + 1][group][2]
+  size_t partials = 0;   // float [batch][kv_heads][splits][group][D]: unnormalised outputs
+  size_t ml = 0;         // float2 [batch][q_heads][splits]: running max, sum of each workgroup
+  size_t tile_mass = 0;  // float2 [batch][q_heads][max_windows*W/32]: raw tile mass, its max
+  size_t app_mass = 0;   // float2 [batch][q_heads]: the same for an appended token
   size_t app_info = 0;   // int [batch][8]: append decision of the step
   size_t total = 0;
 };

@@ -24,10 +24,13 @@ struct AttnArgs {
   const uint16_t* v_new;
   float* out;
   float* mass;
-  float* partials;
-  float* tile_mass;
+  float* partials;      // [batch][kv_heads][splits][group][D]
+  float2* ml;           // [batch][q_heads][splits]: (max, sum)
+  float2* tile_mass;    // [batch][q_heads][max_windows*W/32]: (raw mass, max)
+  float2* app_mass;     // [batch][q_heads]
   int32_t* app_info;    // [batch][8] append decision of this step (workspace)
   int splits;
+  int plan_words;       // page-table entries staged in LDS: max_windows rounded up to 256
   int acc_scores;       // combine also adds the window masses to the scores
   hipEvent_t ev_start;  // optional dispatch timing events (may be null)
   hipEvent_t ev_stop;
