@@ -55,6 +55,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGMax = 8;     // query heads per kv head supported
@@ -125,17 +126,26 @@ __device__ inline uint2 load8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// (m & y) | (~m & c) in one instruction (v_bfi_b32)
+__device__ inline uint32_t bit_select(uint32_t m, uint32_t y, uint32_t c) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(y), "v"(c));
+  return r;
+}
+
 // Eight INT2 codes of one operand chunk -> fp16 (1 + c/4).  Word X holds the
 // fields of chunks 2w (SEL 0) and 2w+1 (SEL 1); register j takes the fields
-// j + 4*SEL (low half) and j + 4*SEL + 8 (high half), 16 bits apart.
+// j + 4*SEL (low half) and j + 4*SEL + 8 (high half), 16 bits apart: one shift
+// puts both at mantissa bits 8-9 and a bit select adds the exponent of 1.0.
+// `mask` = 0x03000300 and `one` = 0x3C003C00 come in registers.
 template <int SEL>
-__device__ inline f16x8 decode_codes(uint32_t X) {
+__device__ inline f16x8 decode_codes(uint32_t X, uint32_t mask, uint32_t one) {
   uint32_t r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int sh = 2 * (j + 4 * SEL);
     const uint32_t y = sh <= 8 ? (X << (8 - sh)) : (X >> (sh - 8));
-    r[j] = (y & 0x03000300u) | 0x3C003C00u;
+    r[j] = bit_select(mask, y, one);
   }
   return __builtin_bit_cast(f16x8, make_uint4(r[0], r[1], r[2], r[3]));
 }
@@ -501,6 +511,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
 
   // ---------------------------------------------------------- INT2 tiles
   {
+    const uint32_t kMaskR = 0x03000300u, kOneR = 0x3C003C00u;   // decode constants
     f16x8 q4[KK];     // 4q in fp16, formed here so it never shares registers with the bf16 buffers
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -544,27 +555,33 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       const f16x8* vm = reinterpret_cast<const f16x8*>(scb + 6 * D);
       // Each lane forms its own B operand: 4 s q as an fp16 product plus its
       // exact fp16 residual (fma TwoProduct), and its share of the tile
-      // constant sum_d q (m - 4 s) in fp32, completed across the 4 lane groups.
+      // constant sum_d q (m - 4 s) = sum 4q m / 4 - sum 4q s (fp16 pairs,
+      // fp32 sums), completed across the 4 lane groups.
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      float cp = 0.f;
+      float cm = 0.f, cs = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const f16x8 s8 = ks[4 * kk + g], m8 = km[4 * kk + g];
         const f16x8 qh = q4[kk] * s8;
         const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
 #pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2)
-          cp = fmaf(float(q4[kk][e2]), fmaf(float(m8[e2]), 0.25f, -float(s8[e2])), cp);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const f16x2 qq2 = {q4[kk][2 * e2], q4[kk][2 * e2 + 1]};
+          cm = __builtin_amdgcn_fdot2(qq2, f16x2{m8[2 * e2], m8[2 * e2 + 1]}, cm, false);
+          cs = __builtin_amdgcn_fdot2(qq2, f16x2{s8[2 * e2], s8[2 * e2 + 1]}, cs, false);
+        }
         const int c0 = kk, c1 = KK + kk;                               // chunks of blk 0 / 1
-        const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1]) : decode_codes<0>(qq.kc[c0 >> 1]);
-        const f16x8 a1 = (c1 & 1) ? decode_codes<1>(qq.kc[c1 >> 1]) : decode_codes<0>(qq.kc[c1 >> 1]);
+        const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1], kMaskR, kOneR)
+                                  : decode_codes<0>(qq.kc[c0 >> 1], kMaskR, kOneR);
+        const f16x8 a1 = (c1 & 1) ? decode_codes<1>(qq.kc[c1 >> 1], kMaskR, kOneR)
+                                  : decode_codes<0>(qq.kc[c1 >> 1], kMaskR, kOneR);
         s0 = mfma_f16(a0, qh, s0);
         s0 = mfma_f16(a0, ql, s0);
         s1 = mfma_f16(a1, qh, s1);
         s1 = mfma_f16(a1, ql, s1);
       }
       // the MFMA result lanes (g, hn) hold head hn, as the B operand lanes do
-      const float bias0 = sum_rows(cp);
+      const float bias0 = sum_rows(fmaf(cm, 0.25f, -cs));
       float z[8], p[8], rs;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -581,11 +598,23 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
         p4[e2] = (_Float16)x;
         p4l[e2] = (_Float16)(x - float(p4[e2]));
       }
-      const int jr = hn & (D / 32 - 1);   // min-term row = 32-channel group (rows >= D/32 unused)
-      const f16x8 mv = (vm[4 * jr + g] + vs[4 * jr + g] * (_Float16)1.5f) * (_Float16)0.25f;
-      st.ob = mfma_f16(mv, p4, st.ob);
-      const f16x8 ctr = {(_Float16)1.375f, (_Float16)1.375f, (_Float16)1.375f, (_Float16)1.375f,
-                         (_Float16)1.375f, (_Float16)1.375f, (_Float16)1.375f, (_Float16)1.375f};
+      // v = (m' - 4 s') + (1 + c/4) 4 s': the min term sum_t 4p (m'/4 - s') on
+      // the MFMA with both factors as fp16 high + low parts (row = 32-channel
+      // group jr; rows >= D/32 repeat them and are not read)
+      {
+        const int jr = hn & (D / 32 - 1);
+        const f16x8 vm8 = vm[4 * jr + g], vs8 = vs[4 * jr + g];
+        f16x8 mvh, mvl;
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) {
+          const float x = fmaf(float(vm8[e2]), 0.25f, -float(vs8[e2]));
+          mvh[e2] = (_Float16)x;
+          mvl[e2] = (_Float16)(x - float(mvh[e2]));
+        }
+        st.ob = mfma_f16(mvh, p4, st.ob);
+        st.ob = mfma_f16(mvh, p4l, st.ob);
+        st.ob = mfma_f16(mvl, p4, st.ob);
+      }
 #pragma unroll
       for (int jd = 0; jd < D / 32; ++jd) {
         const f16x8 sv = vs[4 * jd + g];
@@ -594,7 +623,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int nb = 2 * jd + h2;
-          const f16x8 av = ((nb & 1) ? decode_codes<1>(qq.vc[nb >> 1]) : decode_codes<0>(qq.vc[nb >> 1])) - ctr;
+          const f16x8 av = (nb & 1) ? decode_codes<1>(qq.vc[nb >> 1], kMaskR, kOneR)
+                                    : decode_codes<0>(qq.vc[nb >> 1], kMaskR, kOneR);
           st.o[nb] = mfma_f16(av, ph, st.o[nb]);
           st.o[nb] = mfma_f16(av, pl, st.o[nb]);
         }
@@ -710,7 +740,6 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   __shared__ float s_m[kMaxSplits * kGMax];
   __shared__ float s_hm[kGMax], s_hz[kGMax];
   __shared__ float4 s_acc[256];
-  __shared__ int s_lv[kMassWindows];
   extern __shared__ float s_dynf[];   // mass blocks: M, 1/Z [Hq], masses [kMassWindows][Hq], appended [Hq]
   const int b = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
   const int G = pv.G, Hkv = pv.Hkv, Hq = pv.Hq, S = a.splits, W = pv.W, maxw = pv.maxw;
@@ -801,42 +830,36 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   float* s_M = s_dynf;             // [Hq]
   float* s_Zh = s_dynf + Hq;       // [Hq] 1 / normaliser
   float* s_mv = s_dynf + 2 * Hq;   // [kMassWindows][Hq]
-  // thread (head sub-row hs, window wl, tile k): heads hs, hs + HP, ...; the
-  // TPW tiles of a window sit in adjacent lanes, so each load instruction
-  // reads consecutive records of one head
-  const int HT = kMassWindows * TPW, HP = 256 / HT;   // threads per head, heads per pass
-  const int hs = tid / HT, wl = (tid % HT) / TPW, k = tid % TPW;
-  const int w = w0 + wl;
+  float2* s_app = reinterpret_cast<float2*>(s_dynf + (2 + kMassWindows) * Hq);   // [Hq]
+  // thread (window wl = tid % 32, head row) takes the (head, window) pairs
+  // h = tid / 32 + 8 i: the TPW tile records of a pair are contiguous
+  const int wl = c32, w = w0 + wl;
   const bool in = w < n_win;
-  constexpr int kBatch = 16;
-  const int passes = (Hq + HP - 1) / HP;
+  constexpr int kPairs = 4, kTiles = 8;   // pairs per batch; tiles per window at most
   const auto rtm = tile_rsrc(a.tile_mass + size_t(b) * Hq * maxw * TPW, Hq * maxw * TPW * 8);
   const auto rml = tile_rsrc(a.ml + size_t(b) * Hq * S, Hq * S * 8);
   const auto rpg = tile_rsrc(pv.pages + size_t(seg) * maxw, maxw * 4);
   const auto rsc = tile_rsrc(pv.scores + size_t(seg) * maxw, maxw * 4);
-  float2* s_app = reinterpret_cast<float2*>(s_dynf + (2 + kMassWindows) * Hq);   // [Hq]
-  // the window the appended token joins adds that token's record
-  const bool vwin = app && w == len_old / W;
-  // t[p]: tile record of head (p0 + p) * HP + hs
-  auto tile_masses = [&](int p0, float2 (&t)[kBatch]) {
+  auto tile_masses = [&](int h0, float2 (&t)[kPairs][kTiles]) {
 #pragma unroll
-    for (int p = 0; p < kBatch; ++p) {
-      const int h = (p0 + p) * HP + hs;
-      const bool hv = p0 + p < passes && h < Hq;
-      t[p] = as_f2(load8(rtm, boff(hv && w < maxw, ((h * maxw + w) * TPW + k) * 8)));
+    for (int i = 0; i < kPairs; ++i) {
+      const int h = h0 + 8 * i + r8;
+#pragma unroll
+      for (int k = 0; k < kTiles; ++k)
+        t[i][k] = as_f2(load8(rtm, boff(h < Hq && w < maxw && k < TPW, ((h * maxw + w) * TPW + k) * 8)));
     }
   };
   // loads of the first batch in flight together: tile masses, the page entry,
   // the score, the appended token's records and the (m, l) pairs of the
   // per-head reductions
-  float2 t1[kBatch];
+  float2 t1[kPairs][kTiles];
   tile_masses(0, t1);
+  const uint32_t pe = load4(rpg, boff(in && w < n_old, w * 4));
+  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tid < kMassWindows && w < maxw, w * 4)));
   if (app) {
     const auto rap = tile_rsrc(a.app_mass + size_t(b) * Hq, Hq * 8);
     for (int h = tid; h < Hq; h += 256) s_app[h] = as_f2(load8(rap, h * 8));
   }
-  const uint32_t pe = load4(rpg, boff(in && w < n_old, w * 4));
-  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tid < kMassWindows && w0 + tid < maxw, (w0 + tid) * 4)));
   for (int h0 = 0; h0 < Hq; h0 += 32) {
     float2 mr[4][2];
 #pragma unroll
@@ -869,43 +892,34 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       live = true;   // the window the appended token opened
     }
   }
-  auto masses = [&](int p0, const float2 (&t)[kBatch]) {
+  const bool vwin = app && w == len_old / W;
+  auto masses = [&](int h0, const float2 (&t)[kPairs][kTiles]) {
 #pragma unroll
-    for (int p = 0; p < kBatch; ++p) {
-      if (p0 + p >= passes) break;
-      const int h = (p0 + p) * HP + hs;
-      const bool hv = h < Hq;
-      const float M = hv ? s_M[h] : 0.f;
-      float acc = (hv && live && k < vt) ? t[p].x * fast_exp2(t[p].y - M) : 0.f;
-      // sum over the window's TPW adjacent lanes
-      if (TPW >= 2) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0xB1, 0xF, 0xF, false));
-      if (TPW >= 4) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x4E, 0xF, 0xF, false));
-      if (TPW >= 8) acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), 0x141, 0xF, 0xF, false));
-      if (hv && k == 0) {
-        if (vwin) acc += s_app[h].x * fast_exp2(s_app[h].y - M);
-        s_mv[wl * Hq + h] = (in && live) ? acc * s_Zh[h] : 0.f;
-      }
+    for (int i = 0; i < kPairs; ++i) {
+      const int h = h0 + 8 * i + r8;
+      if (h >= Hq) break;
+      const float M = s_M[h];
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < kTiles; ++k)
+        if (k < vt) acc += t[i][k].x * fast_exp2(t[i][k].y - M);
+      if (vwin) acc += s_app[h].x * fast_exp2(s_app[h].y - M);
+      const float mv = (in && live) ? acc * s_Zh[h] : 0.f;
+      if (in && a.mass) a.mass[(size_t(b) * Hq + h) * maxw + w] = mv;
+      s_mv[wl * Hq + h] = mv;
     }
   };
   masses(0, t1);
-  for (int p0 = kBatch; p0 < passes; p0 += kBatch) {
-    float2 t2[kBatch];
-    tile_masses(p0, t2);
-    masses(p0, t2);
+  for (int h0 = 8 * kPairs; h0 < Hq; h0 += 8 * kPairs) {
+    float2 t2[kPairs][kTiles];
+    tile_masses(h0, t2);
+    masses(h0, t2);
   }
-  if (hs == 0 && k == 0) s_lv[wl] = in && live;
   __syncthreads();
-  // masses out in window order (32 consecutive windows per head)
-  if (a.mass) {
-    for (int idx = tid; idx < Hq * kMassWindows; idx += 256) {
-      const int h = idx / kMassWindows, ww = idx % kMassWindows;
-      if (w0 + ww < n_win) a.mass[(size_t(b) * Hq + h) * maxw + w0 + ww] = s_mv[ww * Hq + h];
-    }
-  }
-  if (acc_scores && tid < kMassWindows && s_lv[tid]) {
+  if (acc_scores && tid < kMassWindows && in && live) {
     float ssum = 0.f;
     for (int h = 0; h < Hq; ++h) ssum += s_mv[tid * Hq + h];   // heads in order
-    pv.scores[size_t(seg) * maxw + w0 + tid] = s_old + ssum;
+    pv.scores[size_t(seg) * maxw + w] = s_old + ssum;
   }
 }
 
