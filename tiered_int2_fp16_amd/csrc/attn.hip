@@ -59,7 +59,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGMax = 8;     // query heads per kv head supported
-constexpr int kWq = 5;       // weight of an INT2 tile (a bf16 tile weighs 16)
+constexpr int kWq = 9;       // weight of an INT2 tile (a bf16 tile weighs 16; set by measurement)
 constexpr int kMaxSplits = 64;
 constexpr int kMassWindows = 32;   // windows per mass block of the combine kernel
 

@@ -59,13 +59,13 @@ __device__ inline void device_tier_counts(int n, int R, double beta, double phi,
 __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, double beta, double phi,
                                                      int32_t* transitions, int32_t* counts) {
   extern __shared__ uint32_t smem[];
-  const int b = blockIdx.x, seg = layer * pv.B + b;
-  const int maxw = pv.maxw;
-  uint32_t* pages = smem;                                    // [maxw]
-  float* S = reinterpret_cast<float*>(smem + maxw);          // [maxw]
-  uint8_t* newt = reinterpret_cast<uint8_t*>(smem + 2 * maxw);  // [maxw]
+  const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
+  const int maxw = pv.maxw, kpad = (maxw + 7) & ~7;
+  float* key = reinterpret_cast<float*>(smem);               // [kpad] score of eligible windows, else NaN
+  int* rank = reinterpret_cast<int*>(smem + kpad);           // [maxw]
+  uint32_t* pages = smem + kpad + maxw;                      // [maxw]
+  uint8_t* newt = reinterpret_cast<uint8_t*>(smem + kpad + 2 * maxw);  // [maxw]
   __shared__ int wave_tot[16][4];
-  __shared__ int base[4];
   const int len = pv.tokens[seg];
   const int n = windows_of(len, pv.W);
   const int fr = n - pv.R > 0 ? n - pv.R : 0;  // first recent window
@@ -75,27 +75,52 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
   nf = nf > 0 ? nf : 0;
   uint32_t* gp = pv.pages + size_t(seg) * maxw;
   const float* gs = pv.scores + size_t(seg) * maxw;
-  for (int w = threadIdx.x; w < n; w += blockDim.x) {
+  const int fpad = (fr + 7) & ~7;
+  for (int w = tid; w < fpad; w += blockDim.x) {
+    float k = __builtin_nanf("");
+    if (w < fr) {
+      const uint32_t e = gp[w];
+      if (pe_tier(e) != TIER_E) k = gs[w];
+    }
+    key[w] = k;
+  }
+  for (int w = tid; w < n; w += blockDim.x) {
     pages[w] = gp[w];
-    S[w] = gs[w];
+    rank[w] = 0;
   }
   __syncthreads();
-  for (int w = threadIdx.x; w < n; w += blockDim.x) {
-    const uint32_t e = pages[w];
-    const int t = pe_tier(e);
+  // rank[w] = number of eligible x with S[x] > S[w], or S[x] == S[w] and x < w
+  // (NaN keys never compare).  Thread jobs (w, part): each part counts one
+  // slice of x, eight keys per step.
+  {
+    const int parts = fr > 0 ? max(1, min(8, int(blockDim.x) / fr)) : 1;
+    const int chunk = ((fpad / 8 + parts - 1) / parts) * 8;
+    for (int job = tid; job < fr * parts; job += blockDim.x) {
+      const int w = job % fr, part = job / fr;
+      const float sw = key[w];
+      if (sw != sw) continue;   // not eligible
+      const int x0 = part * chunk, x1 = min(fpad, x0 + chunk);
+      int cnt = 0;
+      for (int x = x0; x < x1; x += 8) {
+        const float4 a = *reinterpret_cast<const float4*>(key + x);
+        const float4 c = *reinterpret_cast<const float4*>(key + x + 4);
+        const float k8[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cnt += (k8[j] > sw) || (k8[j] == sw && x + j < w);
+      }
+      if (cnt) atomicAdd(&rank[w], cnt);
+    }
+  }
+  __syncthreads();
+  for (int w = tid; w < n; w += blockDim.x) {
+    const int t = pe_tier(pages[w]);
     int nt = t;
     if (t != TIER_E) {
       if (w >= fr) {
         nt = TIER_F;
       } else {
-        const float sw = S[w];
-        int rank = 0;
-        for (int x = 0; x < fr; ++x) {
-          if (pe_tier(pages[x]) == TIER_E) continue;
-          const float sx = S[x];
-          rank += (sx > sw) || (sx == sw && x < w);
-        }
-        nt = rank < nf ? TIER_F : (rank < nf + n_lo ? TIER_Q : TIER_E);
+        const int r = rank[w];
+        nt = r < nf ? TIER_F : (r < nf + n_lo ? TIER_Q : TIER_E);
       }
     }
     newt[w] = uint8_t(nt);
@@ -129,7 +154,6 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
   if (threadIdx.x < 4) {
     int tot = 0;
     for (int i = 0; i < nw; ++i) tot += wave_tot[i][threadIdx.x];
-    base[threadIdx.x] = tot;
     if (counts) counts[threadIdx.x * pv.B + b] = tot;
   }
 #pragma unroll
@@ -162,7 +186,7 @@ hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, 
     if (e != hipSuccess) return e;
   }
   if (do_route) {
-    const size_t shm = size_t(pv.maxw) * 9;
+    const size_t shm = size_t((pv.maxw + 7) & ~7) * 4 + size_t(pv.maxw) * 9;
     hipLaunchKernelGGL(route_kernel, dim3(pv.B), dim3(1024), shm, s, pv, layer, beta, phi, transitions,
                        counts);
     return hipGetLastError();

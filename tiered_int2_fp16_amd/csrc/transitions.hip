@@ -109,36 +109,54 @@ struct WorkItem {
   int w, src, dst, flag;  // flag 1: move bytes; 2: tier flip only; 0: invalid
 };
 
-__device__ inline int find_free(uint32_t* bits, int nbits) {
-  for (int word = 0; word * 32 < nbits; ++word) {
-    uint32_t x = ~bits[word];
+// Lowest free slot at or after word *cursor (slots are taken in ascending
+// order, so the words before the cursor are full); marks it used.
+__device__ inline int take_free(uint32_t* bits, int nbits, int* cursor) {
+  for (int word = *cursor; word * 32 < nbits; ++word) {
+    const uint32_t x = ~bits[word];
     if (x) {
       const int j = word * 32 + __builtin_ctz(x);
       if (j >= nbits) return -1;
       bits[word] |= 1u << (j & 31);
+      *cursor = word;
       return j;
     }
   }
+  *cursor = (nbits + 31) / 32;
   return -1;
 }
 
 // promote == false: demote plan (ledger slots); true: promote plan (bf16 slots).
+// One workgroup per sequence.  The page table, the occupied-slot bitmap and
+// the item list are staged in LDS; items are then validated and given slots
+// in list order (the lowest free slot each), and the page table is written
+// back.
 __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const int32_t* items, int stride,
                                                    const int32_t* counts, int promote) {
   extern __shared__ uint32_t smem[];
-  const int b = blockIdx.x, seg = layer * pv.B + b;
+  const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
   const int maxw = pv.maxw, W = pv.W;
   const int nslots = promote ? pv.nb : pv.nl;
   const int words = (nslots + 31) / 32;
-  uint32_t* pages = smem;
-  uint32_t* used = smem + maxw;
+  const int cap = stride < maxw ? stride : maxw;
+  uint32_t* pages = smem;                                         // [maxw]
+  uint32_t* used = smem + maxw;                                   // [words]
+  int32_t* item_w = reinterpret_cast<int32_t*>(used + words);    // [cap]
   const int len = pv.tokens[seg];
   const int n = windows_of(len, W);
   uint32_t* gp = pv.pages + size_t(seg) * maxw;
-  for (int w = threadIdx.x; w < maxw; w += blockDim.x) pages[w] = gp[w];
-  for (int i = threadIdx.x; i < words; i += blockDim.x) used[i] = 0u;
+  int cnt = counts[b];
+  int errs = 0;
+  if (cnt < 0) cnt = 0;
+  if (cnt > cap) {
+    cnt = cap;
+    errs |= KV_ERR_ITEM_RANGE;
+  }
+  for (int w = tid; w < maxw; w += blockDim.x) pages[w] = gp[w];
+  for (int i = tid; i < words; i += blockDim.x) used[i] = 0u;
+  for (int i = tid; i < cnt; i += blockDim.x) item_w[i] = items[size_t(b) * stride + i];
   __syncthreads();
-  for (int w = threadIdx.x; w < maxw; w += blockDim.x) {
+  for (int w = tid; w < maxw; w += blockDim.x) {
     const uint32_t e = pages[w];
     if (promote) {
       if (pe_tier(e) == TIER_F && w < n) {
@@ -152,17 +170,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
   }
   __syncthreads();
   WorkItem* work = reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + size_t(b) * maxw;
-  if (threadIdx.x == 0) {
-    int cnt = counts[b];
-    int errs = 0;
-    const int cap = stride < maxw ? stride : maxw;
-    if (cnt < 0) cnt = 0;
-    if (cnt > cap) {
-      cnt = cap;
-      errs |= KV_ERR_ITEM_RANGE;
-    }
+  if (tid == 0) {
+    int cursor = 0;
     for (int i = 0; i < cnt; ++i) {
-      const int w = items[size_t(b) * stride + i];
+      const int w = item_w[i];
       WorkItem it{w, -1, -1, 0};
       if (w < 0 || w >= n) {
         errs |= KV_ERR_ITEM_RANGE;
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
             pages[w] = pe_make(TIER_Q, true, 0, pe_lslot(e));
             it.flag = 2;
           } else {
-            const int j = find_free(used, nslots);
+            const int j = take_free(used, nslots, &cursor);
             if (j < 0) {
               errs |= KV_ERR_NO_LEDGER_SLOT;
             } else {
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
           if (pe_tier(e) != TIER_Q || !pe_has_ledger(e)) {
             errs |= KV_ERR_PROMOTE_STATE;
           } else {
-            const int j = find_free(used, nslots);
+            const int j = take_free(used, nslots, &cursor);
             if (j < 0) {
               errs |= KV_ERR_NO_BF16_SLOT;
             } else {
@@ -203,108 +214,117 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
     if (errs) set_err(pv.err, errs);
   }
   __syncthreads();
-  for (int w = threadIdx.x; w < maxw; w += blockDim.x) gp[w] = pages[w];
+  for (int w = tid; w < maxw; w += blockDim.x) gp[w] = pages[w];
 }
 
-// Demote data kernel: for each planned (item, kv head), quantise every 32-token
-// tile of the bf16 window into its ledger entry.  A tile's K groups are its
-// channels (32 tokens each), its V groups each token's 32-channel blocks.
-__global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer, int cap) {
+// The data kernels walk units (item, kv head, 32-token tile) of sequence
+// blockIdx.y; a workgroup takes units blockIdx.x, blockIdx.x + gridDim.x, ...
+// up to the planned item count, so a launch sized for the largest possible
+// list costs little when the list is short.
+
+// Demote data kernel: quantise one tile of a bf16 window into its ledger
+// entry.  K groups are the tile's channels (32 tokens each), V groups each
+// token's 32-channel blocks.
+__global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
   __shared__ float xs[2][32][129];          // K, V of one tile, canonical [token][dim]
   __shared__ uint8_t cs[2][32][128];        // their codes
-  const int kvh = blockIdx.y, W = pv.W, D = pv.D;
+  const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, D = pv.D, TPW = W / 32;
+  const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D);
-  const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items);
-  for (int k = blockIdx.x; k < pv.B * cap; k += gridDim.x) {
-    const int b = k / cap, i = k % cap;
-    if (i >= pv.work[pv.work_counts + b]) continue;
-    const WorkItem it = work[size_t(b) * pv.maxw + i];
+  const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
+  const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int i = u / (pv.Hkv * TPW), r = u % (pv.Hkv * TPW), kvh = r / TPW, tile = r % TPW;
+    const WorkItem it = work[i];
     if (it.flag != 1) continue;
-    const int seg = layer * pv.B + b;
-    const uint16_t* blk = pv.block(seg, it.src, kvh);
-    uint8_t* E = pv.entry(seg, it.dst, kvh);
-    for (int tile = 0; tile < W / 32; ++tile) {
-      const uint16_t* tb = blk + size_t(tile) * 64 * D;
-      uint8_t* et = E + size_t(tile) * LT.bytes;
-      for (int x = threadIdx.x; x < 32 * D; x += blockDim.x) {
-        const int t = x / D, d = x % D;
-        xs[0][t][d] = bf16_to_f32(tb[layout::bf16_k_offset(t, d, D)]);
-        xs[1][t][d] = bf16_to_f32(tb[layout::bf16_v_offset(t, d, D)]);
+    const uint16_t* tb = pv.block(seg, it.src, kvh) + size_t(tile) * 64 * D;
+    uint8_t* et = pv.entry(seg, it.dst, kvh) + size_t(tile) * LT.bytes;
+    // the tile's 16-byte chunks, read in order, into the canonical layout
+    for (int c = tid; c < 8 * D; c += blockDim.x) {
+      const int part = c / (4 * D), cc = c % (4 * D), cmb = cc >> 6, lane = cc & 63;
+      const uint4 q = reinterpret_cast<const uint4*>(tb + part * 32 * D)[cc];
+      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int t, d;
+        if (part) layout::v_chunk_elem(cmb, lane, e, &t, &d);
+        else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
+        xs[part][t][d] = __uint_as_float((e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16));
       }
-      __syncthreads();
-      uint16_t* ks = reinterpret_cast<uint16_t*>(et + LT.ks);
-      uint16_t* km = reinterpret_cast<uint16_t*>(et + LT.km);
-      uint16_t* vs = reinterpret_cast<uint16_t*>(et + LT.vs);
-      uint16_t* vm = reinterpret_cast<uint16_t*>(et + LT.vm);
-      for (int g = threadIdx.x; g < D + D; g += blockDim.x) {
-        float x[32];
-        uint8_t c[32];
-        if (g < D) {                       // K group: channel g over the tile's 32 tokens
-#pragma unroll
-          for (int t = 0; t < 32; ++t) x[t] = xs[0][t][g];
-          quant_group(x, c, ks + g, km + g);
-#pragma unroll
-          for (int t = 0; t < 32; ++t) cs[0][t][g] = c[t];
-        } else {                           // V group: token t, channels 32j..32j+31
-          const int t = (g - D) / (D / 32), j = (g - D) % (D / 32);
-#pragma unroll
-          for (int e = 0; e < 32; ++e) x[e] = xs[1][t][32 * j + e];
-          quant_group(x, c, vs + j * 32 + t, vm + j * 32 + t);
-#pragma unroll
-          for (int e = 0; e < 32; ++e) cs[1][t][32 * j + e] = c[e];
-        }
-      }
-      __syncthreads();
-      // pack: one 32-bit code word per thread step (64 lanes x D/32 words per part)
-      const int words = 64 * (D / 32);
-      for (int x = threadIdx.x; x < 2 * words; x += blockDim.x) {
-        const bool is_v = x >= words;
-        const int q = is_v ? x - words : x;
-        const int lane = q / (D / 32), w = q % (D / 32);
-        uint32_t word = 0;
-#pragma unroll
-        for (int f = 0; f < 16; ++f) {
-          int cmb, e, t, d;
-          layout::field_elem(w, f, &cmb, &e);
-          if (is_v) layout::v_chunk_elem(cmb, lane, e, &t, &d);
-          else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
-          word |= uint32_t(cs[is_v][t][d]) << (2 * f);
-        }
-        reinterpret_cast<uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + w] = word;
-      }
-      __syncthreads();
     }
+    __syncthreads();
+    uint16_t* ks = reinterpret_cast<uint16_t*>(et + LT.ks);
+    uint16_t* km = reinterpret_cast<uint16_t*>(et + LT.km);
+    uint16_t* vs = reinterpret_cast<uint16_t*>(et + LT.vs);
+    uint16_t* vm = reinterpret_cast<uint16_t*>(et + LT.vm);
+    for (int g = tid; g < D + D; g += blockDim.x) {
+      float x[32];
+      uint8_t c[32];
+      if (g < D) {                       // K group: channel g over the tile's 32 tokens
+#pragma unroll
+        for (int t = 0; t < 32; ++t) x[t] = xs[0][t][g];
+        quant_group(x, c, ks + g, km + g);
+#pragma unroll
+        for (int t = 0; t < 32; ++t) cs[0][t][g] = c[t];
+      } else {                           // V group: token t, channels 32j..32j+31
+        const int t = (g - D) / (D / 32), j = (g - D) % (D / 32);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[e] = xs[1][t][32 * j + e];
+        quant_group(x, c, vs + j * 32 + t, vm + j * 32 + t);
+#pragma unroll
+        for (int e = 0; e < 32; ++e) cs[1][t][32 * j + e] = c[e];
+      }
+    }
+    __syncthreads();
+    // pack: one 32-bit code word per thread step (64 lanes x D/32 words per part)
+    const int words = 64 * (D / 32);
+    for (int x = tid; x < 2 * words; x += blockDim.x) {
+      const bool is_v = x >= words;
+      const int q = is_v ? x - words : x;
+      const int lane = q / (D / 32), w = q % (D / 32);
+      uint32_t word = 0;
+#pragma unroll
+      for (int f = 0; f < 16; ++f) {
+        int cmb, e, t, d;
+        layout::field_elem(w, f, &cmb, &e);
+        if (is_v) layout::v_chunk_elem(cmb, lane, e, &t, &d);
+        else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
+        word |= uint32_t(cs[is_v][t][d]) << (2 * f);
+      }
+      reinterpret_cast<uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + w] = word;
+    }
+    __syncthreads();
   }
 }
 
-// Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of the window.
+// Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of one tile.
 // A ledger chunk (lane, cmb) and the bf16 chunk (cmb, lane) hold the same 8
-// values, so each thread step turns one code half-word into one 16-byte chunk.
-__global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, int cap) {
-  const int kvh = blockIdx.y, W = pv.W, D = pv.D;
+// values, so each thread step turns one code half-word into one 16-byte chunk;
+// the tile's scale block is staged in LDS first.
+__global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
+  __shared__ uint4 s_sc[64];   // Ks | Km | Vs | Vm of one tile (8 D bytes, D <= 128)
+  const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, D = pv.D, TPW = W / 32;
+  const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D);
-  const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items);
-  for (int k = blockIdx.x; k < pv.B * cap; k += gridDim.x) {
-    const int b = k / cap, i = k % cap;
-    if (i >= pv.work[pv.work_counts + b]) continue;
-    const WorkItem it = work[size_t(b) * pv.maxw + i];
+  const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
+  const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
+  const _Float16* ks = reinterpret_cast<const _Float16*>(s_sc);
+  const _Float16* km = ks + D;
+  const _Float16* vs = ks + 2 * D;
+  const _Float16* vm = ks + 3 * D;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int i = u / (pv.Hkv * TPW), r = u % (pv.Hkv * TPW), kvh = r / TPW, tile = r % TPW;
+    const WorkItem it = work[i];
     if (it.flag != 1) continue;
-    const int seg = layer * pv.B + b;
-    const uint8_t* E = pv.entry(seg, it.src, kvh);
-    uint16_t* blk = pv.block(seg, it.dst, kvh);
-    const int per_tile = 4 * D;    // chunks per part per tile
-    for (int idx = threadIdx.x; idx < (W / 32) * 2 * per_tile; idx += blockDim.x) {
-      const int tile = idx / (2 * per_tile), rem = idx % (2 * per_tile);
-      const bool is_v = rem >= per_tile;
-      const int c = is_v ? rem - per_tile : rem;
-      const int cmb = c >> 6, lane = c & 63;
-      const uint8_t* et = E + size_t(tile) * LT.bytes;
+    const uint8_t* et = pv.entry(seg, it.src, kvh) + size_t(tile) * LT.bytes;
+    uint16_t* tb = pv.block(seg, it.dst, kvh) + size_t(tile) * 64 * D;
+    if (tid < D / 2) s_sc[tid] = reinterpret_cast<const uint4*>(et + LT.ks)[tid];
+    __syncthreads();
+    for (int c = tid; c < 8 * D; c += blockDim.x) {
+      const bool is_v = c >= 4 * D;
+      const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
       const uint32_t word =
           reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + (cmb >> 1)];
-      const uint16_t* ks = reinterpret_cast<const uint16_t*>(et + LT.ks);
-      const uint16_t* km = reinterpret_cast<const uint16_t*>(et + LT.km);
-      const uint16_t* vs = reinterpret_cast<const uint16_t*>(et + LT.vs);
-      const uint16_t* vm = reinterpret_cast<const uint16_t*>(et + LT.vm);
       uint32_t out[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -315,42 +335,45 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, in
           const int f = e2 + 4 * (cmb & 1) + 8 * h;
           const float code = float((word >> (2 * f)) & 3u);
           int t, d;
-          float s, m;
+          float sc, mn;
           if (is_v) {
             layout::v_chunk_elem(cmb, lane, e, &t, &d);
-            s = float(__builtin_bit_cast(_Float16, vs[(d >> 5) * 32 + t]));
-            m = float(__builtin_bit_cast(_Float16, vm[(d >> 5) * 32 + t]));
+            sc = float(vs[(d >> 5) * 32 + t]);
+            mn = float(vm[(d >> 5) * 32 + t]);
           } else {
             layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
-            s = float(__builtin_bit_cast(_Float16, ks[d]));
-            m = float(__builtin_bit_cast(_Float16, km[d]));
+            sc = float(ks[d]);
+            mn = float(km[d]);
           }
-          pair |= uint32_t(f32_to_bf16_rne(__builtin_fmaf(code, s, m))) << (16 * h);
+          pair |= uint32_t(f32_to_bf16_rne(__builtin_fmaf(code, sc, mn))) << (16 * h);
         }
         out[e2] = pair;
       }
-      *reinterpret_cast<uint4*>(blk + size_t(tile) * 64 * D + (is_v ? 32 * D : 0) + size_t(c) * 8) =
-          make_uint4(out[0], out[1], out[2], out[3]);
+      reinterpret_cast<uint4*>(tb + (is_v ? 32 * D : 0))[cc] = make_uint4(out[0], out[1], out[2], out[3]);
     }
+    __syncthreads();
   }
 }
 
 static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t* items, int stride,
                                     const int32_t* counts, bool promote, hipStream_t s) {
   const int nslots = promote ? pv.nb : pv.nl;
-  const size_t shm = size_t(pv.maxw) * 4 + size_t((nslots + 31) / 32) * 4;
+  const int cap = stride < pv.maxw ? stride : pv.maxw;
+  const size_t shm = (size_t(pv.maxw) + size_t((nslots + 31) / 32) + size_t(cap > 0 ? cap : 0)) * 4;
   hipLaunchKernelGGL(plan_kernel, dim3(pv.B), dim3(256), shm, s, pv, layer, items, stride, counts,
                      int(promote));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int cap = stride < pv.maxw ? stride : pv.maxw;
   if (cap <= 0) return hipSuccess;
-  int grid = pv.B * cap;
-  if (grid > 1024) grid = 1024;
+  // about 1024 workgroups in all, never more than the largest unit count
+  const long max_units = long(cap) * pv.Hkv * (pv.W / 32);
+  long gx = (1024 + pv.B - 1) / pv.B;
+  if (gx > max_units) gx = max_units;
+  if (gx < 1) gx = 1;
   if (promote)
-    hipLaunchKernelGGL(dequant_kernel, dim3(grid, pv.Hkv), dim3(256), 0, s, pv, layer, cap);
+    hipLaunchKernelGGL(dequant_kernel, dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer);
   else
-    hipLaunchKernelGGL(quantize_kernel, dim3(grid, pv.Hkv), dim3(256), 0, s, pv, layer, cap);
+    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer);
   return hipGetLastError();
 }
 
