@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=24)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run 8 plain device copies of this many MiB (a known-size kernel that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the tiered decode path here is single-GPU "
@@ -125,6 +128,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_mb > 0:
+        n = args.copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 8}), flush=True)
+        return
     from tiered_int2_fp16_amd import binding as B
 
     c = CONFIGS["llama8b_32k"]
