@@ -20,7 +20,9 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from tests.gpu_harness import Pair, dev, log  # noqa: E402
+from oracle.router import F, Q  # noqa: E402
+from tests.gpu_harness import CachedSegment, Pair, dev, log  # noqa: E402
+from workload import score_prior  # noqa: E402
 
 
 def test_tiny_route_state_and_attention():
@@ -157,3 +159,73 @@ def test_decode_step_fuses_the_score_update_bit_exactly():
         assert torch.equal(oa, ob) and torch.equal(ma, mb)
         assert torch.equal(a.pool.scores(0), b.pool.scores(0))
     assert a.pool.check() == 0 and b.pool.check() == 0
+
+
+@pytest.mark.gpu
+def test_mistral_full_step_sampled():
+    """The Mistral-7B full step at full size: 32 layers x 32 sequences, 16K
+    context.  Per (layer, sequence): route to the pre-state (12 bf16 / 21 INT2 /
+    95 evicted windows), demote the 8 non-recent bf16 windows (first
+    quantisation into the ledger), promote the 4 highest-score INT2 windows,
+    then one attention step.  The contexts are drawn on the device (they are
+    34 G values); the oracle checks sampled (layer, sequence) pairs on copies
+    of their inputs: routing bit-exact, ledger bytes, promoted bf16, output and
+    window mass."""
+    from workload import kv_history_device
+    c = CONFIGS["mistral7b_step"]
+    checked = {0: [0, 31], 13: [7], 31: [0, 20]}
+    n, R = c.n_windows, c.n_recent
+    p = Pair(c, seqs=[], bf16_slots=n, ledger_slots=40)
+    rng = np.random.default_rng(4)
+    for layer in range(c.layers):
+        p.seqs = checked.get(layer, [])
+        K = torch.empty((c.batch, c.kv_heads, c.context, c.head_dim), dtype=torch.int16, device="cuda")
+        V = torch.empty_like(K)
+        for b in range(c.batch):
+            K[b], V[b] = kv_history_device(c, layer, b, "cuda")
+        prior = np.stack([score_prior(c, layer, b) for b in range(c.batch)])
+        p.pool.prefill(layer, K, V, c.context, dev(prior))
+        for b in p.seqs:
+            seg = CachedSegment(c.kv_heads, c.window, c.head_dim, c.n_recent)
+            seg.prefill(K[b].cpu().numpy().view(np.uint16), V[b].cpu().numpy().view(np.uint16),
+                        prior=prior[b].astype(np.float64))
+            p.oracle[(layer, b)] = seg
+        del K, V
+        # the pre-state: 12 bf16 (4 recent + 8), 21 INT2, 95 evicted
+        _, cnt = p.route(layer, c.pre_budget_frac, c.pre_hi_frac)
+        pages = p.pool.pages(layer).cpu().numpy().view(np.uint32)[:, :n] & 3
+        assert (pages == F).sum(axis=1).tolist() == [12] * c.batch
+        assert (pages == Q).sum(axis=1).tolist() == [21] * c.batch
+        # the move set: demote the 8 non-recent bf16 windows, then promote the
+        # 4 highest-score INT2 windows (score descending, lower index first)
+        S = p.pool.scores(layer).cpu().numpy()[:, :n]
+        dem = np.zeros((c.batch, n), np.int32)
+        pro = np.zeros((c.batch, n), np.int32)
+        for b in range(c.batch):
+            d = [w for w in range(n - R) if pages[b][w] == F]
+            assert len(d) == c.demote_per_seg
+            dem[b, : len(d)] = d
+            q_after = [w for w in range(n) if pages[b][w] == Q or w in d]
+            top = sorted(q_after, key=lambda w: (-float(S[b][w]), w))[: c.promote_per_seg]
+            pro[b, : len(top)] = sorted(top)
+        cnt_d = np.full(c.batch, c.demote_per_seg, np.int32)
+        cnt_p = np.full(c.batch, c.promote_per_seg, np.int32)
+        p.pool.demote(layer, dev(dem), dev(cnt_d))
+        p.pool.promote(layer, dev(pro), dev(cnt_p))
+        for b in p.seqs:
+            seg = p.oracle[(layer, b)]
+            for w in dem[b][: c.demote_per_seg]:
+                seg.demote(int(w))
+            for w in pro[b][: c.promote_per_seg]:
+                seg.promote(int(w))
+        pages = p.pool.pages(layer).cpu().numpy().view(np.uint32)[:, :n] & 3
+        assert (pages == F).sum(axis=1).tolist() == [8] * c.batch
+        assert (pages == Q).sum(axis=1).tolist() == [25] * c.batch
+        if p.seqs:
+            p.check_state(layer, ledger_sample=12, window_sample=8, rng=rng)
+        _, _, _, errs = p.step(layer, 0, check=bool(p.seqs))
+        if p.seqs:
+            log("mistral layer %d: out err %.2e mass err %.2e" % (layer, *errs))
+        if layer % 8 == 7:
+            log(f"mistral: {layer + 1} layers done")
+    assert p.pool.check() == 0

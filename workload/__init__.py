@@ -9,6 +9,7 @@ from .synth import (  # noqa: F401
     CONFIGS,
     Config,
     kv_history,
+    kv_history_device,
     new_kv,
     query,
     score_prior,

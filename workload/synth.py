@@ -19,7 +19,7 @@ from typing import Dict, Tuple
 import numpy as np
 
 # stream ids inside one config seed
-_T_SCORES, _T_Q, _T_K, _T_V, _T_OUTLIER, _T_STEP_Q, _T_STEP_K, _T_STEP_V = range(8)
+_T_SCORES, _T_Q, _T_K, _T_V, _T_OUTLIER, _T_STEP_Q, _T_STEP_K, _T_STEP_V, _T_DEVICE_KV = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -126,6 +126,29 @@ def kv_history(cfg: Config, layer: int, b: int,
             k[h][:, ch] *= np.float32(cfg.k_outlier_scale)
     v = _rng(cfg, _T_V, layer, b).standard_normal(shape, dtype=np.float32)
     return _to_bf16_bits(k), _to_bf16_bits(v)
+
+
+def kv_history_device(cfg: Config, layer: int, b: int, device):
+    """K and V of the cached context of sequence ``b`` in ``layer``, drawn on
+    ``device`` by torch's counter-based Philox generator (seeded from the
+    config seed, layer and sequence): for full-size workloads whose contexts
+    are too large to draw on the host.  Same distributions as
+    :func:`kv_history` (normal, K outlier channels scaled, bf16 by dropping the
+    low 16 bits), different streams.  Returns two int16 tensors holding bf16
+    bits, [kv_heads][context][head_dim].
+    """
+    import torch
+    seed = int(np.random.SeedSequence([cfg.seed, _T_DEVICE_KV, layer, b]).generate_state(1, np.uint64)[0] >> 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (cfg.kv_heads, cfg.context, cfg.head_dim)
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    for h in range(cfg.kv_heads):
+        ch = outlier_channels(cfg, layer, h)
+        if ch.size:
+            k[h][:, torch.from_numpy(ch).to(device)] *= cfg.k_outlier_scale
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return ((k.view(torch.int32) >> 16).to(torch.int16), (v.view(torch.int32) >> 16).to(torch.int16))
 
 
 def score_prior(cfg: Config, layer: int, b: int) -> np.ndarray:
