@@ -66,7 +66,7 @@ def kernel_source_hash():
 def measured_traffic(kernel_hash):
     """HBM bytes per attention launch from the committed counter summary, if it
     was taken on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", "attn_llama8b_32k_traffic.json")
+    p = os.path.join(ROOT, "profiles", "attn_kernel_llama8b_32k_traffic.json")
     try:
         d = json.load(open(p))
     except (OSError, ValueError):

@@ -61,7 +61,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGMax = 8;     // query heads per kv head supported
 constexpr int kWq = 9;       // weight of an INT2 tile (a bf16 tile weighs 16; set by measurement)
 constexpr int kMaxSplits = 64;
-constexpr int kMassWindows = 32;   // windows per mass block of the combine kernel
+constexpr int kMassWindows = 16;   // windows per mass block of the combine kernel
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -374,7 +374,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   for (int nb = 0; nb < NB; ++nb) st.o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.ob = f32x4{0.f, 0.f, 0.f, 0.f};
   // raw tile masses of this kv head's query heads: row h holds tile w*TPW + k
-  float2* tmass = a.tile_mass + (size_t(b) * pv.Hq + size_t(kvh) * G) * maxw * TPW;
+  // raw tile masses: row (tile w*TPW + k), column query head
+  float2* tmass = a.tile_mass + size_t(b) * maxw * TPW * pv.Hq + size_t(kvh) * G;
   // tile masses feed the window masses and the fused score update
   const bool want_mass = a.mass != nullptr || a.acc_scores != 0;
   const bool rec_mass = want_mass && g == 0 && hn < G;
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     for (int idx = lane; idx < nt * G; idx += 64) {
       const int h = idx / nt, t = idx - h * nt;
       const uint32_t e = list[t];
-      tmass[size_t(h) * maxw * TPW + te_win(e) * TPW + te_tile(e)] = rec[t][h];
+      tmass[(size_t(te_win(e)) * TPW + te_tile(e)) * pv.Hq + h] = rec[t][h];
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -740,6 +741,7 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   __shared__ float s_m[kMaxSplits * kGMax];
   __shared__ float s_hm[kGMax], s_hz[kGMax];
   __shared__ float4 s_acc[256];
+  __shared__ int s_win[kMassWindows];
   extern __shared__ float s_dynf[];   // mass blocks: M, 1/Z [Hq], masses [kMassWindows][Hq], appended [Hq]
   const int b = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
   const int G = pv.G, Hkv = pv.Hkv, Hq = pv.Hq, S = a.splits, W = pv.W, maxw = pv.maxw;
@@ -831,31 +833,33 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   float* s_Zh = s_dynf + Hq;       // [Hq] 1 / normaliser
   float* s_mv = s_dynf + 2 * Hq;   // [kMassWindows][Hq]
   float2* s_app = reinterpret_cast<float2*>(s_dynf + (2 + kMassWindows) * Hq);   // [Hq]
-  // thread (window wl = tid % 32, head row) takes the (head, window) pairs
-  // h = tid / 32 + 8 i: the TPW tile records of a pair are contiguous
-  const int wl = c32, w = w0 + wl;
-  const bool in = w < n_win;
+  // thread pairs (head h, window wl), heads fastest: pair p = tid + 256 i has
+  // h = p % Hq, wl = p / Hq, and the records of one tile of all heads are
+  // contiguous
   constexpr int kPairs = 4, kTiles = 8;   // pairs per batch; tiles per window at most
-  const auto rtm = tile_rsrc(a.tile_mass + size_t(b) * Hq * maxw * TPW, Hq * maxw * TPW * 8);
+  const int npairs = Hq * kMassWindows;
+  const auto rtm = tile_rsrc(a.tile_mass + size_t(b) * maxw * TPW * Hq, maxw * TPW * Hq * 8);
   const auto rml = tile_rsrc(a.ml + size_t(b) * Hq * S, Hq * S * 8);
   const auto rpg = tile_rsrc(pv.pages + size_t(seg) * maxw, maxw * 4);
   const auto rsc = tile_rsrc(pv.scores + size_t(seg) * maxw, maxw * 4);
-  auto tile_masses = [&](int h0, float2 (&t)[kPairs][kTiles]) {
+  auto tile_masses = [&](int p0, float2 (&t)[kPairs][kTiles]) {
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
-      const int h = h0 + 8 * i + r8;
+      const int pi = p0 + tid + 256 * i, h = pi % Hq, w = w0 + pi / Hq;
 #pragma unroll
       for (int k = 0; k < kTiles; ++k)
-        t[i][k] = as_f2(load8(rtm, boff(h < Hq && w < maxw && k < TPW, ((h * maxw + w) * TPW + k) * 8)));
+        t[i][k] = as_f2(load8(rtm, boff(pi < npairs && w < maxw && k < TPW, ((w * TPW + k) * Hq + h) * 8)));
     }
   };
-  // loads of the first batch in flight together: tile masses, the page entry,
-  // the score, the appended token's records and the (m, l) pairs of the
-  // per-head reductions
+  // loads of the first batch in flight together: tile masses, the page entries
+  // and scores of the block's windows, the appended token's records and the
+  // (m, l) pairs of the per-head reductions
   float2 t1[kPairs][kTiles];
   tile_masses(0, t1);
-  const uint32_t pe = load4(rpg, boff(in && w < n_old, w * 4));
-  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tid < kMassWindows && w < maxw, w * 4)));
+  const int wt = w0 + tid;   // thread tid < kMassWindows: its window's page entry and score
+  const bool tin = tid < kMassWindows && wt < n_win;
+  const uint32_t pe = load4(rpg, boff(tin && wt < n_old, wt * 4));
+  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tin, wt * 4)));
   if (app) {
     const auto rap = tile_rsrc(a.app_mass + size_t(b) * Hq, Hq * 8);
     for (int h = tid; h < Hq; h += 256) s_app[h] = as_f2(load8(rap, h * 8));
@@ -881,45 +885,56 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       }
     }
   }
-  __syncthreads();
-  bool live = false;
-  int vt = 0;
-  if (in) {
-    if (w < n_old) {
-      live = pe_tier(pe) != TIER_E;
-      vt = (min(W, len_old - w * W) + 31) / 32;
-    } else {
-      live = true;   // the window the appended token opened
+  // liveness and valid tiles of the block's windows
+  if (tid < kMassWindows) {
+    bool live = false;
+    int vt = 0;
+    if (tin) {
+      if (wt < n_old) {
+        live = pe_tier(pe) != TIER_E;
+        vt = (min(W, len_old - wt * W) + 31) / 32;
+      } else {
+        live = true;   // the window the appended token opened
+      }
     }
+    s_win[tid] = live ? vt + 1 : 0;   // 0: not live; else 1 + valid tiles
   }
-  const bool vwin = app && w == len_old / W;
-  auto masses = [&](int h0, const float2 (&t)[kPairs][kTiles]) {
+  __syncthreads();
+  const int vwin = app ? len_old / W : -1;
+  auto masses = [&](int p0, const float2 (&t)[kPairs][kTiles]) {
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
-      const int h = h0 + 8 * i + r8;
-      if (h >= Hq) break;
+      const int pi = p0 + tid + 256 * i, h = pi % Hq, wl = pi / Hq;
+      if (pi >= npairs) break;
+      const int lw = s_win[wl];
+      const int vt = lw - 1;
       const float M = s_M[h];
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < kTiles; ++k)
         if (k < vt) acc += t[i][k].x * fast_exp2(t[i][k].y - M);
-      if (vwin) acc += s_app[h].x * fast_exp2(s_app[h].y - M);
-      const float mv = (in && live) ? acc * s_Zh[h] : 0.f;
-      if (in && a.mass) a.mass[(size_t(b) * Hq + h) * maxw + w] = mv;
-      s_mv[wl * Hq + h] = mv;
+      if (w0 + wl == vwin) acc += s_app[h].x * fast_exp2(s_app[h].y - M);
+      s_mv[wl * Hq + h] = lw ? acc * s_Zh[h] : 0.f;
     }
   };
   masses(0, t1);
-  for (int h0 = 8 * kPairs; h0 < Hq; h0 += 8 * kPairs) {
+  for (int p0 = 256 * kPairs; p0 < npairs; p0 += 256 * kPairs) {
     float2 t2[kPairs][kTiles];
-    tile_masses(h0, t2);
-    masses(h0, t2);
+    tile_masses(p0, t2);
+    masses(p0, t2);
   }
   __syncthreads();
-  if (acc_scores && tid < kMassWindows && in && live) {
+  // masses out in window order (16 consecutive windows per head)
+  if (a.mass) {
+    for (int idx = tid; idx < npairs; idx += 256) {
+      const int h = idx / kMassWindows, ww = idx % kMassWindows;
+      if (w0 + ww < n_win) a.mass[(size_t(b) * Hq + h) * maxw + w0 + ww] = s_mv[ww * Hq + h];
+    }
+  }
+  if (acc_scores && tin && s_win[tid]) {
     float ssum = 0.f;
     for (int h = 0; h < Hq; ++h) ssum += s_mv[tid * Hq + h];   // heads in order
-    pv.scores[size_t(seg) * maxw + w] = s_old + ssum;
+    pv.scores[size_t(seg) * maxw + wt] = s_old + ssum;
   }
 }
 

@@ -44,7 +44,7 @@ int attn_splits(const Geometry& g, int compute_units);
 struct AttnWorkspace {
   size_t partials = 0;   // float [batch][kv_heads][splits][group][D]: unnormalised outputs
   size_t ml = 0;         // float2 [batch][q_heads][splits]: running max, sum of each workgroup
-  size_t tile_mass = 0;  // float2 [batch][q_heads][max_windows*W/32]: raw tile mass, its max
+  size_t tile_mass = 0;  // float2 [batch][max_windows*W/32][q_heads]: raw tile mass, its max
   size_t app_mass = 0;   // float2 [batch][q_heads]: the same for an appended token
   size_t app_info = 0;   // int [batch][8]: append decision of the step
   size_t total = 0;

@@ -26,7 +26,7 @@ struct AttnArgs {
   float* mass;
   float* partials;      // [batch][kv_heads][splits][group][D]
   float2* ml;           // [batch][q_heads][splits]: (max, sum)
-  float2* tile_mass;    // [batch][q_heads][max_windows*W/32]: (raw mass, max)
+  float2* tile_mass;    // [batch][max_windows*W/32][q_heads]: (raw mass, max)
   float2* app_mass;     // [batch][q_heads]
   int32_t* app_info;    // [batch][8] append decision of this step (workspace)
   int splits;
