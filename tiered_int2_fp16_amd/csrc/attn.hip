@@ -9,15 +9,18 @@
 // kernel: HBM carries 3 bits per INT2 value, never a rebuilt bf16 copy.
 //
 // Work split: grid (splits, kv heads, sequences), 4 wave64 per workgroup.  The
-// live 32-token tiles of a (sequence, kv head) are listed bf16 first, then
-// INT2, weighted 16 (bf16, 16 KB) and kWq (INT2, 3 KB) and the weight range is
-// cut evenly over all waves of all splits.  A wave streams its bf16 tiles and
-// then its INT2 tiles, each loop double-buffered in registers, and keeps an
-// online softmax (running max, sum, output) for the G query heads of its kv
-// head; every tile's raw mass is recorded with the running max it was taken
-// at.  A second kernel combines the partials of each (sequence, kv head) into
-// the output and normalises the window masses (the order of tokens does not
-// matter: A.V = A_P.V_P, LogQuant summary, "Positie-agnostische optimalisatie").
+// live 32-token tiles of a (sequence, kv head) are listed per tier (bf16,
+// INT2) and each tier's list is cut evenly over all waves of all splits, so
+// every wave - and so every SIMD and CU - gets its share of the bytes (mostly
+// bf16) and of the decode work (mostly INT2).  A wave requests its first INT2
+// tiles, requests its first bf16 tile once the first INT2 tile is in, decodes
+// its INT2 tiles while the bf16 data arrives, then streams its bf16 tiles;
+// both loops are double-buffered in registers.  It keeps an online softmax
+// (running max, sum, output) for the G query heads of its kv head; every
+// tile's raw mass is recorded with the running max it was taken at.  A second
+// kernel combines the partials of each (sequence, kv head) into the output and
+// normalises the window masses (the order of tokens does not matter:
+// A.V = A_P.V_P, LogQuant summary, "Positie-agnostische optimalisatie").
 // Splitting the combine off keeps every workgroup of the first kernel free of
 // device-wide fences and atomics; the kernel boundary orders the two.
 //
@@ -30,13 +33,11 @@
 //        4 s q is exact in fp32 and goes to the MFMA as fp16 high + low parts,
 //        the second sum (constant over the tile's tokens) is taken in fp32 -
 //        an fp16 rounding of either would shift a whole tile's logits at once.
-//        Both are computed once per (head, channel) in a compact lane layout
-//        and handed to the MFMA layout through the wave's LDS buffer.  With
-//        per-token V scale s' and min m',
+//        Each lane forms its own B operand from the tile's scales, which
+//        reach it through the wave's LDS buffer.  With per-token V scale s'
+//        and min m',
 //          sum_t p v = sum_t (1 + c/4)(4 p s') + sum_t (m'/4 - s')(4 p):
-//        one MFMA per 16 channels for the codes, one for the min term.  The
-//        tile's scales reach the lanes that need them through the same LDS
-//        buffer.
+//        one MFMA per 16 channels for the codes, one for the min term.
 //
 // A decode step may append a token: it is attended straight from k_new/v_new
 // and stored in the newest window by the combine kernel, which also rewrites
@@ -44,6 +45,8 @@
 // read them.
 #include <hip/hip_ext.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "host_core.h"
 #include "launch.h"
@@ -59,7 +62,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGMax = 8;     // query heads per kv head supported
-constexpr int kWq = 9;       // weight of an INT2 tile (a bf16 tile weighs 16; set by measurement)
 constexpr int kMaxSplits = 64;
 constexpr int kMassWindows = 16;   // windows per mass block of the combine kernel
 
@@ -201,13 +203,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   constexpr int NB = D / 16;   // 16-channel blocks of the PV product (= code chunks per part)
   constexpr int CW = D / 32;   // 32-bit code words per lane per part
   constexpr int kList = 64;    // tile entries a wave lists at a time
-  constexpr int kQGroup = 4;   // INT2 tiles loaded together
   extern __shared__ uint32_t s_dyn[];    // plan (page entries, tile prefixes), slot bitmap
   __shared__ float s_wm[kAttnWaves][kGMax], s_wl[kAttnWaves][kGMax];
   __shared__ float s_wo[kAttnWaves][kGMax][D];
   __shared__ float s_wb[kAttnWaves][kGMax][4];
   __shared__ __attribute__((aligned(16))) uint8_t s_scb[kAttnWaves][8 * D];  // INT2 tile scales
-  __shared__ uint32_t s_list[kAttnWaves][kList];                               // a wave's tiles
+  __shared__ uint32_t s_listf[kAttnWaves][kList];                              // a wave's bf16 tiles
+  __shared__ uint32_t s_listq[kAttnWaves][kList];                              // and INT2 tiles
   __shared__ float2 s_rec[kAttnWaves][kList][kGMax];                           // their raw masses
   __shared__ int s_gt[kMaxWindows / 64];                                       // tiles per 64 windows
 
@@ -283,18 +285,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     tot = __builtin_amdgcn_readlane(incl, 63);
   }
   const int NF = tot & 0xFFFF, NQ = tot >> 16;
-  const long U = 16L * NF + long(kWq) * NQ;
-  const long nwaves = long(S) * kAttnWaves;
-  const long widx = long(split) * kAttnWaves + wid;
-  const long u0 = widx * U / nwaves, u1 = (widx + 1) * U / nwaves;
-  auto cdiv = [](long x, long y) { return x <= 0 ? 0L : (x + y - 1) / y; };
-  const int f_beg = int(min(long(NF), cdiv(u0, 16))), f_end = int(min(long(NF), cdiv(u1, 16)));
-  const int q_beg = int(min(long(NQ), cdiv(u0 - 16L * NF, kWq)));
-  const int q_end = int(min(long(NQ), cdiv(u1 - 16L * NF, kWq)));
-  uint32_t* list = s_list[wid];
-  // the wave lists the tiles [lo, hi) of tier `tier`: lane l takes window
-  // 64r + l of each group r whose tiles of that tier meet the range
-  auto build_list = [&](int tier, int lo, int hi) {
+  // Every wave takes an even share of the bf16 tiles and, separately, of the
+  // INT2 tiles, so HBM bytes (mostly bf16) and decode work (mostly INT2) are
+  // spread alike over all waves - and so over all SIMDs and CUs.
+  const int nwaves = S * kAttnWaves, widx = split * kAttnWaves + wid;
+  const int f_beg = widx * NF / nwaves, f_end = (widx + 1) * NF / nwaves;
+  const int q_beg = widx * NQ / nwaves, q_end = (widx + 1) * NQ / nwaves;
+  uint32_t* listf = s_listf[wid];
+  uint32_t* listq = s_listq[wid];
+  // the wave lists the tiles [lo, hi) of tier `tier` into `list`: lane l takes
+  // window 64r + l of each group r whose tiles of that tier meet the range
+  auto build_list = [&](int tier, int lo, int hi, uint32_t* list) {
     const int sh = tier == TIER_F ? 0 : 16;
     for (int r = 0; r < NG; ++r) {
       const int b0 = (__builtin_amdgcn_readlane(gbase, r) >> sh) & 0xFFFF;
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   // the raw masses of a listed chunk of nt tiles go out after the chunk: no
   // global store inside the tile loops, where it would hold up the next
   // tile's loads
-  auto flush_masses = [&](int nt) {
+  auto flush_masses = [&](int nt, const uint32_t* list) {
     if (!want_mass) return;
     __builtin_amdgcn_wave_barrier();
     for (int idx = lane; idx < nt * G; idx += 64) {
@@ -425,243 +426,272 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     if (rec_mass) a.app_mass[size_t(b) * pv.Hq + size_t(kvh) * G + hn] = make_float2(rs, st.m_run);
   }
 
-  // ---------------------------------------------------------- bf16 tiles
-  // Loads go through a buffer resource spanning one tile; a prefetch past the
-  // last tile gets an empty resource and reads zeros without touching memory,
-  // so the loop has no branch around a load and every tile waits only for
-  // its own loads.
-  {
-    constexpr int kTileBytes = 64 * D * 2;
-    struct FB {
-      uint4 k[NB];
-      uint4 v[NB];
-    };
-    auto load_f = [&](FB& fb, int i, int nt) {
-      const uint32_t e = uniform(int(list[min(i, nt - 1)]));
-      const uint16_t* base = pv.block(seg, te_slot(e), kvh) + size_t(te_tile(e)) * 64 * D;
-      const auto rs = tile_rsrc(base, i < nt ? kTileBytes : 0);
+  // ------------------------------------------------------------ tile loops
+  // Issue order: the first two INT2 tiles, then the first bf16 tile, then the
+  // INT2 tiles are decoded while the (larger) bf16 data is still arriving;
+  // the bf16 tiles come last.  Loads go through a buffer resource spanning one
+  // tile; a prefetch past the last tile gets an empty resource and reads zeros
+  // without touching memory, so no load sits behind a branch and every tile
+  // waits only for its own loads.
+  constexpr int kTileBytes = 64 * D * 2;
+  struct FB {
+    uint4 k[NB];
+    uint4 v[NB];
+  };
+  auto load_f = [&](FB& fb, int i, int nt) {
+    const uint32_t e = uniform(int(listf[max(0, min(i, nt - 1))]));
+    const uint16_t* base = pv.block(seg, te_slot(e), kvh) + size_t(te_tile(e)) * 64 * D;
+    const auto rs = tile_rsrc(base, i < nt ? kTileBytes : 0);
 #pragma unroll
-      for (int c = 0; c < NB; ++c) fb.k[c] = load16(rs, (c * 64 + lane) * 16);
+    for (int c = 0; c < NB; ++c) fb.k[c] = load16(rs, (c * 64 + lane) * 16);
 #pragma unroll
-      for (int c = 0; c < NB; ++c) fb.v[c] = load16(rs, 32 * D * 2 + (c * 64 + lane) * 16);
-    };
-    auto compute_f = [&](FB& fb, int t) {
-      const uint32_t e = uniform(int(list[t]));
-      const int w = te_win(e), k = te_tile(e);
-      const int valid = min(32, len_old - w * W - 32 * k);
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NB; ++c) fb.v[c] = load16(rs, 32 * D * 2 + (c * 64 + lane) * 16);
+  };
+  auto compute_f = [&](FB& fb, int t) {
+    const uint32_t e = uniform(int(listf[t]));
+    const int w = te_win(e), k = te_tile(e);
+    const int valid = min(32, len_old - w * W - 32 * k);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s0 = mfma_bf16(as_bf16x8(fb.k[kk]), qb[kk], s0);
-        s1 = mfma_bf16(as_bf16x8(fb.k[KK + kk]), qb[kk], s1);
-      }
-      float z[8], p[8], rs;
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = mfma_bf16(as_bf16x8(fb.k[kk]), qb[kk], s0);
+      s1 = mfma_bf16(as_bf16x8(fb.k[KK + kk]), qb[kk], s1);
+    }
+    float z[8], p[8], rs;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        z[i4] = (8 * g + i4 < valid) ? s0[i4] * qscale : -INFINITY;
-        z[4 + i4] = (8 * g + 4 + i4 < valid) ? s1[i4] * qscale : -INFINITY;
-      }
-      softmax_tile<NB>(st, z, p, &rs);
-      if (valid < 32) {   // stale values past the last token: zero them (0 * NaN)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      z[i4] = (8 * g + i4 < valid) ? s0[i4] * qscale : -INFINITY;
+      z[4 + i4] = (8 * g + 4 + i4 < valid) ? s1[i4] * qscale : -INFINITY;
+    }
+    softmax_tile<NB>(st, z, p, &rs);
+    if (valid < 32) {   // stale values past the last token: zero them (0 * NaN)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          uint32_t w4[4] = {fb.v[c].x, fb.v[c].y, fb.v[c].z, fb.v[c].w};
+      for (int c = 0; c < NB; ++c) {
+        uint32_t w4[4] = {fb.v[c].x, fb.v[c].y, fb.v[c].z, fb.v[c].w};
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            if (8 * g + 2 * e2 >= valid) w4[e2] &= 0xFFFF0000u;
-            if (8 * g + 2 * e2 + 1 >= valid) w4[e2] &= 0x0000FFFFu;
-          }
-          fb.v[c] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          if (8 * g + 2 * e2 >= valid) w4[e2] &= 0xFFFF0000u;
+          if (8 * g + 2 * e2 + 1 >= valid) w4[e2] &= 0x0000FFFFu;
         }
+        fb.v[c] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
-      bf16x8 ph, pl;
+    }
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) {
+      ph[e2] = (__bf16)p[e2];
+      pl[e2] = (__bf16)(p[e2] - float(ph[e2]));
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      st.o[nb] = mfma_bf16(as_bf16x8(fb.v[nb]), ph, st.o[nb]);
+      st.o[nb] = mfma_bf16(as_bf16x8(fb.v[nb]), pl, st.o[nb]);
+    }
+    if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
+  };
+
+  const uint32_t kMaskR = 0x03000300u, kOneR = 0x3C003C00u;   // decode constants
+  f16x8 q4[KK];     // 4q in fp16, formed here so it never shares registers with the bf16 buffers
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(4.f * float(qb[kk][e]));
+  const layout::LedgerTile LT(D);
+  struct QB {
+    uint32_t kc[CW], vc[CW], sc[CW];
+  };
+  auto load_words = [&](__amdgpu_buffer_rsrc_t rs, int off, uint32_t (&w)[CW]) {
+    if constexpr (CW == 4) {
+      const uint4 u = load16(rs, off + lane * 16);
+      w[0] = u.x;
+      w[1] = u.y;
+      w[2] = u.z;
+      w[3] = u.w;
+    } else {
+      const uint2 u = load8(rs, off + lane * 8);
+      w[0] = u.x;
+      w[1] = u.y;
+    }
+  };
+  auto load_q = [&](QB& qq, int i, int nt) {
+    const uint32_t e = uniform(int(listq[max(0, min(i, nt - 1))]));
+    const uint8_t* t = pv.entry(seg, te_slot(e), kvh) + size_t(te_tile(e)) * LT.bytes;
+    const auto rs = tile_rsrc(t, i < nt ? LT.bytes : 0);
+    load_words(rs, LT.kc, qq.kc);
+    load_words(rs, LT.vc, qq.vc);
+    load_words(rs, LT.ks, qq.sc);
+  };
+  uint8_t* scb = s_scb[wid];
+  auto compute_q = [&](QB& qq, int t) {
+    // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer
+    if constexpr (CW == 4)
+      reinterpret_cast<uint4*>(scb)[lane] = make_uint4(qq.sc[0], qq.sc[1], qq.sc[2], qq.sc[3]);
+    else
+      reinterpret_cast<uint2*>(scb)[lane] = make_uint2(qq.sc[0], qq.sc[1]);
+    const f16x8* ks = reinterpret_cast<const f16x8*>(scb);              // [D]
+    const f16x8* km = reinterpret_cast<const f16x8*>(scb + 2 * D);      // [D]
+    const f16x8* vs = reinterpret_cast<const f16x8*>(scb + 4 * D);      // [D/32][32]
+    const f16x8* vm = reinterpret_cast<const f16x8*>(scb + 6 * D);
+    // Each lane forms its own B operand: 4 s q as an fp16 product plus its
+    // exact fp16 residual (fma TwoProduct), and its share of the tile
+    // constant sum_d q (m - 4 s) = sum 4q m / 4 - sum 4q s (fp16 pairs,
+    // fp32 sums), completed across the 4 lane groups.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    float cm = 0.f, cs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const f16x8 s8 = ks[4 * kk + g], m8 = km[4 * kk + g];
+      const f16x8 qh = q4[kk] * s8;
+      const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const f16x2 qq2 = {q4[kk][2 * e2], q4[kk][2 * e2 + 1]};
+        cm = __builtin_amdgcn_fdot2(qq2, f16x2{m8[2 * e2], m8[2 * e2 + 1]}, cm, false);
+        cs = __builtin_amdgcn_fdot2(qq2, f16x2{s8[2 * e2], s8[2 * e2 + 1]}, cs, false);
+      }
+      const int c0 = kk, c1 = KK + kk;                               // chunks of blk 0 / 1
+      const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1], kMaskR, kOneR)
+                                : decode_codes<0>(qq.kc[c0 >> 1], kMaskR, kOneR);
+      const f16x8 a1 = (c1 & 1) ? decode_codes<1>(qq.kc[c1 >> 1], kMaskR, kOneR)
+                                : decode_codes<0>(qq.kc[c1 >> 1], kMaskR, kOneR);
+      s0 = mfma_f16(a0, qh, s0);
+      s0 = mfma_f16(a0, ql, s0);
+      s1 = mfma_f16(a1, qh, s1);
+      s1 = mfma_f16(a1, ql, s1);
+    }
+    // the MFMA result lanes (g, hn) hold head hn, as the B operand lanes do
+    const float bias0 = sum_rows(fmaf(cm, 0.25f, -cs));
+    float z[8], p[8], rs;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      z[i4] = (s0[i4] + bias0) * qscale;
+      z[4 + i4] = (s1[i4] + bias0) * qscale;
+    }
+    softmax_tile<NB>(st, z, p, &rs);
+    // 4p as fp16 high + low parts, then 4 p s' = high*s' + (exact residual
+    // of that product + low*s'), all in packed fp16
+    f16x8 p4, p4l;
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) {
+      const float x = 4.f * p[e2];
+      p4[e2] = (_Float16)x;
+      p4l[e2] = (_Float16)(x - float(p4[e2]));
+    }
+    // v = (m' - 4 s') + (1 + c/4) 4 s': the min term sum_t 4p (m'/4 - s') on
+    // the MFMA with both factors as fp16 high + low parts (row = 32-channel
+    // group jr; rows >= D/32 repeat them and are not read)
+    {
+      const int jr = hn & (D / 32 - 1);
+      const f16x8 vm8 = vm[4 * jr + g], vs8 = vs[4 * jr + g];
+      f16x8 mvh, mvl;
 #pragma unroll
       for (int e2 = 0; e2 < 8; ++e2) {
-        ph[e2] = (__bf16)p[e2];
-        pl[e2] = (__bf16)(p[e2] - float(ph[e2]));
+        const float x = fmaf(float(vm8[e2]), 0.25f, -float(vs8[e2]));
+        mvh[e2] = (_Float16)x;
+        mvl[e2] = (_Float16)(x - float(mvh[e2]));
       }
+      st.ob = mfma_f16(mvh, p4, st.ob);
+      st.ob = mfma_f16(mvh, p4l, st.ob);
+      st.ob = mfma_f16(mvl, p4, st.ob);
+    }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        st.o[nb] = mfma_bf16(as_bf16x8(fb.v[nb]), ph, st.o[nb]);
-        st.o[nb] = mfma_bf16(as_bf16x8(fb.v[nb]), pl, st.o[nb]);
+    for (int jd = 0; jd < D / 32; ++jd) {
+      const f16x8 sv = vs[4 * jd + g];
+      const f16x8 ph = p4 * sv;
+      const f16x8 pl = __builtin_elementwise_fma(p4l, sv, __builtin_elementwise_fma(p4, sv, -ph));
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int nb = 2 * jd + h2;
+        const f16x8 av = (nb & 1) ? decode_codes<1>(qq.vc[nb >> 1], kMaskR, kOneR)
+                                  : decode_codes<0>(qq.vc[nb >> 1], kMaskR, kOneR);
+        st.o[nb] = mfma_f16(av, ph, st.o[nb]);
+        st.o[nb] = mfma_f16(av, pl, st.o[nb]);
       }
-      if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
-    };
-    for (int cb = f_beg; cb < f_end; cb += kList) {
-      const int ce = min(f_end, cb + kList), nt = ce - cb;
-      build_list(TIER_F, cb, ce);
-      // two tiles in flight; a buffer is refilled as soon as its tile is
-      // consumed (sched_barrier keeps the loads ahead of the next tile's math)
-      FB A, Bf;
-      load_f(A, 0, nt);
-      load_f(Bf, 1, nt);
+    }
+    if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
+  };
+
+  if (f_beg < f_end) build_list(TIER_F, f_beg, min(f_end, f_beg + kList), listf);
+  if (q_beg < q_end) build_list(TIER_Q, q_beg, min(q_end, q_beg + kList), listq);
+  FB FA;   // the wave's first bf16 tile, in flight while INT2 tiles are decoded
+  // ---------------------------------------------------------- INT2 tiles
+  // two tiles in flight; a buffer is refilled as soon as its tile is consumed
+  // (sched_barrier keeps the loads ahead of the next tile's math).  Instanced
+  // with and without the early bf16 load so that the compiler counts the
+  // loads in flight exactly on both paths.
+  auto int2_tiles = [&](auto early_f) {
+    int cb = q_beg, nt = max(0, min(q_end, cb + kList) - cb);
+    QB A, Bq;
+    load_q(A, 0, nt);
+    load_q(Bq, 1, nt);
+    int i0 = 0;
+    if constexpr (decltype(early_f)::value) {
+      // The bf16 tile is requested once the first INT2 tile is in: all waves'
+      // INT2 data is then served ahead of the (larger) bf16 data, which
+      // arrives while INT2 tiles are decoded.  The first two tiles sit outside
+      // the loop, where the compiler can count the loads in flight exactly
+      // (every load here is unconditional); the loop's own count would make
+      // its first wait include the bf16 tile.
+      if (nt > 0) compute_q(A, 0);
+      load_q(A, 2, nt);
       __builtin_amdgcn_sched_barrier(0);
-      for (int i = 0; i < nt; i += 2) {
-        compute_f(A, i);
+      load_f(FA, 0, min(f_end, f_beg + kList) - f_beg);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nt > 1) compute_q(Bq, 1);
+      load_q(Bq, 3, nt);
+      __builtin_amdgcn_sched_barrier(0);
+      i0 = 2;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    while (nt > 0) {
+      for (int i = i0; i < nt; i += 2) {
+        compute_q(A, i);
         if (i + 1 >= nt) break;
-        load_f(A, i + 2, nt);
+        load_q(A, i + 2, nt);
         __builtin_amdgcn_sched_barrier(0);
-        compute_f(Bf, i + 1);
-        load_f(Bf, i + 3, nt);   // (empty past the end: one path back to the loop head)
+        compute_q(Bq, i + 1);
+        load_q(Bq, i + 3, nt);   // (empty past the end: one path back to the loop head)
         __builtin_amdgcn_sched_barrier(0);
       }
       drain_loads();   // the last (empty) prefetch: nothing pending into the next chunk
-      flush_masses(nt);
+      flush_masses(nt, listq);
+      cb += kList;
+      nt = max(0, min(q_end, cb + kList) - cb);
+      i0 = 0;
+      if (nt > 0) {
+        build_list(TIER_Q, cb, cb + nt, listq);
+        load_q(A, 0, nt);
+        load_q(Bq, 1, nt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
+  };
+  if (f_beg < f_end)
+    int2_tiles(std::true_type{});
+  else
+    int2_tiles(std::false_type{});
 
-  // ---------------------------------------------------------- INT2 tiles
-  {
-    const uint32_t kMaskR = 0x03000300u, kOneR = 0x3C003C00u;   // decode constants
-    f16x8 q4[KK];     // 4q in fp16, formed here so it never shares registers with the bf16 buffers
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(4.f * float(qb[kk][e]));
-    const layout::LedgerTile LT(D);
-    struct QB {
-      uint32_t kc[CW], vc[CW], sc[CW];
-    };
-    auto load_words = [&](__amdgpu_buffer_rsrc_t rs, int off, uint32_t (&w)[CW]) {
-      if constexpr (CW == 4) {
-        const uint4 u = load16(rs, off + lane * 16);
-        w[0] = u.x;
-        w[1] = u.y;
-        w[2] = u.z;
-        w[3] = u.w;
-      } else {
-        const uint2 u = load8(rs, off + lane * 8);
-        w[0] = u.x;
-        w[1] = u.y;
-      }
-    };
-    auto load_q = [&](QB& qq, int i, int nt) {
-      const uint32_t e = uniform(int(list[min(i, nt - 1)]));
-      const uint8_t* t = pv.entry(seg, te_slot(e), kvh) + size_t(te_tile(e)) * LT.bytes;
-      const auto rs = tile_rsrc(t, i < nt ? LT.bytes : 0);
-      load_words(rs, LT.kc, qq.kc);
-      load_words(rs, LT.vc, qq.vc);
-      load_words(rs, LT.ks, qq.sc);
-    };
-    uint8_t* scb = s_scb[wid];
-    auto compute_q = [&](QB& qq, int t) {
-      // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer
-      if constexpr (CW == 4)
-        reinterpret_cast<uint4*>(scb)[lane] = make_uint4(qq.sc[0], qq.sc[1], qq.sc[2], qq.sc[3]);
-      else
-        reinterpret_cast<uint2*>(scb)[lane] = make_uint2(qq.sc[0], qq.sc[1]);
-      const f16x8* ks = reinterpret_cast<const f16x8*>(scb);              // [D]
-      const f16x8* km = reinterpret_cast<const f16x8*>(scb + 2 * D);      // [D]
-      const f16x8* vs = reinterpret_cast<const f16x8*>(scb + 4 * D);      // [D/32][32]
-      const f16x8* vm = reinterpret_cast<const f16x8*>(scb + 6 * D);
-      // Each lane forms its own B operand: 4 s q as an fp16 product plus its
-      // exact fp16 residual (fma TwoProduct), and its share of the tile
-      // constant sum_d q (m - 4 s) = sum 4q m / 4 - sum 4q s (fp16 pairs,
-      // fp32 sums), completed across the 4 lane groups.
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      float cm = 0.f, cs = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const f16x8 s8 = ks[4 * kk + g], m8 = km[4 * kk + g];
-        const f16x8 qh = q4[kk] * s8;
-        const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const f16x2 qq2 = {q4[kk][2 * e2], q4[kk][2 * e2 + 1]};
-          cm = __builtin_amdgcn_fdot2(qq2, f16x2{m8[2 * e2], m8[2 * e2 + 1]}, cm, false);
-          cs = __builtin_amdgcn_fdot2(qq2, f16x2{s8[2 * e2], s8[2 * e2 + 1]}, cs, false);
-        }
-        const int c0 = kk, c1 = KK + kk;                               // chunks of blk 0 / 1
-        const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1], kMaskR, kOneR)
-                                  : decode_codes<0>(qq.kc[c0 >> 1], kMaskR, kOneR);
-        const f16x8 a1 = (c1 & 1) ? decode_codes<1>(qq.kc[c1 >> 1], kMaskR, kOneR)
-                                  : decode_codes<0>(qq.kc[c1 >> 1], kMaskR, kOneR);
-        s0 = mfma_f16(a0, qh, s0);
-        s0 = mfma_f16(a0, ql, s0);
-        s1 = mfma_f16(a1, qh, s1);
-        s1 = mfma_f16(a1, ql, s1);
-      }
-      // the MFMA result lanes (g, hn) hold head hn, as the B operand lanes do
-      const float bias0 = sum_rows(fmaf(cm, 0.25f, -cs));
-      float z[8], p[8], rs;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        z[i4] = (s0[i4] + bias0) * qscale;
-        z[4 + i4] = (s1[i4] + bias0) * qscale;
-      }
-      softmax_tile<NB>(st, z, p, &rs);
-      // 4p as fp16 high + low parts, then 4 p s' = high*s' + (exact residual
-      // of that product + low*s'), all in packed fp16
-      f16x8 p4, p4l;
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        const float x = 4.f * p[e2];
-        p4[e2] = (_Float16)x;
-        p4l[e2] = (_Float16)(x - float(p4[e2]));
-      }
-      // v = (m' - 4 s') + (1 + c/4) 4 s': the min term sum_t 4p (m'/4 - s') on
-      // the MFMA with both factors as fp16 high + low parts (row = 32-channel
-      // group jr; rows >= D/32 repeat them and are not read)
-      {
-        const int jr = hn & (D / 32 - 1);
-        const f16x8 vm8 = vm[4 * jr + g], vs8 = vs[4 * jr + g];
-        f16x8 mvh, mvl;
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) {
-          const float x = fmaf(float(vm8[e2]), 0.25f, -float(vs8[e2]));
-          mvh[e2] = (_Float16)x;
-          mvl[e2] = (_Float16)(x - float(mvh[e2]));
-        }
-        st.ob = mfma_f16(mvh, p4, st.ob);
-        st.ob = mfma_f16(mvh, p4l, st.ob);
-        st.ob = mfma_f16(mvl, p4, st.ob);
-      }
-#pragma unroll
-      for (int jd = 0; jd < D / 32; ++jd) {
-        const f16x8 sv = vs[4 * jd + g];
-        const f16x8 ph = p4 * sv;
-        const f16x8 pl = __builtin_elementwise_fma(p4l, sv, __builtin_elementwise_fma(p4, sv, -ph));
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int nb = 2 * jd + h2;
-          const f16x8 av = (nb & 1) ? decode_codes<1>(qq.vc[nb >> 1], kMaskR, kOneR)
-                                    : decode_codes<0>(qq.vc[nb >> 1], kMaskR, kOneR);
-          st.o[nb] = mfma_f16(av, ph, st.o[nb]);
-          st.o[nb] = mfma_f16(av, pl, st.o[nb]);
-        }
-      }
-      if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
-    };
-    for (int cb = q_beg; cb < q_end; cb += kList) {
-      const int ce = min(q_end, cb + kList), nt = ce - cb;
-      build_list(TIER_Q, cb, ce);
-      // groups of kQGroup tiles: a whole group's loads are in flight together,
-      // and the next group's loads are issued before this group is computed
-      QB A[kQGroup], Bq[kQGroup];
-      auto load_group = [&](QB (&grp)[kQGroup], int i0) {
-#pragma unroll
-        for (int j = 0; j < kQGroup; ++j) load_q(grp[j], i0 + j, nt);
-      };
-      auto compute_group = [&](QB (&grp)[kQGroup], int i0) {
-#pragma unroll
-        for (int j = 0; j < kQGroup; ++j)
-          if (i0 + j < nt) compute_q(grp[j], i0 + j);
-      };
-      load_group(A, 0);
-      load_group(Bq, kQGroup);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int i = 0; i < nt; i += 2 * kQGroup) {
-        compute_group(A, i);
-        if (i + kQGroup >= nt) break;
-        load_group(A, i + 2 * kQGroup);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_group(Bq, i + kQGroup);
-        load_group(Bq, i + 3 * kQGroup);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      drain_loads();
-      flush_masses(nt);
+  // ---------------------------------------------------------- bf16 tiles
+  for (int cb = f_beg; cb < f_end; cb += kList) {
+    const int ce = min(f_end, cb + kList), nt = ce - cb;
+    if (cb != f_beg) {
+      build_list(TIER_F, cb, ce, listf);
+      load_f(FA, 0, nt);
     }
+    FB Bf;
+    load_f(Bf, 1, nt);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < nt; i += 2) {
+      compute_f(FA, i);
+      if (i + 1 >= nt) break;
+      load_f(FA, i + 2, nt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_f(Bf, i + 1);
+      load_f(Bf, i + 3, nt);   // (empty past the end: one path back to the loop head)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    drain_loads();
+    flush_masses(nt, listf);
   }
 
   // -------------------------------------------- combine the 4 waves in LDS
