@@ -197,7 +197,7 @@ __device__ inline void softmax_tile(WaveState<NB>& st, const float (&z)[8], floa
 
 }  // namespace
 
-template <int D>
+template <int D, int GP>
 __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   constexpr int KK = D / 32;   // 32-dim slices of the QK product
   constexpr int NB = D / 16;   // 16-channel blocks of the PV product (= code chunks per part)
@@ -215,23 +215,31 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
-  const int g = lane >> 4, hn = lane & 15;   // lane = (column block g, head hn)
+  const int g = lane >> 4, hn = lane & 15;   // lane = (column block g, column hn)
+  // The 16 MFMA columns carry the query heads replicated: column hn holds head
+  // hh = hn % GP of column group jc = hn / GP (GP = 4 when G <= 4, else 8).
+  // bf16 tiles and INT2 logits give every group the same values; in an INT2
+  // tile's V product group jc carries the scales of one 32-channel group, so
+  // a single B operand serves RG channel groups (NPASS operands per tile).
+  constexpr int RG = (D / 32) < (16 / GP) ? (D / 32) : (16 / GP);
+  constexpr int NPASS = (D / 32) / RG;
+  const int hh = hn % GP, jc = hn / GP;
   const int W = pv.W, maxw = pv.maxw, TPW = W / 32, G = pv.G;
   const int seg = a.layer * pv.B + b;
   const int S = a.splits;
 
   // ------------------------------------------------------------ the query
   // issued first: it does not depend on the plan.  Lane (g, hn) holds channels
-  // 32kk + 8g .. 32kk + 8g + 7 of head hn: the B operand of the QK products.
+  // 32kk + 8g .. 32kk + 8g + 7 of head hh: the B operand of the QK products.
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e / sqrtf(float(D));
   bf16x8 qb[KK];    // q (bf16)
   {
-    const uint16_t* qp = a.q + (size_t(b) * pv.Hq + size_t(kvh) * G + hn) * D + 8 * g;
+    const uint16_t* qp = a.q + (size_t(b) * pv.Hq + size_t(kvh) * G + hh) * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (hn < G) u = *reinterpret_cast<const uint4*>(qp + 32 * kk);
+      if (hh < G) u = *reinterpret_cast<const uint4*>(qp + 32 * kk);
       qb[kk] = as_bf16x8(u);
     }
   }
@@ -559,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       s1 = mfma_f16(a1, qh, s1);
       s1 = mfma_f16(a1, ql, s1);
     }
-    // the MFMA result lanes (g, hn) hold head hn, as the B operand lanes do
+    // the MFMA result lanes (g, hn) hold head hh, as the B operand lanes do
     const float bias0 = sum_rows(fmaf(cm, 0.25f, -cs));
     float z[8], p[8], rs;
 #pragma unroll
@@ -594,14 +602,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       st.ob = mfma_f16(mvh, p4l, st.ob);
       st.ob = mfma_f16(mvl, p4, st.ob);
     }
+    // one B operand per pass: column group jc takes channel group
+    // ps * RG + jc (the other groups' columns of st.o[nb] are not read)
 #pragma unroll
-    for (int jd = 0; jd < D / 32; ++jd) {
-      const f16x8 sv = vs[4 * jd + g];
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const f16x8 sv = vs[4 * (ps * RG + jc % RG) + g];
       const f16x8 ph = p4 * sv;
       const f16x8 pl = __builtin_elementwise_fma(p4l, sv, __builtin_elementwise_fma(p4, sv, -ph));
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int nb = 2 * jd + h2;
+      for (int nb = 2 * ps * RG; nb < 2 * (ps + 1) * RG; ++nb) {
         const f16x8 av = (nb & 1) ? decode_codes<1>(qq.vc[nb >> 1], kMaskR, kOneR)
                                   : decode_codes<0>(qq.vc[nb >> 1], kMaskR, kOneR);
         st.o[nb] = mfma_f16(av, ph, st.o[nb]);
@@ -695,11 +704,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   }
 
   // -------------------------------------------- combine the 4 waves in LDS
-  if (hn < G) {
+  // channels of block nb come from the column group that carried their
+  // channel group's scales (any group for the min term, m and l)
+  if (hh < G) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
+      if (jc == (nb / 2) % RG) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) s_wo[wid][hn][16 * nb + 4 * g + i4] = st.o[nb][i4];
+        for (int i4 = 0; i4 < 4; ++i4) s_wo[wid][hh][16 * nb + 4 * g + i4] = st.o[nb][i4];
+      }
+  }
+  if (hn < G) {
     if (g == 0) {
       s_wm[wid][hn] = st.m_run;
       s_wl[wid][hn] = st.l_run;
@@ -968,16 +983,21 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   }
 }
 
+template <int D, int GP>
+static hipError_t launch_attn_kernel(const PoolView& pv, const AttnArgs& a, size_t shm, hipStream_t s) {
+  if (a.ev_start || a.ev_stop) {
+    hipExtLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
+                          a.ev_start, a.ev_stop, 0u, pv, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pv, a);
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream_t s) {
   const size_t shm = (2 * size_t(a.plan_words) + (pv.nb + 31) / 32) * 4;
-  if (a.ev_start || a.ev_stop) {
-    hipExtLaunchKernelGGL((attn_kernel<D>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
-                          a.ev_start, a.ev_stop, 0u, pv, a);
-  } else {
-    hipLaunchKernelGGL((attn_kernel<D>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pv, a);
-  }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = pv.G <= 4 ? launch_attn_kernel<D, 4>(pv, a, shm, s) : launch_attn_kernel<D, 8>(pv, a, shm, s);
   if (e != hipSuccess) return e;
   const int mass_blocks = (a.mass || a.acc_scores) ? (pv.maxw + kMassWindows - 1) / kMassWindows : 0;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(pv.Hkv * (D / 32) + mass_blocks, pv.B), dim3(256),
