@@ -86,6 +86,17 @@ __device__ inline float sum_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// x summed over the column groups of a 16-lane row: lanes n, n + 16/NREP, ..
+// (DPP row rotations by 4 and 8 lanes, or by 8 alone)
+template <int NREP>
+__device__ inline float sum_groups_t(float x) {
+  if constexpr (NREP == 4)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+  if constexpr (NREP >= 2)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+  return x;
+}
+
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -166,8 +177,8 @@ __device__ inline int te_tile(uint32_t e) { return int(e >> 27); }
 template <int NB>
 struct WaveState {
   float m_run, l_run;
-  f32x4 o[NB];   // O^T block nb: lane (g, n) holds head n, channels 16nb + 4g + i
-  f32x4 ob;      // INT2 V min term: lane (0, n) holds head n, channel group i
+  f32x4 o[NB];   // O^T block nb: lane (g, n) holds column n, channels 16nb + 4g + i
+  f32x4 ob;      // 4 x INT2 V min term: lane (0, n) holds column n, channel group i
 };
 
 template <int NB>
@@ -223,6 +234,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   // a single B operand serves RG channel groups (NPASS operands per tile).
   constexpr int RG = (D / 32) < (16 / GP) ? (D / 32) : (16 / GP);
   constexpr int NPASS = (D / 32) / RG;
+  constexpr int NREP = 16 / GP;                            // column groups
+  constexpr int NKK = (D / 32) > NREP ? (D / 32) / NREP : 1;   // tile-constant slices per lane
   const int hh = hn % GP, jc = hn / GP;
   const int W = pv.W, maxw = pv.maxw, TPW = W / 32, G = pv.G;
   const int seg = a.layer * pv.B + b;
@@ -504,6 +517,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
     for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(4.f * float(qb[kk][e]));
+  // this lane's slices of the tile constant: q4[jc + i * NREP], zero past KK
+  f16x8 q4s[NKK];
+#pragma unroll
+  for (int i = 0; i < NKK; ++i) {
+    q4s[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      if (jc + i * NREP == kk) q4s[i] = q4[kk];
+  }
   const layout::LedgerTile LT(D);
   struct QB {
     uint32_t kc[CW], vc[CW], sc[CW];
@@ -541,22 +563,28 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     const f16x8* vs = reinterpret_cast<const f16x8*>(scb + 4 * D);      // [D/32][32]
     const f16x8* vm = reinterpret_cast<const f16x8*>(scb + 6 * D);
     // Each lane forms its own B operand: 4 s q as an fp16 product plus its
-    // exact fp16 residual (fma TwoProduct), and its share of the tile
-    // constant sum_d q (m - 4 s) = sum 4q m / 4 - sum 4q s (fp16 pairs,
-    // fp32 sums), completed across the 4 lane groups.
+    // exact fp16 residual (fma TwoProduct).  The tile constant
+    // sum_d q (m - 4 s) = sum 4q m / 4 - sum 4q s (fp16 pairs, fp32 sums) is
+    // split over the column groups (group jc takes slices jc, jc + NREP, ..)
+    // and completed across groups and lane rows.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     float cm = 0.f, cs = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const f16x8 s8 = ks[4 * kk + g], m8 = km[4 * kk + g];
-      const f16x8 qh = q4[kk] * s8;
-      const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
+    for (int i = 0; i < NKK; ++i) {
+      const int kk = min(jc + i * NREP, KK - 1);   // q4s is zero past the last slice
+      const f16x8 m8 = km[4 * kk + g], s8 = ks[4 * kk + g];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const f16x2 qq2 = {q4[kk][2 * e2], q4[kk][2 * e2 + 1]};
+        const f16x2 qq2 = {q4s[i][2 * e2], q4s[i][2 * e2 + 1]};
         cm = __builtin_amdgcn_fdot2(qq2, f16x2{m8[2 * e2], m8[2 * e2 + 1]}, cm, false);
         cs = __builtin_amdgcn_fdot2(qq2, f16x2{s8[2 * e2], s8[2 * e2 + 1]}, cs, false);
       }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const f16x8 s8 = ks[4 * kk + g];
+      const f16x8 qh = q4[kk] * s8;
+      const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
       const int c0 = kk, c1 = KK + kk;                               // chunks of blk 0 / 1
       const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1], kMaskR, kOneR)
                                 : decode_codes<0>(qq.kc[c0 >> 1], kMaskR, kOneR);
@@ -568,7 +596,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       s1 = mfma_f16(a1, ql, s1);
     }
     // the MFMA result lanes (g, hn) hold head hh, as the B operand lanes do
-    const float bias0 = sum_rows(fmaf(cm, 0.25f, -cs));
+    const float bias0 = sum_rows(sum_groups_t<NREP>(fmaf(cm, 0.25f, -cs)));
     float z[8], p[8], rs;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -585,22 +613,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
       p4[e2] = (_Float16)x;
       p4l[e2] = (_Float16)(x - float(p4[e2]));
     }
-    // v = (m' - 4 s') + (1 + c/4) 4 s': the min term sum_t 4p (m'/4 - s') on
-    // the MFMA with both factors as fp16 high + low parts (row = 32-channel
-    // group jr; rows >= D/32 repeat them and are not read)
+    // v = (m' - 4 s') + (1 + c/4) 4 s'.  The min term, 4 times over:
+    // sum_t 4p m' + sum_t 4p (-4 s'), straight from the fp16 scales (-4 s'
+    // is exact; exact products; row = 32-channel group jr, rows >= D/32
+    // repeat and are not read).
     {
       const int jr = hn & (D / 32 - 1);
-      const f16x8 vm8 = vm[4 * jr + g], vs8 = vs[4 * jr + g];
-      f16x8 mvh, mvl;
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        const float x = fmaf(float(vm8[e2]), 0.25f, -float(vs8[e2]));
-        mvh[e2] = (_Float16)x;
-        mvl[e2] = (_Float16)(x - float(mvh[e2]));
-      }
-      st.ob = mfma_f16(mvh, p4, st.ob);
-      st.ob = mfma_f16(mvh, p4l, st.ob);
-      st.ob = mfma_f16(mvl, p4, st.ob);
+      const f16x8 vm8 = vm[4 * jr + g], vn8 = vs[4 * jr + g] * (_Float16)(-4.f);
+      st.ob = mfma_f16(vm8, p4, st.ob);
+      st.ob = mfma_f16(vm8, p4l, st.ob);
+      st.ob = mfma_f16(vn8, p4, st.ob);
+      st.ob = mfma_f16(vn8, p4l, st.ob);
     }
     // one B operand per pass: column group jc takes channel group
     // ps * RG + jc (the other groups' columns of st.o[nb] are not read)
@@ -734,7 +757,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < kAttnWaves; ++v) {
       const float sc = s_wm[v][h] == -INFINITY ? 0.f : fast_exp2(s_wm[v][h] - M);
-      acc += sc * (s_wo[v][h][d] + s_wb[v][h][d >> 5]);
+      acc += sc * fmaf(0.25f, s_wb[v][h][d >> 5], s_wo[v][h][d]);   // s_wb: 4 x the min term
     }
     part[idx] = acc;
   }
