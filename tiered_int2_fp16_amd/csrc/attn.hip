@@ -181,28 +181,42 @@ struct WaveState {
   f32x4 ob;      // 4 x INT2 V min term: lane (0, n) holds column n, channel group i
 };
 
-template <int NB>
-__device__ inline void softmax_tile(WaveState<NB>& st, const float (&z)[8], float (&p)[8], float* rs_out) {
-  float tm = z[0];
+// Online softmax over one tile of 8 scores per lane, z = s * scale + shift
+// (scale > 0; a score of -inf is a masked token).  The reference max m_run is
+// raised lazily: only when some head's tile max exceeds it by more than kTau
+// do all heads move to their new max and the accumulators rescale (not at all
+// on the wave's first tile, when they are still zero).  Until then a tile's
+// values are taken against the older reference, so p <= 2^kTau.  Returns
+// p[e] = 2^LG exp2(z[e] - m_run) and the tile sum of exp2(z - m_run).
+constexpr float kTau = 3.f;   // 4p <= 32 keeps 4p*s' in fp16 range for |s'| < 2047
+
+template <int NB, int LG>
+__device__ inline void softmax_tile(WaveState<NB>& st, const float (&s)[8], float scale, float shift,
+                                    float (&p)[8], float* rs_out) {
+  float sm = s[0];
 #pragma unroll
-  for (int e = 1; e < 8; ++e) tm = fmaxf(tm, z[e]);
-  tm = max_rows(tm);
-  const float mn = fmaxf(st.m_run, tm);
-  const float alpha = fast_exp2(st.m_run - mn);
+  for (int e = 1; e < 8; ++e) sm = fmaxf(sm, s[e]);
+  const float tm = fmaf(max_rows(sm), scale, shift);
+  if (__builtin_amdgcn_ballot_w64(tm > st.m_run + kTau)) {
+    const float mn = fmaxf(st.m_run, tm);
+    if (st.m_run != -INFINITY) {   // the same on every lane: all heads start and move together
+      const float alpha = fast_exp2(st.m_run - mn);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) st.o[nb] *= alpha;
+      st.ob *= alpha;
+      st.l_run *= alpha;
+    }
+    st.m_run = mn;
+  }
+  const float off = shift - st.m_run + float(LG);
   float rs = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = fast_exp2(z[e] - mn);
+    p[e] = fast_exp2(fmaf(s[e], scale, off));
     rs += p[e];
   }
-  rs = sum_rows(rs);
-  st.l_run = st.l_run * alpha + rs;
-  st.m_run = mn;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) st.o[nb] *= alpha;
-    st.ob *= alpha;
-  }
+  rs = sum_rows(rs) * (1.f / float(1 << LG));
+  st.l_run += rs;
   *rs_out = rs;
 }
 
@@ -431,10 +445,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     // the token counts once: only lane group 0 carries it into the softmax;
     // its probability then reaches the other groups' output channels
     float z[8], p[8], rs;
-    z[0] = g == 0 ? zp * qscale : -INFINITY;
+    z[0] = g == 0 ? zp : -INFINITY;
 #pragma unroll
     for (int e = 1; e < 8; ++e) z[e] = -INFINITY;
-    softmax_tile<NB>(st, z, p, &rs);
+    softmax_tile<NB, 0>(st, z, qscale, 0.f, p, &rs);
     const float p0 = __shfl(p[0], hn, 64);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -481,10 +495,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     float z[8], p[8], rs;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      z[i4] = (8 * g + i4 < valid) ? s0[i4] * qscale : -INFINITY;
-      z[4 + i4] = (8 * g + 4 + i4 < valid) ? s1[i4] * qscale : -INFINITY;
+      z[i4] = (8 * g + i4 < valid) ? s0[i4] : -INFINITY;
+      z[4 + i4] = (8 * g + 4 + i4 < valid) ? s1[i4] : -INFINITY;
     }
-    softmax_tile<NB>(st, z, p, &rs);
+    softmax_tile<NB, 0>(st, z, qscale, 0.f, p, &rs);
     if (valid < 32) {   // stale values past the last token: zero them (0 * NaN)
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
@@ -597,19 +611,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     }
     // the MFMA result lanes (g, hn) hold head hh, as the B operand lanes do
     const float bias0 = sum_rows(sum_groups_t<NREP>(fmaf(cm, 0.25f, -cs)));
-    float z[8], p[8], rs;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      z[i4] = (s0[i4] + bias0) * qscale;
-      z[4 + i4] = (s1[i4] + bias0) * qscale;
-    }
-    softmax_tile<NB>(st, z, p, &rs);
+    const float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float p[8], rs;
+    softmax_tile<NB, 2>(st, z, qscale, bias0 * qscale, p, &rs);   // p = 4 x probability
     // 4p as fp16 high + low parts, then 4 p s' = high*s' + (exact residual
     // of that product + low*s'), all in packed fp16
     f16x8 p4, p4l;
 #pragma unroll
     for (int e2 = 0; e2 < 8; ++e2) {
-      const float x = 4.f * p[e2];
+      const float x = p[e2];
       p4[e2] = (_Float16)x;
       p4l[e2] = (_Float16)(x - float(p4[e2]));
     }
