@@ -24,6 +24,11 @@ SOURCES = ["api.hip", "attn.hip", "route.hip", "transitions.hip", "host_core.cpp
 ARCH = os.environ.get("KVTIER_ARCH", "gfx950")
 
 
+# Sources whose kernels take leading scalar arguments meant to be preloaded
+# (attn_kernel: page table, token counts, row length).
+KERNARG_PRELOAD = {"attn.hip": 3}
+
+
 def hipcc() -> str:
     for c in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"), shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -42,6 +47,9 @@ def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     cmd = [hipcc()] + _flags() + ["-c", path, "-o", obj]
+    if src in KERNARG_PRELOAD:
+        # the first N kernel arguments of every kernel in the file arrive in SGPRs
+        cmd[1:1] = ["-mllvm", f"-amdgpu-kernarg-preload-count={KERNARG_PRELOAD[src]}"]
     if src.endswith(".cpp"):
         cmd = [hipcc(), "-O2", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
                "-x", "c++", "-c", path, "-o", obj]

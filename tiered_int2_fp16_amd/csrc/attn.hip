@@ -222,8 +222,13 @@ __device__ inline void softmax_tile(WaveState<NB>& st, const float (&s)[8], floa
 
 }  // namespace
 
+// The first three arguments (the layer's page table and token counts, the
+// page table's row length) come preloaded in SGPRs (the library is built with
+// kernarg preloading), so the plan's first loads need no kernel-argument load.
 template <int D, int GP>
-__global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict__ pages_layer,
+                                                      const int32_t* __restrict__ tokens_layer, int maxw_arg,
+                                                      PoolView pv, AttnArgs a) {
   constexpr int KK = D / 32;   // 32-dim slices of the QK product
   constexpr int NB = D / 16;   // 16-channel blocks of the PV product (= code chunks per part)
   constexpr int CW = D / 32;   // 32-bit code words per lane per part
@@ -255,6 +260,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   const int seg = a.layer * pv.B + b;
   const int S = a.splits;
 
+  // ------------------------------------- first: page table and token count
+  // issued before anything that needs the kernel arguments in memory; the
+  // first 1024 entries of the table (entries past the row read 0)
+  uint32_t e_first[4];
+  {
+    const auto prs = tile_rsrc(pages_layer + size_t(b) * maxw_arg, maxw_arg * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e_first[j] = load4(prs, (256 * j + tid) * 4);
+  }
+  // (a vector load, so it goes out now rather than after the argument loads)
+  const uint32_t len_raw = load4(tile_rsrc(tokens_layer, (b + 1) * 4), b * 4);
+
   // ------------------------------------------------------------ the query
   // issued first: it does not depend on the plan.  Lane (g, hn) holds channels
   // 32kk + 8g .. 32kk + 8g + 7 of head hh: the B operand of the QK products.
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
   uint32_t* s_pe = s_dyn;                                        // [roundup(maxw, 256)]
   int* s_ex = reinterpret_cast<int*>(s_dyn + a.plan_words);      // [roundup(maxw, 256)]
   uint32_t* s_used = s_dyn + 2 * a.plan_words;                   // bf16 slot bitmap (append)
-  const int len_old = pv.tokens[seg];
+  const int len_old = uniform(int(len_raw));
   const uint32_t* gp = pv.pages + size_t(seg) * maxw;
   const int n_old = windows_of(len_old, W);
   auto tiles_of = [&](uint32_t e, int w) -> int {
@@ -290,12 +307,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
     return t == TIER_F ? vt : (t == TIER_Q ? (vt << 16) : 0);
   };
   {
-    const auto pt = tile_rsrc(gp, maxw * 4);   // lanes past the table read 0
     const int JR = a.plan_words / 256;
-    for (int j0 = 0; j0 < JR; j0 += 4) {
-      uint32_t e4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) e4[j] = load4(pt, (256 * (j0 + j) + tid) * 4);
+    auto stage = [&](const uint32_t (&e4)[4], int j0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (j0 + j < JR) {
@@ -307,6 +320,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(PoolView pv, AttnArgs a) {
           if (lane == 63) s_gt[w >> 6] = incl;
         }
       }
+    };
+    stage(e_first, 0);
+    const auto pt = tile_rsrc(gp, maxw * 4);   // lanes past the table read 0
+    for (int j0 = 4; j0 < JR; j0 += 4) {
+      uint32_t e4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e4[j] = load4(pt, (256 * (j0 + j) + tid) * 4);
+      stage(e4, j0);
     }
   }
   __syncthreads();
@@ -1018,11 +1039,14 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
 
 template <int D, int GP>
 static hipError_t launch_attn_kernel(const PoolView& pv, const AttnArgs& a, size_t shm, hipStream_t s) {
+  const uint32_t* pl = pv.pages + size_t(a.layer) * pv.B * pv.maxw;
+  const int32_t* tl = pv.tokens + size_t(a.layer) * pv.B;
   if (a.ev_start || a.ev_stop) {
     hipExtLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
-                          a.ev_start, a.ev_stop, 0u, pv, a);
+                          a.ev_start, a.ev_stop, 0u, pl, tl, pv.maxw, pv, a);
   } else {
-    hipLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pv, a);
+    hipLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pl, tl, pv.maxw,
+                       pv, a);
   }
   return hipGetLastError();
 }
