@@ -226,6 +226,43 @@ def main():
         B.kv_attn_profile(p.h, 0)
     attn_ms = float(np.mean(durs))
 
+    # -------------------------------------- cost of emitting the window mass
+    # The same decode steps (attention + combine, no routing), each variant
+    # captured in a HIP graph and replayed: with the mass emission and score
+    # update, and with mass = NULL (what a step that does not feed the router
+    # would save).
+    def step_graph(with_mass, count):
+        gr = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream(device=dev)
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(gr, stream=st):
+                for i in range(count):
+                    r = i % R
+                    if with_mass:
+                        pools[r].attn(0, Q[i % nq], out=outs[r], mass=masses[r], scores=True)
+                    else:
+                        pools[r].attn(0, Q[i % nq], out=outs[r], want_mass=False)
+        torch.cuda.synchronize()
+        return gr
+
+    def replay_us(gr, count):
+        gr.replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        gr.replay()
+        torch.cuda.synchronize()
+        return 1e6 * (time.perf_counter() - t) / count
+
+    n_me = max(R, min(K_steps, 256))
+    g_with, g_without = step_graph(True, n_me), step_graph(False, n_me)
+    mass_us = [replay_us(g_with, n_me), replay_us(g_without, n_me), replay_us(g_with, n_me),
+               replay_us(g_without, n_me)]
+    del g_with, g_without
+    mass_emission = {"steps": n_me, "with_mass_us": round((mass_us[0] + mass_us[2]) / 2, 3),
+                     "without_mass_us": round((mass_us[1] + mass_us[3]) / 2, 3)}
+    mass_emission["overhead_us"] = round(mass_emission["with_mass_us"] - mass_emission["without_mass_us"], 3)
+
     per_attn = attn_bytes(c, n_f, n_q, n)
     total_bytes = K_steps * (per_attn + score_bytes(c, n)) + \
         len(routed) * route_bytes(c, n, 0, 0) + route_bytes(c, 0, fq, pr)
@@ -259,6 +296,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(khash)},
         "kernel_source_hash": khash,
+        "mass_emission": mass_emission,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)

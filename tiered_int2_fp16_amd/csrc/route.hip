@@ -54,17 +54,40 @@ __device__ inline void device_tier_counts(int n, int R, double beta, double phi,
   *lo = l;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
+// 16-lane rows, then row broadcasts across them).
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Ranking key of an eligible window: the score's bits made order-preserving
+// as an unsigned integer in the high word, ~w in the low word, so that
+// key(x) > key(w) exactly when S[x] > S[w], or S[x] == S[w] and x < w.
+// Ineligible windows get 0, below every eligible key.
+__device__ inline uint64_t rank_key(float score, int w) {
+  uint32_t b = __float_as_uint(score);
+  if (b == 0x80000000u) b = 0u;   // -0 ties with +0, as the float compare has it
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (uint64_t(o) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(w));
+}
+
 // One workgroup per sequence: rank the eligible windows by counting, assign
 // tiers, emit the transition lists in ascending window order, apply evictions.
 __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, double beta, double phi,
                                                      int32_t* transitions, int32_t* counts) {
-  extern __shared__ uint32_t smem[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
   const int maxw = pv.maxw, kpad = (maxw + 7) & ~7;
-  float* key = reinterpret_cast<float*>(smem);               // [kpad] score of eligible windows, else NaN
-  int* rank = reinterpret_cast<int*>(smem + kpad);           // [maxw]
-  uint32_t* pages = smem + kpad + maxw;                      // [maxw]
-  uint8_t* newt = reinterpret_cast<uint8_t*>(smem + kpad + 2 * maxw);  // [maxw]
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem);         // [kpad] rank_key, 0 if not eligible
+  int* rank = reinterpret_cast<int*>(smem + 2 * kpad);       // [maxw]
+  uint32_t* pages = smem + 2 * kpad + maxw;                  // [maxw]
+  uint8_t* newt = reinterpret_cast<uint8_t*>(smem + 2 * kpad + 2 * maxw);  // [maxw]
   __shared__ int wave_tot[16][4];
   const int len = pv.tokens[seg];
   const int n = windows_of(len, pv.W);
@@ -77,10 +100,10 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
   const float* gs = pv.scores + size_t(seg) * maxw;
   const int fpad = (fr + 7) & ~7;
   for (int w = tid; w < fpad; w += blockDim.x) {
-    float k = __builtin_nanf("");
+    uint64_t k = 0;
     if (w < fr) {
       const uint32_t e = gp[w];
-      if (pe_tier(e) != TIER_E) k = gs[w];
+      if (pe_tier(e) != TIER_E) k = rank_key(gs[w], w);
     }
     key[w] = k;
   }
@@ -89,24 +112,28 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
     rank[w] = 0;
   }
   __syncthreads();
-  // rank[w] = number of eligible x with S[x] > S[w], or S[x] == S[w] and x < w
-  // (NaN keys never compare).  Thread jobs (w, part): each part counts one
-  // slice of x, eight keys per step.
+  // rank[w] = number of x with key[x] > key[w] (one unsigned compare per
+  // key).  Thread jobs (w, part): each part counts one slice of x, eight keys
+  // per step.
   {
     const int parts = fr > 0 ? max(1, min(8, int(blockDim.x) / fr)) : 1;
     const int chunk = ((fpad / 8 + parts - 1) / parts) * 8;
     for (int job = tid; job < fr * parts; job += blockDim.x) {
       const int w = job % fr, part = job / fr;
-      const float sw = key[w];
-      if (sw != sw) continue;   // not eligible
+      const uint64_t kw = key[w];
+      if (kw == 0) continue;   // not eligible
       const int x0 = part * chunk, x1 = min(fpad, x0 + chunk);
       int cnt = 0;
       for (int x = x0; x < x1; x += 8) {
-        const float4 a = *reinterpret_cast<const float4*>(key + x);
-        const float4 c = *reinterpret_cast<const float4*>(key + x + 4);
-        const float k8[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        uint64_t k8[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cnt += (k8[j] > sw) || (k8[j] == sw && x + j < w);
+        for (int j = 0; j < 8; j += 2) {
+          const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(key + x + j);
+          k8[j] = v.x;
+          k8[j + 1] = v.y;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cnt += k8[j] > kw;
       }
       if (cnt) atomicAdd(&rank[w], cnt);
     }
@@ -141,11 +168,7 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
   int pre[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    int x = c[k];
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
+    const int x = wave_incl_scan(c[k]);
     pre[k] = x - c[k];
     if (lane == 63) wave_tot[wid][k] = x;
   }
@@ -186,7 +209,7 @@ hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, 
     if (e != hipSuccess) return e;
   }
   if (do_route) {
-    const size_t shm = size_t((pv.maxw + 7) & ~7) * 4 + size_t(pv.maxw) * 9;
+    const size_t shm = size_t((pv.maxw + 7) & ~7) * 8 + size_t(pv.maxw) * 9;
     hipLaunchKernelGGL(route_kernel, dim3(pv.B), dim3(1024), shm, s, pv, layer, beta, phi, transitions,
                        counts);
     return hipGetLastError();
