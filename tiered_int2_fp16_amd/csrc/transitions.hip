@@ -75,12 +75,15 @@ hipError_t launch_prefill(const PoolView& pv, int layer, const uint16_t* k, cons
 // s = fp16((max - min) / 3), m = fp16(min); codes use the stored fp16 values:
 // c = clamp(rint_even((x - m) / s), 0, 3), or 0 when s == 0.  float32 IEEE
 // arithmetic throughout (correctly rounded divide, no contraction).
-__device__ inline void quant_group(float (&x)[32], uint8_t (&c)[32], uint16_t* s_out, uint16_t* m_out) {
-  float mn, mx;
+__device__ inline void quant_group(const float* xp, int xstride, uint8_t* cp, int cstride, uint16_t* s_out,
+                                   uint16_t* m_out) {
+  float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) x[i] = (x[i] == 0.f) ? 0.f : x[i];
-  mn = x[0];
-  mx = x[0];
+  for (int i = 0; i < 32; ++i) {
+    const float v = xp[i * xstride];
+    x[i] = (v == 0.f) ? 0.f : v;
+  }
+  float mn = x[0], mx = x[0];
 #pragma unroll
   for (int i = 1; i < 32; ++i) {
     mn = fminf(mn, x[i]);
@@ -91,14 +94,26 @@ __device__ inline void quant_group(float (&x)[32], uint8_t (&c)[32], uint16_t* s
   const _Float16 hs = (_Float16)s32;
   const _Float16 hm = (_Float16)mn;
   const float s = (float)hs, m = (float)hm;
+  // rint(fl(u / s)) from u * rcp(s).  Only the ties 1/2, 3/2, 5/2 decide a
+  // code (the clamp absorbs the rest), and near them the two quotients
+  // differ by under 1e-6, so the codes agree unless a quotient lies within
+  // 1e-5 of some k + 1/2: such values are redone with the exact division in
+  // a separate, rolled loop (it runs rarely; kept out of line, its code is
+  // not fetched with the common path).
+  const float rcp = s == 0.f ? 0.f : __builtin_amdgcn_rcpf(s);
+  uint32_t near = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    float q = 0.f;
-    if (s != 0.f) {
-      const float u = x[i] - m;
-      q = fminf(fmaxf(rintf(__fdiv_rn(u, s)), 0.f), 3.f);
-    }
-    c[i] = uint8_t(q);
+    const float r = (x[i] - m) * rcp;
+    near |= uint32_t(s != 0.f && fabsf(r - floorf(r) - 0.5f) < 1e-5f) << i;
+    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(r), 0.f), 3.f));
+  }
+  while (near) {
+    const int i = __builtin_ctz(near);
+    near &= near - 1;
+    const float v = xp[i * xstride];
+    const float u = ((v == 0.f) ? 0.f : v) - m;
+    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(__fdiv_rn(u, s)), 0.f), 3.f));
   }
   *s_out = __builtin_bit_cast(uint16_t, hs);
   *m_out = __builtin_bit_cast(uint16_t, hm);
@@ -225,24 +240,40 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 // Demote data kernel: quantise one tile of a bf16 window into its ledger
 // entry.  K groups are the tile's channels (32 tokens each), V groups each
 // token's 32-channel blocks.
+// (D, the head dimension, is a template parameter: the chunk and field index
+// arithmetic below then reduces to shifts and masks)
+template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
   __shared__ float xs[2][32][129];          // K, V of one tile, canonical [token][dim]
-  __shared__ uint8_t cs[2][32][128];        // their codes
-  const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, D = pv.D, TPW = W / 32;
+  __shared__ uint8_t cs[2][32][132];        // their codes (rows padded: no bank conflicts)
+  const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
   const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D);
   const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
+  // the first unit's work item is read together with the count (the item
+  // list always has room for it; it is used only if the count covers it)
+  const WorkItem first = work[blockIdx.x / (pv.Hkv * TPW)];
   const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int i = u / (pv.Hkv * TPW), r = u % (pv.Hkv * TPW), kvh = r / TPW, tile = r % TPW;
-    const WorkItem it = work[i];
+    const WorkItem it = u == int(blockIdx.x) ? first : work[i];
     if (it.flag != 1) continue;
     const uint16_t* tb = pv.block(seg, it.src, kvh) + size_t(tile) * 64 * D;
     uint8_t* et = pv.entry(seg, it.dst, kvh) + size_t(tile) * LT.bytes;
-    // the tile's 16-byte chunks, read in order, into the canonical layout
-    for (int c = tid; c < 8 * D; c += blockDim.x) {
+    // the tile's 16-byte chunks, all requested first, into the canonical layout
+    constexpr int kMaxChunks = 4;   // 8 * D / 256 for D <= 128
+    uint4 qv[kMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+      const int c = tid + j * 256;
+      if (c < 8 * D) qv[j] = reinterpret_cast<const uint4*>(tb)[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+      const int c = tid + j * 256;
+      if (c >= 8 * D) break;
       const int part = c / (4 * D), cc = c % (4 * D), cmb = cc >> 6, lane = cc & 63;
-      const uint4 q = reinterpret_cast<const uint4*>(tb + part * 32 * D)[cc];
+      const uint4 q = qv[j];
       const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -258,21 +289,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
     uint16_t* vs = reinterpret_cast<uint16_t*>(et + LT.vs);
     uint16_t* vm = reinterpret_cast<uint16_t*>(et + LT.vm);
     for (int g = tid; g < D + D; g += blockDim.x) {
-      float x[32];
-      uint8_t c[32];
-      if (g < D) {                       // K group: channel g over the tile's 32 tokens
-#pragma unroll
-        for (int t = 0; t < 32; ++t) x[t] = xs[0][t][g];
-        quant_group(x, c, ks + g, km + g);
-#pragma unroll
-        for (int t = 0; t < 32; ++t) cs[0][t][g] = c[t];
-      } else {                           // V group: token t, channels 32j..32j+31
+      if (g < D)   // K group: channel g over the tile's 32 tokens
+        quant_group(&xs[0][0][g], 129, &cs[0][0][g], 132, ks + g, km + g);
+      else {       // V group: token t, channels 32j..32j+31
         const int t = (g - D) / (D / 32), j = (g - D) % (D / 32);
-#pragma unroll
-        for (int e = 0; e < 32; ++e) x[e] = xs[1][t][32 * j + e];
-        quant_group(x, c, vs + j * 32 + t, vm + j * 32 + t);
-#pragma unroll
-        for (int e = 0; e < 32; ++e) cs[1][t][32 * j + e] = c[e];
+        quant_group(&xs[1][t][32 * j], 1, &cs[1][t][32 * j], 1, vs + j * 32 + t, vm + j * 32 + t);
       }
     }
     __syncthreads();
@@ -301,12 +322,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
 // A ledger chunk (lane, cmb) and the bf16 chunk (cmb, lane) hold the same 8
 // values, so each thread step turns one code half-word into one 16-byte chunk;
 // the tile's scale block is staged in LDS first.
+template <int D>
 __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
   __shared__ uint4 s_sc[64];   // Ks | Km | Vs | Vm of one tile (8 D bytes, D <= 128)
-  const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, D = pv.D, TPW = W / 32;
+  const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
   const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D);
   const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
+  // the first unit's work item is read together with the count (used only if
+  // the count covers it)
+  const WorkItem first = work[blockIdx.x / (pv.Hkv * TPW)];
   const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
   const _Float16* ks = reinterpret_cast<const _Float16*>(s_sc);
   const _Float16* km = ks + D;
@@ -314,17 +339,32 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
   const _Float16* vm = ks + 3 * D;
   for (int u = blockIdx.x; u < units; u += gridDim.x) {
     const int i = u / (pv.Hkv * TPW), r = u % (pv.Hkv * TPW), kvh = r / TPW, tile = r % TPW;
-    const WorkItem it = work[i];
+    const WorkItem it = u == int(blockIdx.x) ? first : work[i];
     if (it.flag != 1) continue;
     const uint8_t* et = pv.entry(seg, it.src, kvh) + size_t(tile) * LT.bytes;
     uint16_t* tb = pv.block(seg, it.dst, kvh) + size_t(tile) * 64 * D;
+    // every load of the tile before the barrier: the scale block and the
+    // code word of each of this thread's chunks
     if (tid < D / 2) s_sc[tid] = reinterpret_cast<const uint4*>(et + LT.ks)[tid];
+    constexpr int kMaxChunks = 4;   // 8 * D / 256 for D <= 128
+    uint32_t words[kMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+      const int c = tid + j * 256;
+      if (c < 8 * D) {
+        const bool is_v = c >= 4 * D;
+        const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
+        words[j] = reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + (cmb >> 1)];
+      }
+    }
     __syncthreads();
-    for (int c = tid; c < 8 * D; c += blockDim.x) {
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+      const int c = tid + j * 256;
+      if (c >= 8 * D) break;
       const bool is_v = c >= 4 * D;
       const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
-      const uint32_t word =
-          reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + (cmb >> 1)];
+      const uint32_t word = words[j];
       uint32_t out[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -371,9 +411,11 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   if (gx > max_units) gx = max_units;
   if (gx < 1) gx = 1;
   if (promote)
-    hipLaunchKernelGGL(dequant_kernel, dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer);
+    hipLaunchKernelGGL(pv.D == 64 ? dequant_kernel<64> : dequant_kernel<128>, dim3(unsigned(gx), pv.B), dim3(256),
+                       0, s, pv, layer);
   else
-    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer);
+    hipLaunchKernelGGL(pv.D == 64 ? quantize_kernel<64> : quantize_kernel<128>, dim3(unsigned(gx), pv.B),
+                       dim3(256), 0, s, pv, layer);
   return hipGetLastError();
 }
 
