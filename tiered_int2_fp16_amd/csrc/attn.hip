@@ -846,9 +846,6 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   const int G = pv.G, Hkv = pv.Hkv, Hq = pv.Hq, S = a.splits, W = pv.W, maxw = pv.maxw;
   const int TPW = W / 32, seg = a.layer * pv.B + b;
   const int32_t* info = a.app_info + 8 * b;
-  const int app = info[0], slot = info[1], row = info[2], newwin = info[3], len_old = info[4];
-  const int len = len_old + (app ? 1 : 0);
-  const int n_old = windows_of(len_old, W), n_win = windows_of(len, W);
   const int c32 = tid & 31, r8 = tid >> 5;   // (split lane, row of 32 threads)
 
   if (x < Hkv * NO) {
@@ -909,8 +906,11 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       *reinterpret_cast<float4*>(a.out + (size_t(b) * Hq + size_t(kvh) * G + h) * D + d) =
           make_float4(t4.x * iz, t4.y * iz, t4.z * iz, t4.w * iz);
     }
+    const int app = info[0], slot = info[1], row = info[2], newwin = info[3], len_old = info[4];
     if (app && sl == 0) {
       // the appended token joins its window (no kernel of this step reads it)
+      const int len = len_old + 1;
+      const int n_old = windows_of(len_old, W);
       uint16_t* dst = pv.block(seg, slot, kvh);
       for (int dd = tid; dd < D; dd += 256) {
         dst[layout::bf16_window_k(row, dd, D)] = a.k_new[(size_t(b) * Hkv + kvh) * D + dd];
@@ -927,7 +927,7 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   // ---------------------------------------------------------- window masses
   if (!a.mass && !acc_scores) return;
   const int w0 = (x - Hkv * NO) * kMassWindows;
-  if (w0 >= n_win) return;
+  if (w0 >= maxw) return;
   float* s_M = s_dynf;             // [Hq]
   float* s_Zh = s_dynf + Hq;       // [Hq] 1 / normaliser
   float* s_mv = s_dynf + 2 * Hq;   // [kMassWindows][Hq]
@@ -937,6 +937,7 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   // contiguous
   constexpr int kPairs = 4, kTiles = 8;   // pairs per batch; tiles per window at most
   const int npairs = Hq * kMassWindows;
+  const int bpairs = min(kPairs, (npairs + 255) / 256);   // pairs of a thread in one batch
   const auto rtm = tile_rsrc(a.tile_mass + size_t(b) * maxw * TPW * Hq, maxw * TPW * Hq * 8);
   const auto rml = tile_rsrc(a.ml + size_t(b) * Hq * S, Hq * S * 8);
   const auto rpg = tile_rsrc(pv.pages + size_t(seg) * maxw, maxw * 4);
@@ -944,17 +945,27 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   auto tile_masses = [&](int p0, float2 (&t)[kPairs][kTiles]) {
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
+      if (i >= bpairs) break;   // uniform: no load instruction for pairs the block does not have
       const int pi = p0 + tid + 256 * i, h = pi % Hq, w = w0 + pi / Hq;
 #pragma unroll
-      for (int k = 0; k < kTiles; ++k)
-        t[i][k] = as_f2(load8(rtm, boff(pi < npairs && w < maxw && k < TPW, ((w * TPW + k) * Hq + h) * 8)));
+      for (int k = 0; k < kTiles; ++k) {
+        if (k >= TPW) break;    // uniform: only the tiles a window has
+        t[i][k] = as_f2(load8(rtm, boff(pi < npairs && w < maxw, ((w * TPW + k) * Hq + h) * 8)));
+      }
     }
   };
   // loads of the first batch in flight together: tile masses, the page entries
   // and scores of the block's windows, the appended token's records and the
   // (m, l) pairs of the per-head reductions
+  // the step's append info as vector loads, issued first (the records do not
+  // depend on it)
+  const auto rinfo = tile_rsrc(info, 5 * 4);
+  const uint32_t i0 = load4(rinfo, 0), i4 = load4(rinfo, 16);
   float2 t1[kPairs][kTiles];
   tile_masses(0, t1);
+  const int app = uniform(int(i0)), len_old = uniform(int(i4));
+  const int len = len_old + (app ? 1 : 0);
+  const int n_old = windows_of(len_old, W), n_win = windows_of(len, W);
   const int wt = w0 + tid;   // thread tid < kMassWindows: its window's page entry and score
   const bool tin = tid < kMassWindows && wt < n_win;
   const uint32_t pe = load4(rpg, boff(tin && wt < n_old, wt * 4));
@@ -1010,8 +1021,10 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       const float M = s_M[h];
       float acc = 0.f;
 #pragma unroll
-      for (int k = 0; k < kTiles; ++k)
+      for (int k = 0; k < kTiles; ++k) {
+        if (k >= TPW) break;
         if (k < vt) acc += t[i][k].x * fast_exp2(t[i][k].y - M);
+      }
       if (w0 + wl == vwin) acc += s_app[h].x * fast_exp2(s_app[h].y - M);
       s_mv[wl * Hq + h] = lw ? acc * s_Zh[h] : 0.f;
     }
