@@ -1,8 +1,8 @@
 """Benchmark of the tiered decode path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Workload: the Llama-3.1-8B attention shape at 32K context (batch 1, 32 query /
+Workload (default): the Llama-3.1-8B attention shape at 32K context (batch 1, 32 query /
 8 kv heads, head_dim 128, windows of 128 tokens, 20 % byte budget with 10 % of
 windows in bf16: 25 bf16 / 139 INT2 / 92 evicted windows), synthetic seeded
 data.  One step = one decode step over the tiered cache (kv_decode_step: the
@@ -10,6 +10,13 @@ attention kernel and its combine kernel, which writes the per-window mass and
 adds it to the cumulative scores), and every 16th step of a pool a routing
 event (router, demotions into the write-once ledger, promotions).  Steps rotate over enough pool replicas (each its own arena) that
 every step reads its windows from HBM, not from the 256 MB Infinity Cache.
+
+`--workload llama8b_128k_loop` runs the same measurement on the 128K decode
+loop shape instead (batch 4, 131072 cached tokens, 102 bf16 / 548 INT2 / 374
+evicted windows per sequence, every step appending a token, routing every 16
+steps of a replica; contexts drawn on the device).  Its bytes per step are
+counted at the starting tier counts; the windows that appends open only add to
+them.  The oracle baseline is timed on the default workload only.
 
 The timed region replays a HIP graph of exactly K steps between two device
 synchronisations.  The attention kernel's own duration is then taken over the
@@ -31,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 import numpy as np  # noqa: E402
 
-from workload import CONFIGS, kv_history, query, score_prior  # noqa: E402
+from workload import CONFIGS, kv_history, kv_history_device, new_kv, query, score_prior  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 ROUTE_EVERY = 16
@@ -116,7 +123,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--replicas", type=int, default=24)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="pool replicas the steps rotate over (default: 24 at 32K, 2 at 128K)")
+    ap.add_argument("--workload", choices=("llama8b_32k", "llama8b_128k_loop"), default="llama8b_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -140,39 +149,58 @@ def main():
         return
     from tiered_int2_fp16_amd import binding as B
 
-    c = CONFIGS["llama8b_32k"]
+    c = CONFIGS[args.workload]
+    loop = c.append
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     n = c.n_windows
-    R = max(1, args.replicas)
+    R = max(1, args.replicas or (2 if loop else 24))
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
-    k, v = kv_history(c, 0, 0)
-    prior = score_prior(c, 0, 0)
-    K = torch.from_numpy(k.view(np.int16)[None]).to(dev)
-    V = torch.from_numpy(v.view(np.int16)[None]).to(dev)
-    P = torch.from_numpy(prior[None]).to(dev)
+    if loop:
+        # device-drawn contexts; room for the windows that the appends of every
+        # pass below open (warm-up, timed region, its six replays, event pass)
+        K = torch.empty((c.batch, c.kv_heads, c.context, c.head_dim), dtype=torch.int16, device=dev)
+        V = torch.empty_like(K)
+        for b in range(c.batch):
+            K[b], V[b] = kv_history_device(c, 0, b, dev)
+        P = torch.from_numpy(np.stack([score_prior(c, 0, b) for b in range(c.batch)])).to(dev)
+        appended = -(-(args.warmup + 8 * args.steps) // R)
+        maxw = -(-(c.context + appended) // c.window) + 1
+    else:
+        k, v = kv_history(c, 0, 0)
+        K = torch.from_numpy(k.view(np.int16)[None]).to(dev)
+        V = torch.from_numpy(v.view(np.int16)[None]).to(dev)
+        P = torch.from_numpy(score_prior(c, 0, 0)[None]).to(dev)
+        maxw = n
     nq = 16
     Q = [torch.from_numpy(query(c, 0, s).view(np.int16)).to(dev) for s in range(nq)]
-    cfg = B.make_config(c.batch, c.layers, c.q_heads, c.kv_heads, c.head_dim, c.window, n,
-                        c.n_recent, n, n)
+    KN, VN = [], []
+    if loop:
+        for s in range(nq):
+            kn, vn = new_kv(c, 0, s)
+            KN.append(torch.from_numpy(kn.view(np.int16)).to(dev))
+            VN.append(torch.from_numpy(vn.view(np.int16)).to(dev))
+    cfg = B.make_config(c.batch, c.layers, c.q_heads, c.kv_heads, c.head_dim, c.window, maxw,
+                        c.n_recent, maxw, maxw)
     pools, outs, masses, trs, cnts = [], [], [], [], []
     for r in range(R):
         p = B.Pool(cfg, dev)
         p.prefill(0, K, V, c.context, P)
-        tr = torch.zeros(3, c.batch, n, dtype=torch.int32, device=dev)
+        tr = torch.zeros(3, c.batch, maxw, dtype=torch.int32, device=dev)
         cn = torch.zeros(4, c.batch, dtype=torch.int32, device=dev)
         p.score_route(0, None, 1, c.budget_frac, c.hi_frac, tr, cn)
         p.apply_route(0, tr, cn)
         pools.append(p)
         outs.append(torch.empty(c.batch, c.q_heads, c.head_dim, dtype=torch.float32, device=dev))
-        masses.append(torch.zeros(c.batch, c.q_heads, n, dtype=torch.float32, device=dev))
+        masses.append(torch.zeros(c.batch, c.q_heads, maxw, dtype=torch.float32, device=dev))
         trs.append(tr)
         cnts.append(cn)
     del K, V
     torch.cuda.synchronize()
-    pages = pools[0].pages(0)[0].cpu().numpy() & 3
-    n_f, n_q = int((pages == 2).sum()), int((pages == 1).sum())
+    pages = pools[0].pages(0).cpu().numpy() & 3
+    n_f, n_q = int((pages[0] == 2).sum()), int((pages[0] == 1).sum())
+    assert all(int((pg == 2).sum()) == n_f and int((pg == 1).sum()) == n_q for pg in pages)
     assert all(p.check() == 0 for p in pools)
     log(f"{R} replicas ready: {n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows")
     local = [0] * R
@@ -181,7 +209,10 @@ def main():
     def step(i, record=None):
         r = i % R
         p = pools[r]
-        p.attn(0, Q[i % nq], out=outs[r], mass=masses[r], scores=True)   # kv_decode_step
+        if loop:   # kv_decode_step with the step's new token
+            p.attn(0, Q[i % nq], KN[i % nq], VN[i % nq], out=outs[r], mass=masses[r], scores=True)
+        else:      # kv_decode_step
+            p.attn(0, Q[i % nq], out=outs[r], mass=masses[r], scores=True)
         do_route = (local[r] % ROUTE_EVERY) == ROUTE_EVERY - 1
         if do_route:
             p.score_route(0, None, 1, c.budget_frac, c.hi_frac, trs[r], cnts[r])
@@ -278,8 +309,19 @@ def main():
     value = total_bytes / t_timed / 1e9
     achieved = per_attn / (attn_ms * 1e-3) / 1e9
     khash = kernel_source_hash()
+    if loop:
+        workload_name = (f"{c.name}: Llama-3.1-8B attention shape, 128K context, batch {c.batch}, "
+                         f"32 q / 8 kv heads, head_dim 128, window 128, every step appends a token, "
+                         f"20% byte budget ({n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows "
+                         f"per sequence at the start), route every 16 steps")
+    else:
+        workload_name = ("llama8b_32k: Llama-3.1-8B attention shape, 32K context, one decode "
+                         "step per pool, batch 1, 32 q / 8 kv heads, head_dim 128, window 128, "
+                         "20% byte budget (25 bf16 / 139 INT2 / 92 evicted windows), route "
+                         "every 16 steps")
     result = {
-        "metric": "tiered decode-attn effective HBM GB/s (% of peak) + decode steps/s at 32K ctx",
+        "metric": "tiered decode-attn effective HBM GB/s (% of peak) + decode steps/s at "
+                  + ("128K ctx" if loop else "32K ctx"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -291,10 +333,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16+int2",
         "data": "synthetic",
-        "config": {"workload": "llama8b_32k: Llama-3.1-8B attention shape, 32K context, one decode "
-                               "step per pool, batch 1, 32 q / 8 kv heads, head_dim 128, window 128, "
-                               "20% byte budget (25 bf16 / 139 INT2 / 92 evicted windows), route "
-                               "every 16 steps",
+        "config": {"workload": workload_name,
                    "global_batch": c.batch, "seq_len": c.context, "parallelism": "none (1 GPU)",
                    "replicas": R, "timed_region": "HIP graph replay of exactly K steps"},
         "decode_steps_per_s": round(K_steps / t_timed, 1),
@@ -302,11 +341,11 @@ def main():
         "attn_kernel_us": round(attn_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(khash)},
+                     "traffic": None if loop else measured_traffic(khash)},
         "kernel_source_hash": khash,
         "mass_emission": mass_emission,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not loop:
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

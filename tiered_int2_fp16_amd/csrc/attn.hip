@@ -233,6 +233,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   constexpr int NB = D / 16;   // 16-channel blocks of the PV product (= code chunks per part)
   constexpr int CW = D / 32;   // 32-bit code words per lane per part
   constexpr int kList = 64;    // tile entries a wave lists at a time
+  constexpr int kMixedList = 8;   // INT2 tiles from which a wave takes both tiers in one loop
   extern __shared__ uint32_t s_dyn[];    // plan (page entries, tile prefixes), slot bitmap
   __shared__ float s_wm[kAttnWaves][kGMax], s_wl[kAttnWaves][kGMax];
   __shared__ float s_wo[kAttnWaves][kGMax][D];
@@ -440,13 +441,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   // the raw masses of a listed chunk of nt tiles go out after the chunk: no
   // global store inside the tile loops, where it would hold up the next
   // tile's loads
-  auto flush_masses = [&](int nt, const uint32_t* list) {
+  auto flush_masses = [&](int nt, const uint32_t* list, bool from_top = false) {
     if (!want_mass) return;
     __builtin_amdgcn_wave_barrier();
     for (int idx = lane; idx < nt * G; idx += 64) {
       const int h = idx / nt, t = idx - h * nt;
       const uint32_t e = list[t];
-      tmass[(size_t(te_win(e)) * TPW + te_tile(e)) * pv.Hq + h] = rec[t][h];
+      tmass[(size_t(te_win(e)) * TPW + te_tile(e)) * pv.Hq + h] = rec[from_top ? kList - 1 - t : t][h];
     }
     __builtin_amdgcn_wave_barrier();
   };
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
 #pragma unroll
     for (int c = 0; c < NB; ++c) fb.v[c] = load16(rs, 32 * D * 2 + (c * 64 + lane) * 16);
   };
-  auto compute_f = [&](FB& fb, int t) {
+  auto compute_f = [&](FB& fb, int t) {   // record row t
     const uint32_t e = uniform(int(listf[t]));
     const int w = te_win(e), k = te_tile(e);
     const int valid = min(32, len_old - w * W - 32 * k);
@@ -587,7 +588,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     load_words(rs, LT.ks, qq.sc);
   };
   uint8_t* scb = s_scb[wid];
-  auto compute_q = [&](QB& qq, int t) {
+  auto compute_q = [&](QB& qq, int t, int rt) {   // record row rt
     // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer
     if constexpr (CW == 4)
       reinterpret_cast<uint4*>(scb)[lane] = make_uint4(qq.sc[0], qq.sc[1], qq.sc[2], qq.sc[3]);
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
         st.o[nb] = mfma_f16(av, pl, st.o[nb]);
       }
     }
-    if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
+    if (rec_mass) rec[rt][hn] = make_float2(rs, st.m_run);
   };
 
   if (f_beg < f_end) build_list(TIER_F, f_beg, min(f_end, f_beg + kList), listf);
@@ -695,12 +696,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       // the loop, where the compiler can count the loads in flight exactly
       // (every load here is unconditional); the loop's own count would make
       // its first wait include the bf16 tile.
-      if (nt > 0) compute_q(A, 0);
+      if (nt > 0) compute_q(A, 0, 0);
       load_q(A, 2, nt);
       __builtin_amdgcn_sched_barrier(0);
       load_f(FA, 0, min(f_end, f_beg + kList) - f_beg);
       __builtin_amdgcn_sched_barrier(0);
-      if (nt > 1) compute_q(Bq, 1);
+      if (nt > 1) compute_q(Bq, 1, 1);
       load_q(Bq, 3, nt);
       __builtin_amdgcn_sched_barrier(0);
       i0 = 2;
@@ -708,11 +709,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     __builtin_amdgcn_sched_barrier(0);
     while (nt > 0) {
       for (int i = i0; i < nt; i += 2) {
-        compute_q(A, i);
+        compute_q(A, i, i);
         if (i + 1 >= nt) break;
         load_q(A, i + 2, nt);
         __builtin_amdgcn_sched_barrier(0);
-        compute_q(Bq, i + 1);
+        compute_q(Bq, i + 1, i + 1);
         load_q(Bq, i + 3, nt);   // (empty past the end: one path back to the loop head)
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -729,22 +730,75 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       }
     }
   };
-  if (f_beg < f_end)
-    int2_tiles(std::true_type{});
-  else
-    int2_tiles(std::false_type{});
+  // Both tiers in one loop: a wave with a long INT2 list and some bf16 tiles
+  // takes one bf16 tile after every four INT2 tiles, so that the bf16 bytes
+  // stream in while INT2 tiles are decoded (an INT2 tile costs far more
+  // instructions per byte than a bf16 tile).  Two INT2 tiles and one bf16
+  // tile are in flight; every load is unconditional (empty resources past the
+  // ends), so each tile waits only for its own loads.  INT2 tiles record
+  // their masses from the top rows of the record block, bf16 tiles from the
+  // bottom (both lists fit one chunk).
+  int f_done = 0;   // bf16 tiles of the first chunk taken in the mixed loop
+  auto mixed_tiles = [&]() {
+    const int nq = q_end - q_beg, nf = f_end - f_beg;
+    QB A, Bq;
+    load_q(A, 0, nq);
+    __builtin_amdgcn_sched_barrier(0);
+    load_q(Bq, 1, nq);
+    __builtin_amdgcn_sched_barrier(0);
+    load_f(FA, 0, nf);
+    __builtin_amdgcn_sched_barrier(0);
+    // whole groups of four (the tiles past the end load nothing and are not
+    // computed): the loop has no early exit, so every path into its head has
+    // the same loads in flight in the same order
+    int jf = 0;
+    for (int i = 0; i < nq; i += 4) {
+      compute_q(A, i, kList - 1 - i);
+      load_q(A, i + 2, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < nq) compute_q(Bq, i + 1, kList - 2 - i);
+      load_q(Bq, i + 3, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < nq) compute_q(A, i + 2, kList - 3 - i);
+      load_q(A, i + 4, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 3 < nq) compute_q(Bq, i + 3, kList - 4 - i);
+      load_q(Bq, i + 5, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (jf < nf) compute_f(FA, jf);
+      ++jf;
+      load_f(FA, jf, nf);   // (empty past the end)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    drain_loads();   // FA (the next bf16 tile, if any) is in; nothing else pending
+    flush_masses(nq, listq, true);
+    f_done = min(jf, nf);
+  };
+  // (head groups of more than four need the registers of their wider B
+  // operands: they keep the tiers apart)
+  bool mixed = false;
+  if constexpr (GP == 4) {
+    const int nq_all = q_end - q_beg, nf_all = f_end - f_beg;
+    mixed = nq_all >= kMixedList && nq_all + nf_all <= kList;
+    if (mixed) mixed_tiles();
+  }
+  if (!mixed) {
+    if (f_beg < f_end)
+      int2_tiles(std::true_type{});
+    else
+      int2_tiles(std::false_type{});
+  }
 
   // ---------------------------------------------------------- bf16 tiles
   for (int cb = f_beg; cb < f_end; cb += kList) {
     const int ce = min(f_end, cb + kList), nt = ce - cb;
-    if (cb != f_beg) {
-      build_list(TIER_F, cb, ce, listf);
-      load_f(FA, 0, nt);
-    }
+    const int i0 = cb == f_beg ? f_done : 0;   // FA holds tile i0 after the mixed loop
+    if (cb != f_beg) build_list(TIER_F, cb, ce, listf);
+    if (cb != f_beg) load_f(FA, 0, nt);   // (else requested among the INT2 tiles)
     FB Bf;
-    load_f(Bf, 1, nt);
+    load_f(Bf, i0 + 1, nt);
     __builtin_amdgcn_sched_barrier(0);
-    for (int i = 0; i < nt; i += 2) {
+    for (int i = i0; i < nt; i += 2) {
       compute_f(FA, i);
       if (i + 1 >= nt) break;
       load_f(FA, i + 2, nt);
