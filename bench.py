@@ -302,6 +302,25 @@ def main():
                      "without_mass_us": round((mass_us[1] + mass_us[3]) / 2, 3)}
     mass_emission["overhead_us"] = round(mass_emission["with_mass_us"] - mass_emission["without_mass_us"], 3)
 
+    # ------------------------------------------------ routing diagnostics
+    # kv_route_diagnostics after a routing event (counts) with a step's window
+    # masses standing in for the shadow cache's: churn, Global LIR and future
+    # missed mass of every sequence, graph-replayed.
+    diag = torch.zeros(c.batch, 5, dtype=torch.float32, device=dev)
+    gd = torch.cuda.CUDAGraph()
+    sd = torch.cuda.Stream(device=dev)
+    sd.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(sd):
+        with torch.cuda.graph(gd, stream=sd):
+            for i in range(n_me):
+                pools[i % R].diagnostics(0, diag, counts=cnts[i % R], shadow_mass=masses[i % R])
+    torch.cuda.synchronize()
+    diag_us = replay_us(gd, n_me)
+    del gd
+    diag_bytes = c.batch * (maxw * 4 + c.q_heads * n * 4 + 5 * 4 + 3 * 4)
+    diagnostics = {"calls": n_me, "us_per_call": round(diag_us, 3),
+                   "bytes_per_call": diag_bytes, "gbs": round(diag_bytes / (diag_us * 1e-6) / 1e9, 2)}
+
     per_attn = attn_bytes(c, n_f, n_q, n)
     total_bytes = K_steps * (per_attn + score_bytes(c, n)) + \
         len(routed) * route_bytes(c, n, 0, 0) + route_bytes(c, 0, fq, pr)
@@ -344,6 +363,7 @@ def main():
                      "traffic": None if loop else measured_traffic(khash)},
         "kernel_source_hash": khash,
         "mass_emission": mass_emission,
+        "route_diagnostics": diagnostics,
     }
     if not args.no_cpu_baseline and not loop:
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)

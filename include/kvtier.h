@@ -216,6 +216,28 @@ kv_status kv_score_route(kv_pool* pool, int32_t layer, const float* mass, int32_
                          double budget_frac, double hi_frac,
                          int32_t* transitions, int32_t* counts, void* stream);
 
+/* Routing diagnostics of `layer` ("Technische Samenvatting: QEvict", "Kernbijdragen"
+ * item 1: future missed mass, Global LIR, selection churn), one row per sequence of
+ *   diag   float [batch][5], caller-owned and zeroed before the first call; [1] and [2]
+ *          accumulate over calls.
+ *   counts int32 [4][batch] of the routing event just taken by kv_score_route (its
+ *          evictions are in the page table), or NULL:
+ *            diag[0] = selection churn = (demotions + promotions + evictions) / windows
+ *                      live before the event (live now + evictions), 0 with none live;
+ *            diag[1] += promotions (windows back in bf16);
+ *            diag[2] += demotions (windows that left bf16);
+ *            diag[3] = Global LIR = diag[1] / diag[2], 0 while diag[2] is 0.
+ *   shadow_mass float [batch][q_heads][max_windows]: the window masses of one decode step
+ *          of a cache holding every window in bf16 (another pool routed at a full
+ *          budget, fed the same tokens), or NULL:
+ *            diag[4] = future missed mass = (1 / q_heads) * sum over heads and over the
+ *                      windows this pool has evicted of shadow_mass.
+ *          Call it with this pool in the state that step ran with.
+ * Ratios are IEEE float32 quotients of the integer counts.  KV_EINVAL if diag is NULL
+ * or both counts and shadow_mass are. */
+kv_status kv_route_diagnostics(kv_pool* pool, int32_t layer, const int32_t* counts,
+                               const float* shadow_mass, float* diag, void* stream);
+
 /* Copy window `window` of sequence b, layer l, in the canonical layouts:
  * kv_read_ledger writes kv_heads ledger entries of 3*W*D/4 bytes to dst, each
  * Kc [W][D/4], Vc [W][D/4] (code of (t, d) in byte d/4, bits 2*(d%4)), Ks, Km

@@ -20,9 +20,10 @@ Modules
   router    tier counts from the byte budget and the score-ranked router
   pool      the per-segment ledger/tier state machine (demote, promote, evict,
             append, score update, routing)
+  diagnostics  selection churn, Global LIR and future missed mass of a run
 
 Every function is pinned by tests under tests/ (marked "not gpu") against
 closed forms, library routines, brute force and hand-derived examples; none is
 "parity unpinned".
 """
-from . import attention, codec, pool, router  # noqa: F401
+from . import attention, codec, diagnostics, pool, router  # noqa: F401

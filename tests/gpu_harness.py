@@ -87,6 +87,7 @@ class Pair:
     # ---------------------------------------------------------- routing ---
     def route(self, layer, beta, phi):
         tr, cnt = self.pool.score_route(layer, None, 1, beta, phi)
+        self.last_counts = cnt   # device counts of this event
         s_gpu = self.pool.scores(layer).cpu().numpy().copy()
         self.pool.apply_route(layer, tr, cnt)
         tr_h, cnt_h = tr.cpu().numpy(), cnt.cpu().numpy()

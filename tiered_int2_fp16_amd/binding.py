@@ -28,7 +28,7 @@ EXPORTS = [
     "kv_pool_region", "kv_prefill", "kv_demote_quantize", "kv_promote_dequantize",
     "kv_attn_workspace_bytes", "kv_tiered_decode_attn", "kv_score_route", "kv_read_ledger",
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
-    "kv_attn_profile", "kv_attn_timings", "kv_decode_step",
+    "kv_attn_profile", "kv_attn_timings", "kv_decode_step", "kv_route_diagnostics",
 ]
 
 
@@ -66,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "kv_tiered_decode_attn": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_score_route": (I32, [P, I32, P, I32, D, D, P, P, P]),
+        "kv_route_diagnostics": (I32, [P, I32, P, P, P, P]),
         "kv_read_ledger": (I32, [P, I32, I32, I32, P, P]),
         "kv_read_window": (I32, [P, I32, I32, I32, P, P]),
         "kv_tier_counts": (I32, [I32, I32, D, D, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
@@ -174,6 +175,10 @@ def kv_score_route(h, layer, mass, do_route, budget_frac, hi_frac, transitions=N
                    stream=None):
     _ck(LIB.kv_score_route(h, layer, _ptr(mass), int(do_route), float(budget_frac), float(hi_frac),
                            _ptr(transitions), _ptr(counts), _stream(stream)))
+
+
+def kv_route_diagnostics(h, layer, counts, shadow_mass, diag, stream=None):
+    _ck(LIB.kv_route_diagnostics(h, layer, _ptr(counts), _ptr(shadow_mass), _ptr(diag), _stream(stream)))
 
 
 def kv_read_ledger(h, layer, b, window, dst, stream=None):
@@ -311,6 +316,16 @@ class Pool:
         """Demotions then promotions of a routing event, straight from device lists."""
         self.demote(layer, transitions[0], counts[0])
         self.promote(layer, transitions[1], counts[1])
+
+    def diagnostics(self, layer, diag, counts=None, shadow_mass=None):
+        """kv_route_diagnostics into diag float [batch][5] (churn, promotions,
+        demotions, Global LIR, future missed mass)."""
+        c = self.cfg
+        self._need(diag, (c.batch, 5), (torch.float32,), "diag")
+        self._need(counts, (4, c.batch), (torch.int32,), "counts")
+        self._need(shadow_mass, (c.batch, c.q_heads, c.max_windows), (torch.float32,), "shadow_mass")
+        kv_route_diagnostics(self.h, layer, counts, shadow_mass, diag)
+        return diag
 
     def read_ledger(self, layer, b, w) -> torch.Tensor:
         dst = torch.empty(self.cfg.kv_heads, self.entry_bytes, dtype=torch.uint8, device=self.device)

@@ -314,6 +314,18 @@ kv_status kv_score_route(kv_pool* pool, int32_t layer, const float* mass, int32_
   return e == hipSuccess ? KV_OK : hip_fail(e, "score/route launch");
 }
 
+kv_status kv_route_diagnostics(kv_pool* pool, int32_t layer, const int32_t* counts,
+                               const float* shadow_mass, float* diag, void* stream) {
+  kv_status st = check_pool_layer(pool, layer);
+  if (st) return st;
+  if (!diag) return fail(KV_EINVAL, "diag must not be NULL");
+  if (!counts && !shadow_mass) return fail(KV_EINVAL, "give counts, shadow_mass or both");
+  if ((st = set_device(pool))) return st;
+  hipError_t e = launch_route_diagnostics(view(pool), layer, counts, shadow_mass, diag,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV_OK : hip_fail(e, "diagnostics launch");
+}
+
 kv_status kv_read_ledger(kv_pool* pool, int32_t layer, int32_t b, int32_t window, void* dst,
                          void* stream) {
   kv_status st = check_pool_layer(pool, layer);

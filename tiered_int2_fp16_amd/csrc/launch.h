@@ -37,6 +37,8 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const PoolView& pv, const AttnArgs& a, hipStream_t s);
 
+hipError_t launch_route_diagnostics(const PoolView& pv, int layer, const int32_t* counts,
+                                    const float* shadow_mass, float* diag, hipStream_t s);
 hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, int do_route,
                               double budget_frac, double hi_frac, int32_t* transitions,
                               int32_t* counts, hipStream_t s);

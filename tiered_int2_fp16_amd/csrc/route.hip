@@ -199,6 +199,65 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
     if (pe_tier(pages[w]) != TIER_E && newt[w] == TIER_E) gp[w] = 0u;
 }
 
+// Routing diagnostics of the QEvict summary ("Kernbijdragen", item 1): selection
+// churn and Global LIR from the counts of a routing event, future missed mass
+// from the window masses of a shadow cache that keeps every window in bf16.
+// One block per sequence; diag float [batch][5] (see kv_route_diagnostics).
+__global__ __launch_bounds__(256) void diag_kernel(PoolView pv, int layer, const int32_t* counts,
+                                                   const float* shadow_mass, float* diag) {
+  __shared__ float s_miss[4];
+  __shared__ int s_live[4];
+  const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const uint32_t* pages = pv.pages + size_t(seg) * pv.maxw;
+  // every load is independent of the token count and the page entries (the
+  // window bound and the evicted test only select), so all go out at once
+  const int tokens = pv.tokens[seg];
+  int live = 0;
+  float miss = 0.f;
+  for (int w = tid; w < pv.maxw; w += 256) {
+    const uint32_t e = pages[w];
+    float acc = 0.f;
+    if (shadow_mass) {
+      const float* m = shadow_mass + size_t(b) * pv.Hq * pv.maxw + w;
+#pragma unroll 8
+      for (int h = 0; h < pv.Hq; ++h) acc += m[size_t(h) * pv.maxw];
+    }
+    const bool in = w < windows_of(tokens, pv.W);
+    const bool ev = in && pe_tier(e) == TIER_E;
+    live += (in && !ev) ? 1 : 0;
+    if (ev) miss += acc;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    live += __shfl_xor(live, off, 64);
+    miss += __shfl_xor(miss, off, 64);
+  }
+  if (lane == 0) {
+    s_live[wid] = live;
+    s_miss[wid] = miss;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  const int live_now = s_live[0] + s_live[1] + s_live[2] + s_live[3];
+  float* d = diag + size_t(b) * 5;
+  if (counts) {
+    const int dem = counts[b], pro = counts[pv.B + b], evi = counts[2 * pv.B + b];
+    const int before = live_now + evi;
+    d[0] = before > 0 ? __fdiv_rn(float(dem + pro + evi), float(before)) : 0.f;
+    d[1] += float(pro);
+    d[2] += float(dem);
+    d[3] = d[2] > 0.f ? __fdiv_rn(d[1], d[2]) : 0.f;
+  }
+  if (shadow_mass) d[4] = ((s_miss[0] + s_miss[1]) + (s_miss[2] + s_miss[3])) / float(pv.Hq);
+}
+
+hipError_t launch_route_diagnostics(const PoolView& pv, int layer, const int32_t* counts,
+                                    const float* shadow_mass, float* diag, hipStream_t s) {
+  hipLaunchKernelGGL(diag_kernel, dim3(pv.B), dim3(256), 0, s, pv, layer, counts, shadow_mass, diag);
+  return hipGetLastError();
+}
+
 hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, int do_route,
                               double beta, double phi, int32_t* transitions, int32_t* counts,
                               hipStream_t s) {
