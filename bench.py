@@ -11,8 +11,10 @@ adds it to the cumulative scores), and every 16th step of a pool a routing
 event (router, demotions into the write-once ledger, promotions).  Steps rotate over enough pool replicas (each its own arena) that
 every step reads its windows from HBM, not from the 256 MB Infinity Cache.
 
-`--workload llama8b_128k_loop` runs the same measurement on the 128K decode
-loop shape instead (batch 4, 131072 cached tokens, 102 bf16 / 548 INT2 / 374
+`--workload qwen7b_32k` runs it on the Qwen2.5-7B shape (batch 8, 28 query /
+4 kv heads, 5 bf16 / 41 INT2 / 210 evicted windows per sequence; contexts drawn
+on the device).  `--workload llama8b_128k_loop` runs the same measurement on
+the 128K decode loop shape instead (batch 4, 131072 cached tokens, 102 bf16 / 548 INT2 / 374
 evicted windows per sequence, every step appending a token, routing every 16
 steps of a replica; contexts drawn on the device).  Its bytes per step are
 counted at the starting tier counts; the windows that appends open only add to
@@ -125,7 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--replicas", type=int, default=0,
                     help="pool replicas the steps rotate over (default: 24 at 32K, 2 at 128K)")
-    ap.add_argument("--workload", choices=("llama8b_32k", "llama8b_128k_loop"), default="llama8b_32k")
+    ap.add_argument("--workload", choices=("llama8b_32k", "qwen7b_32k", "llama8b_128k_loop"),
+                    default="llama8b_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -157,16 +160,16 @@ def main():
     R = max(1, args.replicas or (2 if loop else 24))
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
-    if loop:
-        # device-drawn contexts; room for the windows that the appends of every
-        # pass below open (warm-up, timed region, its six replays, event pass)
+    if c.batch > 1:
+        # device-drawn contexts; with appends, room for the windows that every
+        # pass below opens (warm-up, timed region, its six replays, event pass)
         K = torch.empty((c.batch, c.kv_heads, c.context, c.head_dim), dtype=torch.int16, device=dev)
         V = torch.empty_like(K)
         for b in range(c.batch):
             K[b], V[b] = kv_history_device(c, 0, b, dev)
         P = torch.from_numpy(np.stack([score_prior(c, 0, b) for b in range(c.batch)])).to(dev)
-        appended = -(-(args.warmup + 8 * args.steps) // R)
-        maxw = -(-(c.context + appended) // c.window) + 1
+        appended = -(-(args.warmup + 8 * args.steps) // R) if loop else 0
+        maxw = -(-(c.context + appended) // c.window) + (1 if loop else 0)
     else:
         k, v = kv_history(c, 0, 0)
         K = torch.from_numpy(k.view(np.int16)[None]).to(dev)
@@ -333,6 +336,11 @@ def main():
                          f"32 q / 8 kv heads, head_dim 128, window 128, every step appends a token, "
                          f"20% byte budget ({n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows "
                          f"per sequence at the start), route every 16 steps")
+    elif c.name == "qwen7b_32k":
+        workload_name = (f"{c.name}: Qwen2.5-7B attention shape, 32K context, batch {c.batch}, "
+                         f"28 q / 4 kv heads, head_dim 128, window 128, 4 K outlier channels x10, "
+                         f"5% byte budget ({n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows "
+                         f"per sequence), route every 16 steps")
     else:
         workload_name = ("llama8b_32k: Llama-3.1-8B attention shape, 32K context, one decode "
                          "step per pool, batch 1, 32 q / 8 kv heads, head_dim 128, window 128, "
@@ -360,12 +368,12 @@ def main():
         "attn_kernel_us": round(attn_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if loop else measured_traffic(khash)},
+                     "traffic": measured_traffic(khash) if c.name == "llama8b_32k" else None},
         "kernel_source_hash": khash,
         "mass_emission": mass_emission,
         "route_diagnostics": diagnostics,
     }
-    if not args.no_cpu_baseline and not loop:
+    if not args.no_cpu_baseline and c.name == "llama8b_32k":
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
