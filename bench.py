@@ -199,6 +199,7 @@ def main():
         masses.append(torch.zeros(c.batch, c.q_heads, maxw, dtype=torch.float32, device=dev))
         trs.append(tr)
         cnts.append(cn)
+    K_keys = K if c.name == "llama8b_32k" else None   # for the prefill-score pass below
     del K, V
     torch.cuda.synchronize()
     pages = pools[0].pages(0).cpu().numpy() & 3
@@ -324,6 +325,34 @@ def main():
     diagnostics = {"calls": n_me, "us_per_call": round(diag_us, 3),
                    "bytes_per_call": diag_bytes, "gbs": round(diag_bytes / (diag_us * 1e-6) / 1e9, 2)}
 
+    # ------------------------------------- initial scores from the prefill
+    # kv_prefill_scores on the 32K context: causal attention of 32768 prefill
+    # queries (drawn on the device) over the context's keys, twice (row
+    # normalisers, then column sums), then window sums.  Algorithmic work:
+    # 2 passes x q_heads x T (T + 1) / 2 query-key pairs x D multiply-adds.
+    prefill = None
+    if K_keys is not None:
+        gq = torch.Generator(device=dev)
+        gq.manual_seed(int(np.random.SeedSequence([c.seed, 99]).generate_state(1, np.uint64)[0] >> 1))
+        qf = torch.randn((c.batch, c.q_heads, c.context, c.head_dim), generator=gq, device=dev)
+        qp = (qf.view(torch.int32) >> 16).to(torch.int16)
+        del qf
+        ws = pools[0].prefill_scores(0, qp, K_keys, c.context)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            pools[0].prefill_scores(0, qp, K_keys, c.context, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        pf_ms = e0.elapsed_time(e1) / reps
+        flops = 2.0 * c.q_heads * c.context * (c.context + 1) / 2 * c.head_dim * 2 * c.batch
+        prefill = {"tokens": c.context, "ms": round(pf_ms, 3), "tflops": round(flops / (pf_ms * 1e-3) / 1e12, 1),
+                   "bound": "mfma", "peak_tflops": 2500.0,
+                   "frac": round(flops / (pf_ms * 1e-3) / 1e12 / 2500.0, 4)}
+        del qp, ws, K_keys
+
     per_attn = attn_bytes(c, n_f, n_q, n)
     total_bytes = K_steps * (per_attn + score_bytes(c, n)) + \
         len(routed) * route_bytes(c, n, 0, 0) + route_bytes(c, 0, fq, pr)
@@ -373,6 +402,8 @@ def main():
         "mass_emission": mass_emission,
         "route_diagnostics": diagnostics,
     }
+    if prefill is not None:
+        result["prefill_scores"] = prefill
     if not args.no_cpu_baseline and c.name == "llama8b_32k":
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -126,6 +126,27 @@ kv_status kv_pool_destroy(kv_pool* pool);
 /* Byte offset and size of a region inside the arena. [host] */
 kv_status kv_pool_region(const kv_pool* pool, int32_t which, size_t* offset, size_t* bytes);
 
+/* Initial window scores from the prefill attention ("Technische Samenvatting: RDKV",
+ * 2.1: a token's weight is the attention it receives over all query positions,
+ * w_t = sum_tau a_{tau,t}; 2.2 phase 1: computed once after the prefill with the
+ * full cache), as QEvict's cumulative scores start ("Technische Samenvatting:
+ * QEvict", Kernmechanismen): S[w] = sum over query heads and over the window's
+ * tokens of w_t, for the ceil(tokens/W) windows of every sequence of `layer`.
+ *   q  bf16 [batch][q_heads][tokens][D]: the prefill queries of the layer;
+ *   k  bf16 [batch][kv_heads][tokens][D]: its keys (those given to kv_prefill);
+ *      causal attention, query head h reading kv head h / (q_heads / kv_heads),
+ *      logits q.k / sqrt(D).
+ *   workspace  caller-owned device memory of kv_prefill_scores_workspace_bytes:
+ *      float lse [batch][q_heads][tokens] (log2-sum-exp of each query row), then
+ *      float w [batch][q_heads][tokens] (the token weights of each head).
+ * Replaces the scores kv_prefill set; other state is untouched.  KV_EINVAL for
+ * NULL or unaligned pointers, tokens < 1, ceil(tokens/W) > max_windows or
+ * tokens*D*2 >= 2^31; KV_ENOMEM for a short workspace. */
+size_t kv_prefill_scores_workspace_bytes(const kv_pool* pool, int32_t tokens);
+kv_status kv_prefill_scores(kv_pool* pool, int32_t layer, const void* q, const void* k,
+                            int32_t tokens, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Load a prefilled context into `layer`: k, v bf16 [batch][kv_heads][tokens][D].
  * Every window of every sequence becomes a bf16 window (window w in bf16
  * slot w), tokens = `tokens`, scores = prior (float [batch][ceil(tokens/W)],

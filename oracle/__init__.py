@@ -21,9 +21,10 @@ Modules
   pool      the per-segment ledger/tier state machine (demote, promote, evict,
             append, score update, routing)
   diagnostics  selection churn, Global LIR and future missed mass of a run
+  prefill_scores  token weights of the causal prefill attention, window sums
 
 Every function is pinned by tests under tests/ (marked "not gpu") against
 closed forms, library routines, brute force and hand-derived examples; none is
 "parity unpinned".
 """
-from . import attention, codec, diagnostics, pool, router  # noqa: F401
+from . import attention, codec, diagnostics, pool, prefill_scores, router  # noqa: F401

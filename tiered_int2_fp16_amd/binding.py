@@ -29,6 +29,7 @@ EXPORTS = [
     "kv_attn_workspace_bytes", "kv_tiered_decode_attn", "kv_score_route", "kv_read_ledger",
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
     "kv_attn_profile", "kv_attn_timings", "kv_decode_step", "kv_route_diagnostics",
+    "kv_prefill_scores_workspace_bytes", "kv_prefill_scores",
 ]
 
 
@@ -67,6 +68,8 @@ def _load() -> ctypes.CDLL:
         "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_score_route": (I32, [P, I32, P, I32, D, D, P, P, P]),
         "kv_route_diagnostics": (I32, [P, I32, P, P, P, P]),
+        "kv_prefill_scores_workspace_bytes": (SZ, [P, I32]),
+        "kv_prefill_scores": (I32, [P, I32, P, P, I32, P, SZ, P]),
         "kv_read_ledger": (I32, [P, I32, I32, I32, P, P]),
         "kv_read_window": (I32, [P, I32, I32, I32, P, P]),
         "kv_tier_counts": (I32, [I32, I32, D, D, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
@@ -179,6 +182,11 @@ def kv_score_route(h, layer, mass, do_route, budget_frac, hi_frac, transitions=N
 
 def kv_route_diagnostics(h, layer, counts, shadow_mass, diag, stream=None):
     _ck(LIB.kv_route_diagnostics(h, layer, _ptr(counts), _ptr(shadow_mass), _ptr(diag), _stream(stream)))
+
+
+def kv_prefill_scores(h, layer, q, k, tokens, workspace, stream=None):
+    _ck(LIB.kv_prefill_scores(h, layer, _ptr(q), _ptr(k), int(tokens), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def kv_read_ledger(h, layer, b, window, dst, stream=None):
@@ -326,6 +334,18 @@ class Pool:
         self._need(shadow_mass, (c.batch, c.q_heads, c.max_windows), (torch.float32,), "shadow_mass")
         kv_route_diagnostics(self.h, layer, counts, shadow_mass, diag)
         return diag
+
+    def prefill_scores(self, layer, q, k, tokens, workspace=None):
+        """kv_prefill_scores: scores from the prefill attention; returns the
+        workspace (uint8) holding lse then the token weights."""
+        c = self.cfg
+        self._need(q, (c.batch, c.q_heads, tokens, c.head_dim), _BF16, "q")
+        self._need(k, (c.batch, c.kv_heads, tokens, c.head_dim), _BF16, "k")
+        if workspace is None:
+            workspace = torch.empty(LIB.kv_prefill_scores_workspace_bytes(self.h, int(tokens)),
+                                    dtype=torch.uint8, device=self.device)
+        kv_prefill_scores(self.h, layer, q, k, tokens, workspace)
+        return workspace
 
     def read_ledger(self, layer, b, w) -> torch.Tensor:
         dst = torch.empty(self.cfg.kv_heads, self.entry_bytes, dtype=torch.uint8, device=self.device)

@@ -20,7 +20,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(OUT_DIR, "libkvtier.so")
 
-SOURCES = ["api.hip", "attn.hip", "route.hip", "transitions.hip", "host_core.cpp"]
+SOURCES = ["api.hip", "attn.hip", "route.hip", "transitions.hip", "prefill_scores.hip", "host_core.cpp"]
 ARCH = os.environ.get("KVTIER_ARCH", "gfx950")
 
 

@@ -174,6 +174,36 @@ kv_status kv_prefill(kv_pool* pool, int32_t layer, const void* k, const void* v,
   return e == hipSuccess ? KV_OK : hip_fail(e, "prefill launch");
 }
 
+size_t kv_prefill_scores_workspace_bytes(const kv_pool* pool, int32_t tokens) {
+  if (!pool || tokens < 1) return 0;
+  return size_t(2) * 4 * size_t(pool->g.cfg.batch) * size_t(pool->g.cfg.q_heads) * size_t(tokens);
+}
+
+kv_status kv_prefill_scores(kv_pool* pool, int32_t layer, const void* q, const void* k, int32_t tokens,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  kv_status st = check_pool_layer(pool, layer);
+  if (st) return st;
+  const kv_pool_config& c = pool->g.cfg;
+  if (!q || !k || !workspace) return fail(KV_EINVAL, "q, k and workspace must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(workspace, 16))
+    return fail(KV_EINVAL, "q, k and workspace must be 16-byte aligned");
+  if (tokens < 1) return fail(KV_EINVAL, "tokens must be >= 1");
+  if ((tokens + c.window - 1) / c.window > c.max_windows) return fail(KV_EINVAL, "context exceeds max_windows");
+  if (int64_t(tokens) * c.head_dim * 2 >= (int64_t(1) << 31))
+    return fail(KV_EINVAL, "tokens * head_dim * 2 must stay below 2^31");
+  const size_t need = kv_prefill_scores_workspace_bytes(pool, tokens);
+  if (workspace_bytes < need)
+    return fail(KV_ENOMEM, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                               std::to_string(need));
+  if ((st = set_device(pool))) return st;
+  float* lse = static_cast<float*>(workspace);
+  float* wt = lse + size_t(c.batch) * c.q_heads * tokens;
+  hipError_t e = launch_prefill_scores(view(pool), layer, static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k), tokens, lse, wt,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV_OK : hip_fail(e, "prefill scores launch");
+}
+
 static kv_status transition(kv_pool* pool, int32_t layer, const int32_t* items, int32_t stride,
                             const int32_t* counts, void* stream, bool promote) {
   kv_status st = check_pool_layer(pool, layer);

@@ -37,6 +37,8 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const PoolView& pv, const AttnArgs& a, hipStream_t s);
 
+hipError_t launch_prefill_scores(const PoolView& pv, int layer, const uint16_t* q, const uint16_t* k,
+                                 int T, float* lse, float* wt, hipStream_t s);
 hipError_t launch_route_diagnostics(const PoolView& pv, int layer, const int32_t* counts,
                                     const float* shadow_mass, float* diag, hipStream_t s);
 hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, int do_route,

@@ -1,0 +1,223 @@
+// Initial window scores from the prefill attention, for gfx950.
+//
+// The RDKV summary ("Technische Samenvatting: RDKV", 2.1) weighs a cached token
+// by the attention it receives over all query positions, w_t = sum_tau
+// a_{tau,t}, computed once after the prefill with the full cache (2.2, phase
+// 1).  These weights seed QEvict's cumulative window scores ("Technische
+// Samenvatting: QEvict", Kernmechanismen): S[w] = sum over query heads and over
+// the window's tokens of w_t.  The prefill attention is causal; query head h
+// reads kv head h / G.
+//
+// Three kernels, all dense 16x16x32 bf16 MFMA tiles (lane l holds 8
+// consecutive values of operand row l%16 at column block l/16; a result lane
+// holds rows 4*(l/16)+i of column l%16):
+//   1. row pass: each wave takes 16 queries and walks the keys 0..q in chunks
+//      of 32, keeping per-lane running (max, sum) in the log2 domain, merged
+//      over the 16 lanes of a row at the end: lse[q] = max + log2(sum);
+//   2. column pass: each wave takes 16 keys and walks the queries t..T-1 in
+//      chunks of 32, adding exp2(s - lse[q]): w[t] per head;
+//   3. window sums: S[w] = sum over heads (in order) and the window's tokens
+//      (a fixed tree) of w.
+// The next chunk's operands are requested before the current chunk's math.
+#include "launch.h"
+
+namespace kvtier {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ inline bf16x8 load_row8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (max, sum) pairs in the log2 domain merged; an empty side (max -inf) adds nothing
+__device__ inline void merge_ms(float& m, float& l, float mo, float lo) {
+  const float M = fmaxf(m, mo);
+  if (M == -INFINITY) return;
+  l = (m == -INFINITY ? 0.f : l * exp2_hw(m - M)) + (mo == -INFINITY ? 0.f : lo * exp2_hw(mo - M));
+  m = M;
+}
+
+constexpr int kRows = 16;     // queries (pass 1) or keys (pass 2) per wave
+constexpr int kChunk = 32;    // keys (pass 1) or queries (pass 2) per step
+constexpr int kWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_lse_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k, int T, int Hq,
+                                                          int Hkv, float qscale, float* __restrict__ lse) {
+  constexpr int KK = D / 32;
+  const int b = blockIdx.z, h = blockIdx.y, kvh = h / (Hq / Hkv);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, g = lane >> 4, hn = lane & 15;
+  const int q0 = (blockIdx.x * kWaves + wid) * kRows;
+  if (q0 >= T) return;   // the whole wave
+  const auto qr = span_rsrc(q + (size_t(b) * Hq + h) * size_t(T) * D, T * D * 2);
+  const auto kr = span_rsrc(k + (size_t(b) * Hkv + kvh) * size_t(T) * D, T * D * 2);
+  bf16x8 qa[KK];   // query row q0 + hn (zeros past T), dims 32 kk + 8 g ..
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qa[kk] = load_row8(qr, ((q0 + hn) * D + 32 * kk + 8 * g) * 2);
+  float m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+  }
+  const int qlast = min(q0 + kRows, T) - 1;
+  // keys k0 + hn and k0 + 16 + hn (zeros past T; masked by causality)
+  bf16x8 ka[KK], kb[KK];
+  auto load_keys = [&](int k0) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      ka[kk] = load_row8(kr, ((k0 + hn) * D + 32 * kk + 8 * g) * 2);
+      kb[kk] = load_row8(kr, ((k0 + 16 + hn) * D + 32 * kk + 8 * g) * 2);
+    }
+  };
+  load_keys(0);
+  for (int k0 = 0; k0 <= qlast; k0 += kChunk) {
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      c0 = mfma_bf16(qa[kk], ka[kk], c0);
+      c1 = mfma_bf16(qa[kk], kb[kk], c1);
+    }
+    if (k0 + kChunk <= qlast) load_keys(k0 + kChunk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = q0 + 4 * g + i;
+      const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
+      const float s0 = v0 ? c0[i] * qscale : -INFINITY, s1 = v1 ? c1[i] * qscale : -INFINITY;
+      const float mn = fmaxf(m[i], fmaxf(s0, s1));
+      if (mn != -INFINITY) {
+        l[i] = (m[i] == -INFINITY ? 0.f : l[i] * exp2_hw(m[i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
+               (v1 ? exp2_hw(s1 - mn) : 0.f);
+        m[i] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const float mo = __shfl_xor(m[i], off, 64), lo = __shfl_xor(l[i], off, 64);
+      merge_ms(m[i], l[i], mo, lo);
+    }
+    const int row = q0 + 4 * g + i;
+    if (hn == 0 && row < T) lse[(size_t(b) * Hq + h) * T + row] = m[i] + __log2f(l[i]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k, int T, int Hq,
+                                                             int Hkv, float qscale,
+                                                             const float* __restrict__ lse,
+                                                             float* __restrict__ wt) {
+  constexpr int KK = D / 32;
+  const int b = blockIdx.z, h = blockIdx.y, kvh = h / (Hq / Hkv);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, g = lane >> 4, hn = lane & 15;
+  const int t0 = (blockIdx.x * kWaves + wid) * kRows;
+  if (t0 >= T) return;
+  const auto qr = span_rsrc(q + (size_t(b) * Hq + h) * size_t(T) * D, T * D * 2);
+  const auto kr = span_rsrc(k + (size_t(b) * Hkv + kvh) * size_t(T) * D, T * D * 2);
+  const auto lr = span_rsrc(lse + (size_t(b) * Hq + h) * T, T * 4);
+  bf16x8 ka[KK];   // key row t0 + hn
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) ka[kk] = load_row8(kr, ((t0 + hn) * D + 32 * kk + 8 * g) * 2);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // queries q0 + hn and q0 + 16 + hn (zeros and lse 0 past T; masked)
+  bf16x8 qa[KK], qb[KK];
+  float la, lb;
+  auto load_queries = [&](int q0) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qa[kk] = load_row8(qr, ((q0 + hn) * D + 32 * kk + 8 * g) * 2);
+      qb[kk] = load_row8(qr, ((q0 + 16 + hn) * D + 32 * kk + 8 * g) * 2);
+    }
+    la = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + hn) * 4, 0, 0));
+    lb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + 16 + hn) * 4, 0, 0));
+  };
+  const int qstart = t0 & ~(kChunk - 1);
+  load_queries(qstart);
+  for (int q0 = qstart; q0 < T; q0 += kChunk) {
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      c0 = mfma_bf16(ka[kk], qa[kk], c0);
+      c1 = mfma_bf16(ka[kk], qb[kk], c1);
+    }
+    const float l0 = la, l1 = lb;
+    if (q0 + kChunk < T) load_queries(q0 + kChunk);
+    const int qa_i = q0 + hn, qb_i = q0 + 16 + hn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = t0 + 4 * g + i;
+      if (qa_i >= key && qa_i < T) acc[i] += exp2_hw(fmaf(c0[i], qscale, -l0));
+      if (qb_i >= key && qb_i < T) acc[i] += exp2_hw(fmaf(c1[i], qscale, -l1));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = acc[i];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+    const int key = t0 + 4 * g + i;
+    if (hn == 0 && key < T) wt[(size_t(b) * Hq + h) * T + key] = x;
+  }
+}
+
+// S[w] of sequence b: the window's token weights of every head (heads in
+// order per token, then a fixed tree over the window's tokens).
+__global__ __launch_bounds__(256) void prefill_window_kernel(PoolView pv, int layer, int T,
+                                                             const float* __restrict__ wt) {
+  __shared__ float s_part[256];
+  const int w = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int seg = layer * pv.B + b;
+  float x = 0.f;
+  for (int t = tid; t < pv.W; t += 256) {
+    const int tok = w * pv.W + t;
+    if (tok < T) {
+      const float* p = wt + size_t(b) * pv.Hq * T + tok;
+      for (int h = 0; h < pv.Hq; ++h) x += p[size_t(h) * T];
+    }
+  }
+  s_part[tid] = x;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) s_part[tid] += s_part[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) pv.scores[size_t(seg) * pv.maxw + w] = s_part[0];
+}
+
+}  // namespace
+
+hipError_t launch_prefill_scores(const PoolView& pv, int layer, const uint16_t* q, const uint16_t* k,
+                                 int T, float* lse, float* wt, hipStream_t s) {
+  const float qscale = 1.4426950408889634f / sqrtf(float(pv.D));
+  const dim3 grid((T + kWaves * kRows - 1) / (kWaves * kRows), pv.Hq, pv.B);
+  if (pv.D == 128) {
+    hipLaunchKernelGGL((prefill_lse_kernel<128>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale, lse);
+    hipLaunchKernelGGL((prefill_colsum_kernel<128>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale,
+                       lse, wt);
+  } else {
+    hipLaunchKernelGGL((prefill_lse_kernel<64>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale, lse);
+    hipLaunchKernelGGL((prefill_colsum_kernel<64>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale,
+                       lse, wt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = (T + pv.W - 1) / pv.W;
+  hipLaunchKernelGGL(prefill_window_kernel, dim3(n, pv.B), dim3(256), 0, s, pv, layer, T, wt);
+  return hipGetLastError();
+}
+
+}  // namespace kvtier

@@ -11,6 +11,7 @@ from .synth import (  # noqa: F401
     kv_history,
     kv_history_device,
     new_kv,
+    prefill_queries,
     query,
     score_prior,
 )

@@ -19,7 +19,7 @@ from typing import Dict, Tuple
 import numpy as np
 
 # stream ids inside one config seed
-_T_SCORES, _T_Q, _T_K, _T_V, _T_OUTLIER, _T_STEP_Q, _T_STEP_K, _T_STEP_V, _T_DEVICE_KV = range(9)
+_T_SCORES, _T_Q, _T_K, _T_V, _T_OUTLIER, _T_STEP_Q, _T_STEP_K, _T_STEP_V, _T_DEVICE_KV, _T_PREFILL_Q = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -160,6 +160,13 @@ def query(cfg: Config, layer: int, step: int = 0) -> np.ndarray:
     """Decode query of one step: uint16 (bf16 bits) [batch][q_heads][head_dim]."""
     g = _rng(cfg, _T_STEP_Q, layer, step)
     return _to_bf16_bits(g.standard_normal((cfg.batch, cfg.q_heads, cfg.head_dim), dtype=np.float32))
+
+
+def prefill_queries(cfg: Config, layer: int, b: int) -> np.ndarray:
+    """Queries of the prefill of sequence ``b`` (one per cached token): uint16
+    (bf16 bits) [q_heads][context][head_dim], standard normal."""
+    g = _rng(cfg, _T_PREFILL_Q, layer, b)
+    return _to_bf16_bits(g.standard_normal((cfg.q_heads, cfg.context, cfg.head_dim), dtype=np.float32))
 
 
 def new_kv(cfg: Config, layer: int, step: int) -> Tuple[np.ndarray, np.ndarray]:
