@@ -15,7 +15,8 @@ runs in IEEE float32 with round-half-even, the precision the codec reading
 fixes; attention, masses and scores run in float64.
 
 Modules
-  codec     rounding helpers, INT2 group quantiser, ledger layout, promote rule
+  codec     rounding helpers, b-bit (2, 4, 8) group quantiser, ledger layout,
+            promote rule
   attention tiered attention with per-window mass
   router    tier counts from the byte budget and the score-ranked router
   pool      the per-segment ledger/tier state machine (demote, promote, evict,

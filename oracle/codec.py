@@ -1,12 +1,16 @@
-"""INT2 window codec of the oracle (test infrastructure).
+"""Low-bit window codec of the oracle (test infrastructure).
 
 The QEvict summary fixes only that the recoverable tier is a compact low-bit
 format, INT2 in its experiments ("Methodologie: QEvict", tier 2), and that a
 window is quantised once, at its first demotion, into a persistent ledger that
 every later promotion and demotion reuses ("Kernmechanismen", Write-Once
-Quantization Ledger).  The codec reading adopted here:
+Quantization Ledger).  The RDKV summary lists 2, 4 and 8 as the hardware
+bit widths of its packed stream, grouped by width so that each group has one
+dequantisation path ("2.3 Efficiente Gepakte Decode (TriZone)", Zone A); the
+ledger width b is therefore a parameter, one of 2, 4, 8, with 2 the default.
+The codec reading adopted here:
 
-* asymmetric min/max per group of 32 values, 2-bit codes 0..3;
+* asymmetric min/max per group of 32 values, b-bit codes 0..2^b - 1;
 * K grouped per channel over 32 consecutive tokens (the key-per-channel
   strategy the LogQuant summary names in its "Implementatie" section);
 * V grouped per token over 32 consecutive channels;
@@ -50,24 +54,35 @@ def f32_to_f16(x: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------- quantiser ---
-def quantize_groups(x: np.ndarray):
+BITS = (2, 4, 8)
+
+
+def levels(bits: int) -> int:
+    """Largest code of a b-bit group: 2^b - 1."""
+    if bits not in BITS:
+        raise ValueError(f"ledger bit width {bits} is not one of {BITS}")
+    return (1 << bits) - 1
+
+
+def quantize_groups(x: np.ndarray, bits: int = 2):
     """Quantise groups along the last axis (length 32) of float32 values.
 
     Returns (codes uint8 [..., 32], scale fp16 [...], min fp16 [...]).
-    Steps, all in float32:
+    Steps, all in float32, with L = 2^bits - 1:
       1. signed zeros are made +0 so min/max are unique values;
       2. mn, mx = min, max of the group;
-      3. s32 = (mx - mn) / 3   (a true IEEE divide);
+      3. s32 = (mx - mn) / L   (a true IEEE divide);
       4. stored s16 = fp16(s32), m16 = fp16(mn); s, m = their float32 values;
-      5. s == 0: all codes 0; otherwise c = clamp(rint((x - m) / s), 0, 3),
+      5. s == 0: all codes 0; otherwise c = clamp(rint((x - m) / s), 0, L),
          rint = round half to even.
     """
+    top = levels(bits)
     x = np.asarray(x, dtype=np.float32)
     assert x.shape[-1] == GROUP
     x = np.where(x == 0, np.float32(0.0), x).astype(np.float32)
     mn = x.min(axis=-1)
     mx = x.max(axis=-1)
-    s32 = ((mx - mn) / np.float32(3.0)).astype(np.float32)
+    s32 = ((mx - mn) / np.float32(top)).astype(np.float32)
     s16 = f32_to_f16(s32)
     m16 = f32_to_f16(mn)
     s = s16.astype(np.float32)[..., None]
@@ -75,13 +90,13 @@ def quantize_groups(x: np.ndarray):
     u = (x - m).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         t = (u / np.where(s == 0, np.float32(1.0), s)).astype(np.float32)
-    c = np.clip(np.rint(t), 0, 3)
+    c = np.clip(np.rint(t), 0, top)
     c = np.where(s == 0, 0, c).astype(np.uint8)
     return c, s16, m16
 
 
-def quantize_window(k_bits: np.ndarray, v_bits: np.ndarray) -> dict:
-    """Quantise one window of one kv head.
+def quantize_window(k_bits: np.ndarray, v_bits: np.ndarray, bits: int = 2) -> dict:
+    """Quantise one window of one kv head to b-bit codes.
 
     k_bits, v_bits: bf16 bits [W][D] (W, D multiples of 32).
     Returns the ledger entry in unpacked form:
@@ -94,9 +109,9 @@ def quantize_window(k_bits: np.ndarray, v_bits: np.ndarray) -> dict:
     w, d = k.shape
     assert w % GROUP == 0 and d % GROUP == 0
     kg = k.reshape(w // GROUP, GROUP, d).transpose(0, 2, 1)          # [W/32][D][32]
-    kc, ks, km = quantize_groups(kg)
+    kc, ks, km = quantize_groups(kg, bits)
     vg = v.reshape(w, d // GROUP, GROUP)                              # [W][D/32][32]
-    vc, vs, vm = quantize_groups(vg)
+    vc, vs, vm = quantize_groups(vg, bits)
     return {
         "Kc": np.ascontiguousarray(kc.transpose(0, 2, 1).reshape(w, d)),
         "Ks": ks, "Km": km,
@@ -120,48 +135,57 @@ def dequant_window_f64(e: dict):
 def promote_bits(e: dict):
     """bf16 bits a promotion writes back: bf16_rne(float32(c*s + m)).
 
-    c*s + m is exact in float64 (fp16 operands, c <= 3), so one cast to
-    float32 is the single rounding of a fused multiply-add, then one rounding
-    to bf16.
+    c*s + m is exact in float64 (fp16 operands are multiples of 2^-24 below
+    2^16 and c <= 255, so the sum needs at most 48 significant bits), so one
+    cast to float32 is the single rounding of a fused multiply-add, then one
+    rounding to bf16.
     """
     k, v = dequant_window_f64(e)
     return f32_to_bf16_rne(k.astype(np.float32)), f32_to_bf16_rne(v.astype(np.float32))
 
 
 # ------------------------------------------------------- canonical layout ---
-def pack_codes(c: np.ndarray) -> np.ndarray:
-    """[W][D] codes -> [W][D/4] bytes; code (t, d) in byte d//4, bits 2*(d%4)."""
+def pack_codes(c: np.ndarray, bits: int = 2) -> np.ndarray:
+    """[W][D] b-bit codes -> [W][D*b/8] bytes, LSB first: code (t, d) sits in
+    byte (d*b)//8 at bits (d*b) % 8 .. +b-1."""
+    levels(bits)
     c = np.asarray(c, dtype=np.uint8)
     w, d = c.shape
-    q = c.reshape(w, d // 4, 4).astype(np.uint16)
-    return (q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)).astype(np.uint8)
+    per = 8 // bits
+    q = c.reshape(w, d // per, per).astype(np.uint16)
+    out = np.zeros((w, d // per), np.uint16)
+    for i in range(per):
+        out |= q[..., i] << (bits * i)
+    return out.astype(np.uint8)
 
 
-def unpack_codes(p: np.ndarray) -> np.ndarray:
+def unpack_codes(p: np.ndarray, bits: int = 2) -> np.ndarray:
+    levels(bits)
     p = np.asarray(p, dtype=np.uint8)
-    w, d4 = p.shape
-    out = np.empty((w, d4, 4), dtype=np.uint8)
-    for i in range(4):
-        out[..., i] = (p >> (2 * i)) & 3
-    return out.reshape(w, d4 * 4)
+    w, nb = p.shape
+    per = 8 // bits
+    out = np.empty((w, nb, per), dtype=np.uint8)
+    for i in range(per):
+        out[..., i] = (p >> (bits * i)) & ((1 << bits) - 1)
+    return out.reshape(w, nb * per)
 
 
-def entry_bytes(e: dict) -> bytes:
+def entry_bytes(e: dict, bits: int = 2) -> bytes:
     """Canonical ledger bytes of one (window, kv head): Kc, Vc, Ks, Km, Vs, Vm."""
     return b"".join([
-        pack_codes(e["Kc"]).tobytes(), pack_codes(e["Vc"]).tobytes(),
+        pack_codes(e["Kc"], bits).tobytes(), pack_codes(e["Vc"], bits).tobytes(),
         e["Ks"].astype("<f2").tobytes(), e["Km"].astype("<f2").tobytes(),
         e["Vs"].astype("<f2").tobytes(), e["Vm"].astype("<f2").tobytes(),
     ])
 
 
-def entry_from_bytes(buf: bytes, w: int, d: int) -> dict:
+def entry_from_bytes(buf: bytes, w: int, d: int, bits: int = 2) -> dict:
     """Inverse of :func:`entry_bytes`."""
     a = np.frombuffer(buf, dtype=np.uint8)
     o = 0
-    n = w * d // 4
-    kc = unpack_codes(a[o:o + n].reshape(w, d // 4)); o += n
-    vc = unpack_codes(a[o:o + n].reshape(w, d // 4)); o += n
+    n = w * d * bits // 8
+    kc = unpack_codes(a[o:o + n].reshape(w, d * bits // 8), bits); o += n
+    vc = unpack_codes(a[o:o + n].reshape(w, d * bits // 8), bits); o += n
     g = (w // GROUP) * d * 2
     ks = a[o:o + g].view("<f2").reshape(w // GROUP, d); o += g
     km = a[o:o + g].view("<f2").reshape(w // GROUP, d); o += g
@@ -173,6 +197,7 @@ def entry_from_bytes(buf: bytes, w: int, d: int) -> dict:
             "Vs": vs.astype(np.float16), "Vm": vm.astype(np.float16)}
 
 
-def entry_nbytes(w: int, d: int) -> int:
-    """Bytes of one (window, kv head) entry: 2*W*D/4 codes + 4*(W*D/32)*2."""
-    return 2 * (w * d // 4) + 4 * (w * d // GROUP) * 2
+def entry_nbytes(w: int, d: int, bits: int = 2) -> int:
+    """Bytes of one (window, kv head) entry: 2*W*D*b/8 codes + 4*(W*D/32)*2."""
+    levels(bits)
+    return 2 * (w * d * bits // 8) + 4 * (w * d // GROUP) * 2

@@ -4,7 +4,8 @@ A segment is one (sequence, layer) pair: the unit the router ranks.  Each
 window spans all kv heads of the layer.  The transitions follow the QEvict
 summary ("Kernmechanismen", recoverable hierarchy):
 
-* demote (full precision -> INT2): quantise the window's current bf16 values
+* demote (full precision -> INT2, or the ledger's b bits): quantise the
+  window's current bf16 values
   only if it has no ledger entry yet; the ledger entry is written once and
   kept ("Write-Once Quantization Ledger");
 * promote (INT2 -> full precision): dequantise the ledger entry back into
@@ -28,7 +29,10 @@ from .router import E, F, Q
 
 
 class Segment:
-    def __init__(self, kv_heads: int, window: int, head_dim: int, n_recent: int = 4):
+    def __init__(self, kv_heads: int, window: int, head_dim: int, n_recent: int = 4,
+                 bits: int = 2):
+        codec.levels(bits)
+        self.bits = bits                         # ledger code width (2, 4, 8)
         self.hkv = kv_heads
         self.W = window
         self.D = head_dim
@@ -91,7 +95,7 @@ class Segment:
         if self.valid(w) != self.W:
             raise ValueError("a partial window cannot be quantised")
         if w not in self.ledger:
-            self.ledger[w] = [codec.quantize_window(self.k[w][h], self.v[w][h])
+            self.ledger[w] = [codec.quantize_window(self.k[w][h], self.v[w][h], self.bits)
                               for h in range(self.hkv)]
             self.quantized[w] += 1
         del self.k[w], self.v[w]
@@ -138,7 +142,7 @@ class Segment:
 
     # ---------------------------------------------------------- routing ---
     def counts(self, budget_frac: float, hi_frac: float):
-        return router.tier_counts(self.n, self.R, budget_frac, hi_frac)
+        return router.tier_counts(self.n, self.R, budget_frac, hi_frac, self.bits)
 
     def route(self, budget_frac: float, hi_frac: float, scores=None) -> dict:
         """Route every window; apply demotions, promotions and evictions.
@@ -162,7 +166,7 @@ class Segment:
 
     # ------------------------------------------------------------ views ---
     def bytes_used(self) -> int:
-        """Tier bytes of the segment (bf16 windows + INT2 windows), all heads."""
+        """Tier bytes of the segment (bf16 windows + ledger windows), all heads."""
         f = sum(1 for t in self.tier if t == F)
         q = sum(1 for t in self.tier if t == Q)
-        return self.hkv * (f * 4 * self.W * self.D + q * codec.entry_nbytes(self.W, self.D))
+        return self.hkv * (f * 4 * self.W * self.D + q * codec.entry_nbytes(self.W, self.D, self.bits))

@@ -11,12 +11,13 @@ Readings where the pages are silent:
 
 * the most recent R windows always stay full precision;
 * counts from the byte budget beta (fraction of the full bf16 KV) and the
-  full-precision fraction phi, with n windows:
+  full-precision fraction phi, with n windows and a b-bit ledger:
       n_hi = min(n, max(R, floor(phi * n)))
-      n_lo = max(0, min(n - n_hi, floor((beta * n - n_hi) * 16 / 3)))
-  16/3 is bf16 bytes over INT2 bytes of one window (4*W*D against
-  0.75*W*D: 2-bit codes plus an fp16 scale and min per 32 values).  The
-  expression is evaluated in IEEE double in exactly this order;
+      n_lo = max(0, min(n - n_hi, floor((beta * n - n_hi) * 16 / (b + 1))))
+  16/(b + 1) is bf16 bytes over ledger bytes of one window: 16 bits per
+  value against b-bit codes plus an fp16 scale and min per 32 values (one
+  more bit per value); 16/3 for INT2.  The expression is evaluated in IEEE
+  double in exactly this order;
 * ranking key: score descending, ties to the lower (older) window index;
 * an evicted window is never eligible again.
 """
@@ -28,10 +29,13 @@ from typing import Dict, List, Sequence, Tuple
 E, Q, F = 0, 1, 2
 
 
-def tier_counts(n: int, n_recent: int, budget_frac: float, hi_frac: float) -> Tuple[int, int]:
-    """(n_hi, n_lo) for a segment of n windows."""
+def tier_counts(n: int, n_recent: int, budget_frac: float, hi_frac: float,
+                bits: int = 2) -> Tuple[int, int]:
+    """(n_hi, n_lo) for a segment of n windows and a ledger of `bits`-bit codes."""
+    if bits not in (2, 4, 8):
+        raise ValueError(f"ledger bit width {bits} is not one of 2, 4, 8")
     n_hi = min(n, max(n_recent, math.floor(hi_frac * n)))
-    lo = math.floor((budget_frac * n - n_hi) * 16.0 / 3.0)
+    lo = math.floor((budget_frac * n - n_hi) * 16.0 / float(bits + 1))
     n_lo = max(0, min(n - n_hi, lo))
     return n_hi, n_lo
 

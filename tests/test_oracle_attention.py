@@ -6,6 +6,7 @@ float64, on explicitly assembled token sets; plus brute-force scalar loops.
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import attention, codec
@@ -27,8 +28,8 @@ def _sdpa(q, k, v):
     return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0, :].numpy()
 
 
-def _segment(rng, hkv=2, w=64, d=64, tokens=640, outlier=False):
-    seg = Segment(hkv, w, d, 4)
+def _segment(rng, hkv=2, w=64, d=64, tokens=640, outlier=False, bits=2):
+    seg = Segment(hkv, w, d, 4, bits=bits)
     k = _bits(rng, (hkv, tokens, d))
     if outlier:
         k = _bits(rng, (hkv, tokens, d), 1.0)
@@ -65,9 +66,10 @@ def test_eviction_renormalises_over_remaining_tokens():
     assert np.allclose(mass.sum(1), 1.0, atol=1e-12)
 
 
-def test_int2_windows_attend_with_dequantised_values():
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_int2_windows_attend_with_dequantised_values(bits):
     rng = np.random.default_rng(12)
-    seg, k, v = _segment(rng, hkv=1, tokens=640, outlier=True)
+    seg, k, v = _segment(rng, hkv=1, tokens=640, outlier=True, bits=bits)
     for w in (1, 2, 5):
         seg.demote(w)
     seg.evict(6)
@@ -81,7 +83,7 @@ def test_int2_windows_attend_with_dequantised_values():
     keep = np.concatenate([np.arange(w * 64, (w + 1) * 64) for w in range(10) if w != 6])
     ref = _sdpa(codec.bf16_to_f64(q), kf[:, keep], vf[:, keep])
     assert np.abs(out - ref).max() < 1e-12
-    # INT2 windows still receive mass; the evicted one gets none
+    # ledger windows still receive mass; the evicted one gets none
     assert (mass[:, [1, 2, 5]] > 0).all() and (mass[:, 6] == 0).all()
 
 

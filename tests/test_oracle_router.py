@@ -24,6 +24,36 @@ def test_counts_match_workload_descriptions(golden_dir):
             assert round(100 * n_lo / c["n"], 1) == c["percent_int2"]
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_counts_fill_the_byte_budget(bits):
+    """The counts spend the budget: bf16 windows cost 16 bits per value,
+    ledger windows b + 1 (codes plus fp16 scale and min per 32 values); the
+    tiers fit the budget and one more ledger window would not, unless every
+    window is already kept."""
+    rng = np.random.default_rng(12)
+    for _ in range(3000):
+        n = int(rng.integers(1, 1200))
+        beta = float(rng.uniform(0.01, 0.6))
+        phi = float(rng.uniform(0.0, beta))
+        n_hi, n_lo = router.tier_counts(n, 4, beta, phi, bits)
+        assert n_hi == min(n, max(4, int(np.floor(phi * n))))
+        cost = lambda f, q: 16 * f + (bits + 1) * q
+        if n_lo > 0:
+            assert cost(n_hi, n_lo) <= 16 * beta * n * (1 + 1e-12)
+        if n_hi + n_lo < n and cost(n_hi, 0) <= 16 * beta * n:
+            assert cost(n_hi, n_lo + 1) > 16 * beta * n * (1 - 1e-12)
+
+
+def test_counts_wider_ledgers_on_the_llama_32k_shape():
+    # 256 windows, 20 % budget, 10 % bf16: 25 bf16 windows, then what the
+    # remaining 26.2 window-budgets buy at 3, 5 and 9 bits per value
+    assert router.tier_counts(256, 4, 0.2, 0.1, 2) == (25, 139)   # floor(26.2 * 16 / 3)
+    assert router.tier_counts(256, 4, 0.2, 0.1, 4) == (25, 83)    # floor(26.2 * 16 / 5)
+    assert router.tier_counts(256, 4, 0.2, 0.1, 8) == (25, 46)    # floor(26.2 * 16 / 9)
+    with pytest.raises(ValueError):
+        router.tier_counts(256, 4, 0.2, 0.1, 3)
+
+
 def test_counts_edge_cases():
     assert router.tier_counts(3, 4, 0.2, 0.1) == (3, 0)          # fewer windows than R
     assert router.tier_counts(10, 4, 0.1, 0.1) == (4, 0)          # budget below the recent tail
@@ -85,37 +115,40 @@ def test_evicted_never_return_and_recent_stay_bf16():
     assert 8 in tr["promote"]
 
 
-def test_route_respects_budget_and_counts():
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_route_respects_budget_and_counts(bits):
     rng = np.random.default_rng(200)
-    seg = Segment(1, 64, 64, 4)
+    seg = Segment(1, 64, 64, 4, bits=bits)
     k = (rng.standard_normal((1, 64 * 40, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     seg.prefill(k, k, prior=rng.lognormal(0, 1, 40))
     tr = seg.route(0.2, 0.1)
-    n_hi, n_lo = router.tier_counts(40, 4, 0.2, 0.1)
+    n_hi, n_lo = router.tier_counts(40, 4, 0.2, 0.1, bits)
     assert seg.tier.count(F) == n_hi and seg.tier.count(Q) == n_lo
     assert len(tr["first_quant"]) == n_lo and tr["evict"]
     full = 40 * 4 * 64 * 64
     assert seg.bytes_used() <= 0.2 * full
 
 
-def test_write_once_ledger():
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_write_once_ledger(bits):
     """demote -> promote -> demote: the ledger bytes stay identical and the
     window is quantised exactly once; the promoted bf16 is the ledger's
     dequantisation, not the original."""
     rng = np.random.default_rng(201)
-    seg = Segment(2, 64, 64, 4)
+    seg = Segment(2, 64, 64, 4, bits=bits)
     k = (rng.standard_normal((2, 64 * 8, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     v = (rng.standard_normal((2, 64 * 8, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     seg.prefill(k, v)
     seg.demote(1)
-    first = [codec.entry_bytes(e) for e in seg.ledger[1]]
+    first = [codec.entry_bytes(e, bits) for e in seg.ledger[1]]
+    assert len(first[0]) == codec.entry_nbytes(64, 64, bits)
     seg.promote(1)
     assert seg.tier[1] == F
     pk, pv = codec.promote_bits(seg.ledger[1][0])
     assert np.array_equal(seg.k[1][0], pk) and np.array_equal(seg.v[1][0], pv)
     assert not np.array_equal(seg.k[1][0], k[0, 64:128])
     seg.demote(1)
-    assert [codec.entry_bytes(e) for e in seg.ledger[1]] == first
+    assert [codec.entry_bytes(e, bits) for e in seg.ledger[1]] == first
     assert seg.quantized[1] == 1
     seg.evict(1)
     assert 1 not in seg.ledger and seg.tier[1] == E
