@@ -11,6 +11,9 @@ adds it to the cumulative scores), and every 16th step of a pool a routing
 event (router, demotions into the write-once ledger, promotions).  Steps rotate over enough pool replicas (each its own arena) that
 every step reads its windows from HBM, not from the 256 MB Infinity Cache.
 
+`--ledger-bits 4` or `8` gives the pools a 4-bit or 8-bit ledger instead of
+INT2 (same budget: fewer ledger windows, b + 1 bits per value each).
+
 `--workload qwen7b_32k` runs it on the Qwen2.5-7B shape (batch 8, 28 query /
 4 kv heads, 5 bf16 / 41 INT2 / 210 evicted windows per sequence; contexts drawn
 on the device).  `--workload llama8b_128k_loop` runs the same measurement on
@@ -46,12 +49,13 @@ HBM_PEAK_GBS = 8000.0
 ROUTE_EVERY = 16
 
 
-def attn_bytes(c, n_f, n_q, n_windows):
+def attn_bytes(c, n_f, n_q, n_windows, bits=2):
     """Algorithmic bytes of one attention launch: every bf16 window's K and V
-    (4*W*D per kv head), every INT2 window's codes + fp16 scale/min (3*W*D/4),
-    the query, the output, the window masses and the page table."""
+    (4*W*D per kv head), every ledger window's codes + fp16 scale/min
+    ((b+1)*W*D/4: 3*W*D/4 for INT2), the query, the output, the window masses
+    and the page table."""
     wd = c.window * c.head_dim
-    kv = c.batch * c.kv_heads * (n_f * 4 * wd + n_q * 3 * wd // 4)
+    kv = c.batch * c.kv_heads * (n_f * 4 * wd + n_q * (bits + 1) * wd // 4)
     io = c.batch * c.q_heads * c.head_dim * (2 + 4) + c.batch * c.q_heads * n_windows * 4
     return kv + io + c.batch * n_windows * 4
 
@@ -60,9 +64,9 @@ def score_bytes(c, n_windows):
     return c.batch * c.q_heads * n_windows * 4 + c.batch * n_windows * (8 + 4)
 
 
-def route_bytes(c, n_windows, first_quant, promotions):
+def route_bytes(c, n_windows, first_quant, promotions, bits=2):
     wd = c.window * c.head_dim
-    move = c.kv_heads * (4 * wd + 3 * wd // 4)
+    move = c.kv_heads * (4 * wd + (bits + 1) * wd // 4)
     return c.batch * n_windows * (4 + 4) + (first_quant + promotions) * move
 
 
@@ -129,6 +133,8 @@ def main():
                     help="pool replicas the steps rotate over (default: 24 at 32K, 2 at 128K)")
     ap.add_argument("--workload", choices=("llama8b_32k", "qwen7b_32k", "llama8b_128k_loop"),
                     default="llama8b_32k")
+    ap.add_argument("--ledger-bits", type=int, choices=(2, 4, 8), default=2,
+                    help="code width of the pools' ledger (default 2: INT2)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -153,6 +159,7 @@ def main():
     from tiered_int2_fp16_amd import binding as B
 
     c = CONFIGS[args.workload]
+    bits = args.ledger_bits
     loop = c.append
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -185,7 +192,7 @@ def main():
             KN.append(torch.from_numpy(kn.view(np.int16)).to(dev))
             VN.append(torch.from_numpy(vn.view(np.int16)).to(dev))
     cfg = B.make_config(c.batch, c.layers, c.q_heads, c.kv_heads, c.head_dim, c.window, maxw,
-                        c.n_recent, maxw, maxw)
+                        c.n_recent, maxw, maxw, bits)
     pools, outs, masses, trs, cnts = [], [], [], [], []
     for r in range(R):
         p = B.Pool(cfg, dev)
@@ -199,14 +206,14 @@ def main():
         masses.append(torch.zeros(c.batch, c.q_heads, maxw, dtype=torch.float32, device=dev))
         trs.append(tr)
         cnts.append(cn)
-    K_keys = K if c.name == "llama8b_32k" else None   # for the prefill-score pass below
+    K_keys = K if c.name == "llama8b_32k" and bits == 2 else None   # for the prefill-score pass below
     del K, V
     torch.cuda.synchronize()
     pages = pools[0].pages(0).cpu().numpy() & 3
     n_f, n_q = int((pages[0] == 2).sum()), int((pages[0] == 1).sum())
     assert all(int((pg == 2).sum()) == n_f and int((pg == 1).sum()) == n_q for pg in pages)
     assert all(p.check() == 0 for p in pools)
-    log(f"{R} replicas ready: {n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows")
+    log(f"{R} replicas ready: {n_f} bf16 / {n_q} {bits}-bit / {n - n_f - n_q} evicted windows")
     local = [0] * R
     route_log = []  # (replica, counts tensor snapshot index)
 
@@ -353,9 +360,9 @@ def main():
                    "frac": round(flops / (pf_ms * 1e-3) / 1e12 / 2500.0, 4)}
         del qp, ws, K_keys
 
-    per_attn = attn_bytes(c, n_f, n_q, n)
+    per_attn = attn_bytes(c, n_f, n_q, n, bits)
     total_bytes = K_steps * (per_attn + score_bytes(c, n)) + \
-        len(routed) * route_bytes(c, n, 0, 0) + route_bytes(c, 0, fq, pr)
+        len(routed) * route_bytes(c, n, 0, 0, bits) + route_bytes(c, 0, fq, pr, bits)
     ms_per_step = 1e3 * t_timed / K_steps
     value = total_bytes / t_timed / 1e9
     achieved = per_attn / (attn_ms * 1e-3) / 1e9
@@ -373,8 +380,8 @@ def main():
     else:
         workload_name = ("llama8b_32k: Llama-3.1-8B attention shape, 32K context, one decode "
                          "step per pool, batch 1, 32 q / 8 kv heads, head_dim 128, window 128, "
-                         "20% byte budget (25 bf16 / 139 INT2 / 92 evicted windows), route "
-                         "every 16 steps")
+                         f"20% byte budget ({n_f} bf16 / {n_q} INT2 / {n - n_f - n_q} evicted windows), "
+                         "route every 16 steps")
     result = {
         "metric": "tiered decode-attn effective HBM GB/s (% of peak) + decode steps/s at "
                   + ("128K ctx" if loop else "32K ctx"),
@@ -387,7 +394,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+int2",
+        "dtype": f"bf16+int{bits}",
         "data": "synthetic",
         "config": {"workload": workload_name,
                    "global_batch": c.batch, "seq_len": c.context, "parallelism": "none (1 GPU)",
@@ -397,14 +404,18 @@ def main():
         "attn_kernel_us": round(attn_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(khash) if c.name == "llama8b_32k" else None},
+                     "traffic": measured_traffic(khash) if c.name == "llama8b_32k" and bits == 2 else None},
         "kernel_source_hash": khash,
         "mass_emission": mass_emission,
         "route_diagnostics": diagnostics,
     }
     if prefill is not None:
         result["prefill_scores"] = prefill
-    if not args.no_cpu_baseline and c.name == "llama8b_32k":
+    if bits != 2:
+        result["config"]["workload"] = workload_name.replace("INT2", f"{bits}-bit") + \
+            f" ({bits}-bit ledger: {bits + 1} bits per ledger value)"
+        result["config"]["ledger_bits"] = bits
+    if not args.no_cpu_baseline and c.name == "llama8b_32k" and bits == 2:
         result["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

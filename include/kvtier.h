@@ -6,7 +6,8 @@
  * (sequence, layer) segment is cut into windows of consecutive tokens; every
  * window sits in one of three tiers -
  *   F  full precision (bf16 here),
- *   Q  recoverable INT2, backed by a write-once quantisation ledger,
+ *   Q  recoverable low-bit (INT2 in the summary's experiments; INT4 or INT8
+ *      per pool here), backed by a write-once quantisation ledger,
  *   E  evicted, for good -
  * and windows move between tiers under a byte budget by their cumulative
  * attention score.  One decode step attends over F and Q windows and emits the
@@ -58,7 +59,7 @@ enum { KV_TIER_E = 0, KV_TIER_Q = 1, KV_TIER_F = 2 };
 /* Device error word bits (kv_pool_check). */
 enum {
   KV_ERR_DEMOTE_STATE = 1,     /* demote item not a full bf16 window */
-  KV_ERR_PROMOTE_STATE = 2,    /* promote item not INT2 with a ledger entry */
+  KV_ERR_PROMOTE_STATE = 2,    /* promote item not ledger-tier with a ledger entry */
   KV_ERR_NO_BF16_SLOT = 4,     /* no free bf16 slot in the segment */
   KV_ERR_NO_LEDGER_SLOT = 8,   /* no free ledger slot in the segment */
   KV_ERR_APPEND_STATE = 16,    /* append into a window that is not bf16 */
@@ -72,7 +73,16 @@ enum {
  * q_heads / kv_heads in {1, 2, 4, 7, 8}; head_dim in {64, 128}; window a
  * multiple of 32 in [32, 256]; 1 <= max_windows <= 4096 with
  * max_windows * window / 32 <= 8192; bf16_slots <= 16383
- * and ledger_slots <= 32767 per segment; n_recent >= 0. */
+ * and ledger_slots <= 32767 per segment; n_recent >= 0; ledger_bits 0 (= 2),
+ * 2, 4 or 8.
+ * ledger_bits is the code width of the pool's quantised tier: INT2 is the
+ * width of the QEvict summary's experiments ("Methodologie: QEvict", tier 2);
+ * 2, 4 and 8 are the packed widths the RDKV summary groups its stream by
+ * ("2.3 Efficiente Gepakte Decode (TriZone)", Zone A).  Every window of a pool
+ * uses the same width.  Value limits of the quantised tier at b bits (values
+ * beyond them are invalid input: the attention's fp16 operands overflow):
+ * |q| < 65504 / 2^b, K group range * |q| < 65504 * (2^b - 1) / 2^b, and V group
+ * range < 65504 * (2^b - 1) / 2^(b+3) (b = 2: 6141, 4: 7676, 8: 8156). */
 typedef struct {
   int32_t batch, layers, q_heads, kv_heads;
   int32_t head_dim;
@@ -80,7 +90,8 @@ typedef struct {
   int32_t max_windows;   /* windows per segment, including growth by decode */
   int32_t n_recent;      /* newest windows that always stay bf16 */
   int32_t bf16_slots;    /* bf16 window slots per segment */
-  int32_t ledger_slots;  /* INT2 ledger slots per segment */
+  int32_t ledger_slots;  /* ledger slots per segment */
+  int32_t ledger_bits;   /* code width of the ledger: 2 (or 0), 4, 8 */
 } kv_pool_config;
 
 /* Arena regions (kv_pool_region).  All regions are 256-byte aligned.
@@ -88,8 +99,8 @@ typedef struct {
  *                    2*W*D bf16 values in 32-token tiles laid out for the
  *                    matrix cores (K part, then V part of each tile; the
  *                    placement is internal - kv_read_window gives [W][D]).
- *  KV_REGION_LEDGER  INT2 ledger slots: [segment][ledger_slot][kv_head] entries
- *                    of 3*W*D/4 bytes in 32-token tiles (2-bit K and V codes,
+ *  KV_REGION_LEDGER  ledger slots: [segment][ledger_slot][kv_head] entries of
+ *                    (b+1)*W*D/4 bytes in 32-token tiles (b-bit K and V codes,
  *                    fp16 K scale/min per channel, fp16 V scale/min per token
  *                    and 32-channel group; placement internal - kv_read_ledger
  *                    gives the canonical layout below).
@@ -109,9 +120,10 @@ enum {
  * invalid (kv_last_error says why). [host, pure] */
 size_t kv_pool_arena_bytes(const kv_pool_config* cfg);
 
-/* Bytes of one INT2 ledger entry (one window, one kv head): 3*W*D/4, i.e. 2-bit
- * codes plus an fp16 scale and min per 32 values = 3 bits per value. [host] */
-size_t kv_ledger_entry_bytes(int32_t window, int32_t head_dim);
+/* Bytes of one ledger entry (one window, one kv head) of b-bit codes:
+ * (b+1)*W*D/4, i.e. the codes plus an fp16 scale and min per 32 values = b+1
+ * bits per value (ledger_bits 0 means 2); 0 for an invalid argument. [host] */
+size_t kv_ledger_entry_bytes(int32_t window, int32_t head_dim, int32_t ledger_bits);
 
 /* Create a pool over a caller-owned device arena of at least
  * kv_pool_arena_bytes(cfg) bytes, 256-byte aligned.  Enqueues the clearing of
@@ -154,19 +166,20 @@ kv_status kv_prefill_scores(kv_pool* pool, int32_t layer, const void* q, const v
 kv_status kv_prefill(kv_pool* pool, int32_t layer, const void* k, const void* v,
                      int32_t tokens, const float* prior, void* stream);
 
-/* Demote windows from bf16 to INT2 ("Kernmechanismen", demotion; write-once
- * ledger).  items: int32 [batch][stride] window indices of `layer`, counts:
+/* Demote windows from bf16 to the ledger tier ("Kernmechanismen", demotion;
+ * write-once ledger).  items: int32 [batch][stride] window indices of `layer`, counts:
  * int32 [batch] items per sequence (device, so a router's output can be passed
  * straight in).  A window without a ledger entry is quantised now into the
  * lowest free ledger slot (per 32-value groups: K per channel over 32 tokens,
- * V per token over 32 channels; fp16 scale = (max-min)/3 and min; codes
- * round-half-even((x - min)/scale) in float32, clamped to 0..3); a window that
+ * V per token over 32 channels; fp16 scale = (max-min)/L and min, L =
+ * 2^ledger_bits - 1; codes round-half-even((x - min)/scale) in float32,
+ * clamped to 0..L); a window that
  * already has one keeps it unchanged.  Its bf16 slot is freed.  Items are
  * processed in order per sequence. */
 kv_status kv_demote_quantize(kv_pool* pool, int32_t layer, const int32_t* items,
                              int32_t stride, const int32_t* counts, void* stream);
 
-/* Promote windows from INT2 back to bf16 ("Kernmechanismen", promotion): the
+/* Promote windows from the ledger tier back to bf16 ("Kernmechanismen", promotion): the
  * ledger entry is dequantised, bf16_rne(fmaf(code, scale, min)), into the
  * lowest free bf16 slot; the ledger entry is kept.  Same item format as
  * kv_demote_quantize.  Enqueue demotions first: a promotion can reuse a slot
@@ -178,7 +191,7 @@ kv_status kv_promote_dequantize(kv_pool* pool, int32_t layer, const int32_t* ite
 size_t kv_attn_workspace_bytes(const kv_pool* pool);
 
 /* One decode step of grouped-query attention for every sequence of `layer`
- * over its bf16 and INT2 windows; evicted windows take no part (the softmax
+ * over its bf16 and ledger windows; evicted windows take no part (the softmax
  * normaliser runs over the remaining tokens).  Query head h reads kv head
  * h / (q_heads / kv_heads).
  *   q      bf16 [batch][q_heads][D]
@@ -223,10 +236,12 @@ kv_status kv_attn_timings(kv_pool* pool, float* ms, int32_t cap, int32_t* n);
  *          NULL: S[w] += sum over heads of mass[h][w] for live windows.
  *   do_route != 0: route every window.  With n windows, R = n_recent:
  *            n_hi = min(n, max(R, floor(hi_frac * n)))
- *            n_lo = max(0, min(n - n_hi, floor((budget_frac * n - n_hi) * 16 / 3)))
- *          (double precision, in this order); the R newest windows are bf16;
- *          the other live windows ranked by (S descending, index ascending):
- *          the first n_hi - R stay/become bf16, the next n_lo INT2, the rest
+ *            n_lo = max(0, min(n - n_hi, floor((budget_frac * n - n_hi) * 16 / (b + 1))))
+ *          (double precision, in this order; b = ledger_bits, so 16 / 3 for
+ *          INT2: bf16 bits per value over ledger bits per value); the R newest
+ *          windows are bf16; the other live windows ranked by (S descending,
+ *          index ascending): the first n_hi - R stay/become bf16, the next
+ *          n_lo go to the ledger tier, the rest
  *          are evicted now.  Demotions and promotions are written as lists for
  *          kv_demote_quantize / kv_promote_dequantize:
  *   transitions  int32 [3][batch][max_windows]: demote, promote, evict lists
@@ -260,9 +275,10 @@ kv_status kv_route_diagnostics(kv_pool* pool, int32_t layer, const int32_t* coun
                                const float* shadow_mass, float* diag, void* stream);
 
 /* Copy window `window` of sequence b, layer l, in the canonical layouts:
- * kv_read_ledger writes kv_heads ledger entries of 3*W*D/4 bytes to dst, each
- * Kc [W][D/4], Vc [W][D/4] (code of (t, d) in byte d/4, bits 2*(d%4)), Ks, Km
- * fp16 [W/32][D], Vs, Vm fp16 [W][D/32]; kv_read_window writes bf16 K then V
+ * kv_read_ledger writes kv_heads ledger entries of (b+1)*W*D/4 bytes to dst,
+ * each Kc [W][D*b/8], Vc [W][D*b/8] (b-bit code of (t, d) in byte d*b/8, bits
+ * (d*b)%8 .. +b-1), Ks, Km fp16 [W/32][D], Vs, Vm fp16 [W][D/32];
+ * kv_read_window writes bf16 K then V
  * [kv_heads][2][W][D].
  * A window without that copy sets KV_ERR_READ_MISSING and writes zeros. */
 kv_status kv_read_ledger(kv_pool* pool, int32_t layer, int32_t b, int32_t window,
@@ -270,11 +286,11 @@ kv_status kv_read_ledger(kv_pool* pool, int32_t layer, int32_t b, int32_t window
 kv_status kv_read_window(kv_pool* pool, int32_t layer, int32_t b, int32_t window,
                          void* dst, void* stream);
 
-/* The router's tier counts for a segment of n windows (the formula of
- * kv_score_route, evaluated on the host in the same double-precision order).
- * [host, pure] */
+/* The router's tier counts for a segment of n windows and a ledger of
+ * ledger_bits-bit codes (0 means 2): the formula of kv_score_route, evaluated
+ * on the host in the same double-precision order. [host, pure] */
 kv_status kv_tier_counts(int32_t n, int32_t n_recent, double budget_frac, double hi_frac,
-                         int32_t* n_hi, int32_t* n_lo);
+                         int32_t ledger_bits, int32_t* n_hi, int32_t* n_lo);
 
 /* Synchronise `stream`, read and clear the device error word.  Returns KV_OK or
  * KV_ESTATE (kv_last_error lists the bits); *bits (may be NULL) gets them. */

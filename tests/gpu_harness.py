@@ -55,13 +55,15 @@ class CachedSegment(Segment):
 
 
 class Pair:
-    def __init__(self, cfg, layers=None, seqs=None, bf16_slots=None, ledger_slots=None):
+    def __init__(self, cfg, layers=None, seqs=None, bf16_slots=None, ledger_slots=None, bits=2):
         from tiered_int2_fp16_amd import binding as B
         self.B = B
         self.cfg = cfg
+        self.bits = bits          # ledger code width of the pool (and of the oracle's segments)
         self.maxw = cfg.max_windows()
         pc = B.make_config(cfg.batch, cfg.layers, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.window,
-                           self.maxw, cfg.n_recent, bf16_slots or self.maxw, ledger_slots or self.maxw)
+                           self.maxw, cfg.n_recent, bf16_slots or self.maxw, ledger_slots or self.maxw,
+                           bits)
         self.pool = B.Pool(pc)
         self.seqs = list(range(cfg.batch)) if seqs is None else list(seqs)
         self.oracle = {}
@@ -78,7 +80,7 @@ class Pair:
             vs.append(v)
             prs.append(pr)
             if b in self.seqs:
-                seg = CachedSegment(c.kv_heads, c.window, c.head_dim, c.n_recent)
+                seg = CachedSegment(c.kv_heads, c.window, c.head_dim, c.n_recent, bits=self.bits)
                 seg.prefill(k, v, prior=pr.astype(np.float64))
                 self.oracle[(layer, b)] = seg
         self.pool.prefill(layer, dev(np.stack(ks)), dev(np.stack(vs)), c.context, dev(np.stack(prs)))
@@ -131,7 +133,7 @@ class Pair:
             for w in led:
                 got = self.pool.read_ledger(layer, b, w).cpu().numpy()
                 for h in range(self.cfg.kv_heads):
-                    assert got[h].tobytes() == codec.entry_bytes(seg.ledger[w][h]), (b, w, h)
+                    assert got[h].tobytes() == codec.entry_bytes(seg.ledger[w][h], seg.bits), (b, w, h)
             for w in fw:
                 got = self.pool.read_window(layer, b, w).cpu().numpy().view(np.uint16)
                 nt = seg.valid(w)

@@ -56,13 +56,19 @@ def test_arena_size_matches_layout(B):
     assert bf16 + ledger < n < bf16 + ledger + 64 * 1024
     assert B.kv_ledger_entry_bytes(128, 128) == 12288
     assert B.kv_ledger_entry_bytes(64, 64) == 3072
-    # 3 bits per value: 2-bit code + (16 + 16) bits per 32 values
-    assert B.kv_ledger_entry_bytes(128, 128) * 8 == 3 * 2 * 128 * 128
+    # b + 1 bits per value: b-bit code + (16 + 16) bits per 32 values
+    for bits in (2, 4, 8):
+        assert B.kv_ledger_entry_bytes(128, 128, bits) * 8 == (bits + 1) * 2 * 128 * 128
+    assert B.kv_ledger_entry_bytes(128, 128, 0) == 12288
+    assert B.kv_ledger_entry_bytes(128, 128, 3) == 0
+    cfg.ledger_bits = 8
+    assert B.kv_pool_arena_bytes(cfg) - n == 200 * 8 * (36864 - 12288)
 
 
 @pytest.mark.parametrize("field,value", [
     ("q_heads", 30), ("head_dim", 96), ("window", 48), ("max_windows", 0),
-    ("max_windows", 5000), ("bf16_slots", 0), ("bf16_slots", 20000), ("kv_heads", 0)])
+    ("max_windows", 5000), ("bf16_slots", 0), ("bf16_slots", 20000), ("kv_heads", 0),
+    ("ledger_bits", 3), ("ledger_bits", 16), ("ledger_bits", -2)])
 def test_invalid_configs_are_rejected(B, field, value):
     cfg = _cfg(B, CONFIGS["tiny"])
     setattr(cfg, field, value)
@@ -78,7 +84,11 @@ def test_host_tier_counts_match_oracle(B):
         r = int(rng.integers(0, 8))
         beta = float(rng.choice([rng.random(), 0.2, 0.05, 0.1, 0.125, 0.325]))
         phi = float(rng.choice([rng.random() * beta, 0.1, 0.02, 0.0625, 0.09375, 0.25]))
+        bits = int(rng.choice([2, 4, 8]))
         assert B.kv_tier_counts(n, r, beta, phi) == router.tier_counts(n, r, beta, phi)
+        assert B.kv_tier_counts(n, r, beta, phi, bits) == router.tier_counts(n, r, beta, phi, bits)
+    with pytest.raises(B.KvError):
+        B.kv_tier_counts(10, 4, 0.2, 0.1, 5)
 
 
 def test_null_arguments_fail_without_a_gpu(B):

@@ -33,27 +33,41 @@ int main() {
           v_chunk_elem(cmb, lane, e, &t, &d);
           bad += bf16_v_offset(t, d, D) != 32 * D + (cmb * 64 + lane) * 8 + e;
         }
-    // code positions: every (token, dim) gets its own 2-bit field in Kc / Vc
-    std::vector<int> kb(8 * D * 4, 0), vb(8 * D * 4, 0);
-    for (int t = 0; t < 32; ++t)
-      for (int d = 0; d < D; ++d) {
-        int wb, bit;
-        k_code_pos(t, d, D, &wb, &bit);
-        kb[wb * 4 + bit / 2]++;
-        v_code_pos(t, d, D, &wb, &bit);
-        vb[wb * 4 + bit / 2]++;
-      }
-    for (int x : kb) bad += x != 1;
-    for (int x : vb) bad += x != 1;
-    // field_elem inverts code_pos
-    for (int cmb = 0; cmb < D / 16; ++cmb)
-      for (int lane = 0; lane < 64; ++lane)
-        for (int e = 0; e < 8; ++e) {
-          int wb, bit, c2, e2;
-          code_pos(cmb, lane, e, D, &wb, &bit);
-          field_elem((wb - lane * (D / 8)) / 4, bit / 2, &c2, &e2);
-          bad += (c2 != cmb) || (e2 != e) || wb / (D / 8) != lane;
+    for (int bits : {2, 4, 8}) {
+      // code positions: every (token, dim) gets its own b-bit field in Kc / Vc
+      const LedgerTile LT(D, bits);
+      bad += LT.vc != 32 * D * bits / 8 || LT.bytes != 2 * LT.vc + 8 * D;
+      const int fields = 32 / bits;
+      std::vector<int> kb(LT.vc / 4 * fields, 0), vb(LT.vc / 4 * fields, 0);
+      for (int t = 0; t < 32; ++t)
+        for (int d = 0; d < D; ++d) {
+          int wb, bit;
+          k_code_pos(t, d, D, bits, &wb, &bit);
+          bad += wb % 4 != 0 || bit % bits != 0 || bit + bits > 32 || wb >= LT.vc;
+          kb[wb / 4 * fields + bit / bits]++;
+          v_code_pos(t, d, D, bits, &wb, &bit);
+          vb[wb / 4 * fields + bit / bits]++;
         }
+      for (int x : kb) bad += x != 1;
+      for (int x : vb) bad += x != 1;
+      // field_elem_b inverts code_pos; a lane's words are its own
+      const int lane_bytes = bits * D / 16;
+      for (int cmb = 0; cmb < D / 16; ++cmb)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int e = 0; e < 8; ++e) {
+            int wb, bit, c2, e2;
+            code_pos(cmb, lane, e, D, bits, &wb, &bit);
+            field_elem_b(bits, (wb - lane * lane_bytes) / 4, bit / bits, &c2, &e2);
+            bad += (c2 != cmb) || (e2 != e) || wb / lane_bytes != lane;
+            // elements 2r and 2r + 1 of a chunk sit 16 bits apart in one word
+            // (b = 2, 4) or in the same word's bytes 2(r%2), 2(r%2)+1 (b = 8)
+            if (e & 1) {
+              int wb0, bit0;
+              code_pos(cmb, lane, e - 1, D, bits, &wb0, &bit0);
+              bad += wb0 != wb || bit != bit0 + (bits == 8 ? 8 : 16);
+            }
+          }
+    }
     // token permutation of the QK rows is a bijection on 0..31
     std::vector<int> tk(32, 0);
     for (int blk = 0; blk < 2; ++blk)

@@ -36,7 +36,7 @@ EXPORTS = [
 class kv_pool_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "layers", "q_heads", "kv_heads", "head_dim", "window",
-        "max_windows", "n_recent", "bf16_slots", "ledger_slots")]
+        "max_windows", "n_recent", "bf16_slots", "ledger_slots", "ledger_bits")]
 
 
 _BF16 = (torch.int16, torch.bfloat16, torch.uint16) if hasattr(torch, "uint16") else (torch.int16, torch.bfloat16)
@@ -56,7 +56,7 @@ def _load() -> ctypes.CDLL:
     cfgp = ctypes.POINTER(kv_pool_config)
     sig = {
         "kv_pool_arena_bytes": (SZ, [cfgp]),
-        "kv_ledger_entry_bytes": (SZ, [I32, I32]),
+        "kv_ledger_entry_bytes": (SZ, [I32, I32, I32]),
         "kv_pool_create": (I32, [cfgp, P, SZ, P, ctypes.POINTER(P)]),
         "kv_pool_destroy": (I32, [P]),
         "kv_pool_region": (I32, [P, I32, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
@@ -72,7 +72,7 @@ def _load() -> ctypes.CDLL:
         "kv_prefill_scores": (I32, [P, I32, P, P, I32, P, SZ, P]),
         "kv_read_ledger": (I32, [P, I32, I32, I32, P, P]),
         "kv_read_window": (I32, [P, I32, I32, I32, P, P]),
-        "kv_tier_counts": (I32, [I32, I32, D, D, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "kv_tier_counts": (I32, [I32, I32, D, D, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "kv_pool_check": (I32, [P, P, ctypes.POINTER(I32)]),
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_attn_profile": (I32, [P, I32]),
@@ -107,10 +107,10 @@ def _stream(stream=None):
 
 
 def make_config(batch, layers, q_heads, kv_heads, head_dim, window, max_windows,
-                n_recent=4, bf16_slots=None, ledger_slots=None) -> kv_pool_config:
+                n_recent=4, bf16_slots=None, ledger_slots=None, ledger_bits=2) -> kv_pool_config:
     return kv_pool_config(batch, layers, q_heads, kv_heads, head_dim, window, max_windows, n_recent,
                           max_windows if bf16_slots is None else bf16_slots,
-                          max_windows if ledger_slots is None else ledger_slots)
+                          max_windows if ledger_slots is None else ledger_slots, ledger_bits)
 
 
 # ------------------------------------------------------------ C ABI names ---
@@ -121,13 +121,14 @@ def kv_pool_arena_bytes(cfg: kv_pool_config) -> int:
     return n
 
 
-def kv_ledger_entry_bytes(window: int, head_dim: int) -> int:
-    return LIB.kv_ledger_entry_bytes(window, head_dim)
+def kv_ledger_entry_bytes(window: int, head_dim: int, ledger_bits: int = 2) -> int:
+    return LIB.kv_ledger_entry_bytes(window, head_dim, ledger_bits)
 
 
-def kv_tier_counts(n, n_recent, budget_frac, hi_frac):
+def kv_tier_counts(n, n_recent, budget_frac, hi_frac, ledger_bits=2):
     hi, lo = ctypes.c_int32(), ctypes.c_int32()
-    _ck(LIB.kv_tier_counts(n, n_recent, budget_frac, hi_frac, ctypes.byref(hi), ctypes.byref(lo)))
+    _ck(LIB.kv_tier_counts(n, n_recent, budget_frac, hi_frac, ledger_bits, ctypes.byref(hi),
+                           ctypes.byref(lo)))
     return hi.value, lo.value
 
 
@@ -230,7 +231,8 @@ class Pool:
         self.h = kv_pool_create(cfg, self.arena)
         self.workspace = torch.empty(max(kv_attn_workspace_bytes(self.h), 256), dtype=torch.uint8,
                                      device=self.device)
-        self.entry_bytes = kv_ledger_entry_bytes(cfg.window, cfg.head_dim)
+        self.bits = cfg.ledger_bits or 2
+        self.entry_bytes = kv_ledger_entry_bytes(cfg.window, cfg.head_dim, self.bits)
 
     def close(self):
         if self.h is not None:

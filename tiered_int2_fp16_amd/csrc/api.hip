@@ -61,6 +61,7 @@ PoolView view(const kv_pool* p) {
   v.nb = g.cfg.bf16_slots;
   v.nl = g.cfg.ledger_slots;
   v.G = g.group;
+  v.lbits = g.cfg.ledger_bits;
   v.work_items = int(g.work_items);
   v.work_counts = int(g.work_counts);
   v.attn_counters = int(g.attn_counters);
@@ -104,9 +105,11 @@ size_t kv_pool_arena_bytes(const kv_pool_config* cfg) {
   return g.total;
 }
 
-size_t kv_ledger_entry_bytes(int32_t window, int32_t head_dim) {
+size_t kv_ledger_entry_bytes(int32_t window, int32_t head_dim, int32_t ledger_bits) {
   if (window <= 0 || head_dim <= 0 || window % 32 || head_dim % 32) return 0;
-  return size_t(3) * window * head_dim / 4;
+  if (ledger_bits == 0) ledger_bits = 2;
+  if (ledger_bits != 2 && ledger_bits != 4 && ledger_bits != 8) return 0;
+  return size_t(ledger_bits + 1) * window * head_dim / 4;
 }
 
 kv_status kv_pool_create(const kv_pool_config* cfg, void* arena, size_t arena_bytes, void* stream,
@@ -404,10 +407,13 @@ kv_status kv_pool_check(kv_pool* pool, void* stream, int32_t* bits) {
 }
 
 kv_status kv_tier_counts(int32_t n, int32_t n_recent, double budget_frac, double hi_frac,
-                         int32_t* n_hi, int32_t* n_lo) {
+                         int32_t ledger_bits, int32_t* n_hi, int32_t* n_lo) {
   if (!n_hi || !n_lo || n < 0 || n_recent < 0) return fail(KV_EINVAL, "bad arguments");
+  if (ledger_bits == 0) ledger_bits = 2;
+  if (ledger_bits != 2 && ledger_bits != 4 && ledger_bits != 8)
+    return fail(KV_EINVAL, "ledger_bits must be 0 (= 2), 2, 4 or 8");
   int hi = 0, lo = 0;
-  tier_counts(n, n_recent, budget_frac, hi_frac, &hi, &lo);
+  tier_counts(n, n_recent, budget_frac, hi_frac, ledger_bits, &hi, &lo);
   *n_hi = hi;
   *n_lo = lo;
   return KV_OK;

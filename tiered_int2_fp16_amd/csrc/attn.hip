@@ -1,12 +1,15 @@
 // Tiered decode attention with per-window mass for gfx950 (matrix cores).
 //
 // QEvict technical summary ("Methodologie: QEvict", "Kernmechanismen",
-// "Implementatie"): bf16 windows and INT2 windows both take part in attention,
+// "Implementatie"): bf16 windows and ledger windows (INT2 in the summary's
+// experiments; 4 or 8 bits per pool here) both take part in attention,
 // evicted windows do not; grouped-query attention; the attention each window
 // receives is what the cumulative score adds up.  Unlike the summary's
 // FlashAttention-2 path, which dequantises and rebuilds caches before attention
-// ("Resultaten", efficiency), INT2 tiles are decoded in registers inside this
-// kernel: HBM carries 3 bits per INT2 value, never a rebuilt bf16 copy.
+// ("Resultaten", efficiency), ledger tiles are decoded in registers inside this
+// kernel: HBM carries b + 1 bits per b-bit value (codes plus fp16 scale and
+// min per 32 values), never a rebuilt bf16 copy.  "INT2" below names the
+// ledger tier at any of its widths.
 //
 // Work split: grid (splits, kv heads, sequences), 4 wave64 per workgroup.  The
 // live 32-token tiles of a (sequence, kv head) are listed per tier (bf16,
@@ -27,17 +30,19 @@
 // One tile = 16x16x32 MFMAs with the token/dim placement of layout.h:
 //  bf16: S = K.q^T (bf16 inputs, exact products) then O^T += V^T.P^T with P
 //        split into bf16 high and low parts (2^-17 relative error).
-//  INT2: a code c becomes the fp16 value 1 + c/4 (two bit operations per pair
-//        of codes).  With per-channel K scale s and min m,
-//          q.k = sum_d (1 + c/4)(4 s q) + sum_d q (m - 4 s);
-//        4 s q is exact in fp32 and goes to the MFMA as fp16 high + low parts,
-//        the second sum (constant over the tile's tokens) is taken in fp32 -
-//        an fp16 rounding of either would shift a whole tile's logits at once.
-//        Each lane forms its own B operand from the tile's scales, which
-//        reach it through the wave's LDS buffer.  With per-token V scale s'
-//        and min m',
-//          sum_t p v = sum_t (1 + c/4)(4 p s') + sum_t (m'/4 - s')(4 p):
-//        one MFMA per 16 channels for the codes, one for the min term.
+//  ledger (b-bit codes, b = 2, 4, 8; INT2 in the QEvict summary's
+//        experiments): a code c becomes the fp16 value 1 + c/2^b, exactly
+//        (two register operations per pair of codes).  With per-channel K
+//        scale s and min m,
+//          q.k = sum_d (1 + c/2^b)(2^b s q) + sum_d q (m - 2^b s);
+//        2^b s q is exact in fp32 and goes to the MFMA as fp16 high + low
+//        parts, the second sum (constant over the tile's tokens) is taken in
+//        fp32 - an fp16 rounding of either would shift a whole tile's logits
+//        at once.  Each lane forms its own B operand from the tile's scales,
+//        which reach it through the wave's LDS buffer.  With per-token V
+//        scale s' and min m',
+//          sum_t p v = sum_t (1 + c/2^b)(2^b p s') + sum_t (m' - 2^b s')(2^b p) / 2^b:
+//        one MFMA per 16 channels for the codes, four for the min term.
 //
 // A decode step may append a token: it is attended straight from k_new/v_new
 // and stored in the newest window by the combine kernel, which also rewrites
@@ -163,6 +168,46 @@ __device__ inline f16x8 decode_codes(uint32_t X, uint32_t mask, uint32_t one) {
   return __builtin_bit_cast(f16x8, make_uint4(r[0], r[1], r[2], r[3]));
 }
 
+// Eight 4-bit codes of one chunk (word X, field f = element 2(f%4) + f/4)
+// -> fp16 (1 + c/16): register j takes fields j and j + 4, 16 bits apart; one
+// shift puts both at mantissa bits 6-9, a bit select adds the exponent of 1.0.
+__device__ inline f16x8 decode_codes4(uint32_t X) {
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sh = 4 * j;
+    const uint32_t y = sh <= 6 ? (X << (6 - sh)) : (X >> (sh - 6));
+    r[j] = bit_select(0x03C003C0u, y, 0x3C003C00u);
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+// Eight 8-bit codes of one chunk (bytes 0-3 of X0, then of X1, in element
+// order) -> fp16 (1 + c/256): a byte permute spreads elements 2j, 2j+1 over
+// the low bytes of the two halves, a shift-or places them at mantissa bits
+// 2-9 under the exponent of 1.0.
+__device__ inline f16x8 decode_codes8(uint32_t X0, uint32_t X1) {
+  uint32_t r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = __builtin_amdgcn_perm(0u, (j >> 1) ? X1 : X0, (j & 1) ? 0x0C030C02u : 0x0C010C00u);
+    r[j] = (t << 2) | 0x3C003C00u;
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+// The fp16 values 1 + c/2^BITS of the eight codes of chunk c of a part
+// (`w`: the lane's code words of that part).
+template <int BITS, int CW>
+__device__ inline f16x8 decode_chunk(const uint32_t (&w)[CW], int c, uint32_t mask, uint32_t one) {
+  if constexpr (BITS == 2)
+    return (c & 1) ? decode_codes<1>(w[c >> 1], mask, one) : decode_codes<0>(w[c >> 1], mask, one);
+  else if constexpr (BITS == 4)
+    return decode_codes4(w[c]);
+  else
+    return decode_codes8(w[2 * c], w[2 * c + 1]);
+}
+
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // Tile table entry: slot (15 bits) | window (12 bits) << 15 | tile (3 bits) << 27
@@ -178,7 +223,7 @@ template <int NB>
 struct WaveState {
   float m_run, l_run;
   f32x4 o[NB];   // O^T block nb: lane (g, n) holds column n, channels 16nb + 4g + i
-  f32x4 ob;      // 4 x INT2 V min term: lane (0, n) holds column n, channel group i
+  f32x4 ob;      // 2^b x ledger V min term: lane (0, n) holds column n, channel group i
 };
 
 // Online softmax over one tile of 8 scores per lane, z = s * scale + shift
@@ -188,7 +233,8 @@ struct WaveState {
 // on the wave's first tile, when they are still zero).  Until then a tile's
 // values are taken against the older reference, so p <= 2^kTau.  Returns
 // p[e] = 2^LG exp2(z[e] - m_run) and the tile sum of exp2(z - m_run).
-constexpr float kTau = 3.f;   // 4p <= 32 keeps 4p*s' in fp16 range for |s'| < 2047
+// (2^b p <= 2^(b+3) keeps 2^b p s' in fp16 range for |s'| < 65504 / 2^(b+3))
+constexpr float kTau = 3.f;
 
 template <int NB, int LG>
 __device__ inline void softmax_tile(WaveState<NB>& st, const float (&s)[8], float scale, float shift,
@@ -225,20 +271,22 @@ __device__ inline void softmax_tile(WaveState<NB>& st, const float (&s)[8], floa
 // The first three arguments (the layer's page table and token counts, the
 // page table's row length) come preloaded in SGPRs (the library is built with
 // kernarg preloading), so the plan's first loads need no kernel-argument load.
-template <int D, int GP>
+template <int D, int GP, int BITS>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict__ pages_layer,
                                                       const int32_t* __restrict__ tokens_layer, int maxw_arg,
                                                       PoolView pv, AttnArgs a) {
   constexpr int KK = D / 32;   // 32-dim slices of the QK product
   constexpr int NB = D / 16;   // 16-channel blocks of the PV product (= code chunks per part)
-  constexpr int CW = D / 32;   // 32-bit code words per lane per part
+  constexpr int CW = BITS * D / 64;   // 32-bit code words per lane per part
+  constexpr int SCW = D / 32;        // 32-bit words per lane of a tile's scale block
+  constexpr float kCodeScale = float(1 << BITS);   // 2^b
   constexpr int kList = 64;    // tile entries a wave lists at a time
   constexpr int kMixedList = 8;   // INT2 tiles from which a wave takes both tiers in one loop
   extern __shared__ uint32_t s_dyn[];    // plan (page entries, tile prefixes), slot bitmap
   __shared__ float s_wm[kAttnWaves][kGMax], s_wl[kAttnWaves][kGMax];
   __shared__ float s_wo[kAttnWaves][kGMax][D];
   __shared__ float s_wb[kAttnWaves][kGMax][4];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scb[kAttnWaves][8 * D];  // INT2 tile scales
+  __shared__ __attribute__((aligned(16))) uint8_t s_scb[kAttnWaves][8 * D];  // ledger tile scales
   __shared__ uint32_t s_listf[kAttnWaves][kList];                              // a wave's bf16 tiles
   __shared__ uint32_t s_listq[kAttnWaves][kList];                              // and INT2 tiles
   __shared__ float2 s_rec[kAttnWaves][kList][kGMax];                           // their raw masses
@@ -547,12 +595,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
   };
 
-  const uint32_t kMaskR = 0x03000300u, kOneR = 0x3C003C00u;   // decode constants
-  f16x8 q4[KK];     // 4q in fp16, formed here so it never shares registers with the bf16 buffers
+  const uint32_t kMaskR = 0x03000300u, kOneR = 0x3C003C00u;   // INT2 decode constants
+  // 2^b q in fp16 (4q for INT2), formed here so it never shares registers
+  // with the bf16 buffers
+  f16x8 q4[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(4.f * float(qb[kk][e]));
+    for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(kCodeScale * float(qb[kk][e]));
   // this lane's slices of the tile constant: q4[jc + i * NREP], zero past KK
   f16x8 q4s[NKK];
 #pragma unroll
@@ -562,17 +612,22 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     for (int kk = 0; kk < KK; ++kk)
       if (jc + i * NREP == kk) q4s[i] = q4[kk];
   }
-  const layout::LedgerTile LT(D);
+  const layout::LedgerTile LT(D, BITS);
   struct QB {
-    uint32_t kc[CW], vc[CW], sc[CW];
+    uint32_t kc[CW], vc[CW], sc[SCW];
   };
-  auto load_words = [&](__amdgpu_buffer_rsrc_t rs, int off, uint32_t (&w)[CW]) {
-    if constexpr (CW == 4) {
-      const uint4 u = load16(rs, off + lane * 16);
-      w[0] = u.x;
-      w[1] = u.y;
-      w[2] = u.z;
-      w[3] = u.w;
+  // a lane's NW consecutive words of an area (16-byte loads, or one 8-byte load)
+  auto load_words = [&](__amdgpu_buffer_rsrc_t rs, int off, auto& w) {
+    constexpr int NW = sizeof(w) / sizeof(uint32_t);
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) {
+        const uint4 u = load16(rs, off + lane * NW * 4 + 16 * i);
+        w[4 * i] = u.x;
+        w[4 * i + 1] = u.y;
+        w[4 * i + 2] = u.z;
+        w[4 * i + 3] = u.w;
+      }
     } else {
       const uint2 u = load8(rs, off + lane * 8);
       w[0] = u.x;
@@ -590,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   uint8_t* scb = s_scb[wid];
   auto compute_q = [&](QB& qq, int t, int rt) {   // record row rt
     // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer
-    if constexpr (CW == 4)
+    if constexpr (SCW == 4)
       reinterpret_cast<uint4*>(scb)[lane] = make_uint4(qq.sc[0], qq.sc[1], qq.sc[2], qq.sc[3]);
     else
       reinterpret_cast<uint2*>(scb)[lane] = make_uint2(qq.sc[0], qq.sc[1]);
@@ -598,11 +653,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     const f16x8* km = reinterpret_cast<const f16x8*>(scb + 2 * D);      // [D]
     const f16x8* vs = reinterpret_cast<const f16x8*>(scb + 4 * D);      // [D/32][32]
     const f16x8* vm = reinterpret_cast<const f16x8*>(scb + 6 * D);
-    // Each lane forms its own B operand: 4 s q as an fp16 product plus its
+    // Each lane forms its own B operand: 2^b s q as an fp16 product plus its
     // exact fp16 residual (fma TwoProduct).  The tile constant
-    // sum_d q (m - 4 s) = sum 4q m / 4 - sum 4q s (fp16 pairs, fp32 sums) is
-    // split over the column groups (group jc takes slices jc, jc + NREP, ..)
-    // and completed across groups and lane rows.
+    // sum_d q (m - 2^b s) = sum 2^b q m / 2^b - sum 2^b q s (fp16 pairs, fp32
+    // sums) is split over the column groups (group jc takes slices jc,
+    // jc + NREP, ..) and completed across groups and lane rows.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     float cm = 0.f, cs = 0.f;
 #pragma unroll
@@ -622,22 +677,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       const f16x8 qh = q4[kk] * s8;
       const f16x8 ql = __builtin_elementwise_fma(q4[kk], s8, -qh);
       const int c0 = kk, c1 = KK + kk;                               // chunks of blk 0 / 1
-      const f16x8 a0 = (c0 & 1) ? decode_codes<1>(qq.kc[c0 >> 1], kMaskR, kOneR)
-                                : decode_codes<0>(qq.kc[c0 >> 1], kMaskR, kOneR);
-      const f16x8 a1 = (c1 & 1) ? decode_codes<1>(qq.kc[c1 >> 1], kMaskR, kOneR)
-                                : decode_codes<0>(qq.kc[c1 >> 1], kMaskR, kOneR);
+      const f16x8 a0 = decode_chunk<BITS>(qq.kc, c0, kMaskR, kOneR);
+      const f16x8 a1 = decode_chunk<BITS>(qq.kc, c1, kMaskR, kOneR);
       s0 = mfma_f16(a0, qh, s0);
       s0 = mfma_f16(a0, ql, s0);
       s1 = mfma_f16(a1, qh, s1);
       s1 = mfma_f16(a1, ql, s1);
     }
     // the MFMA result lanes (g, hn) hold head hh, as the B operand lanes do
-    const float bias0 = sum_rows(sum_groups_t<NREP>(fmaf(cm, 0.25f, -cs)));
+    const float bias0 = sum_rows(sum_groups_t<NREP>(fmaf(cm, 1.f / kCodeScale, -cs)));
     const float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     float p[8], rs;
-    softmax_tile<NB, 2>(st, z, qscale, bias0 * qscale, p, &rs);   // p = 4 x probability
-    // 4p as fp16 high + low parts, then 4 p s' = high*s' + (exact residual
-    // of that product + low*s'), all in packed fp16
+    softmax_tile<NB, BITS>(st, z, qscale, bias0 * qscale, p, &rs);   // p = 2^b x probability
+    // 2^b p as fp16 high + low parts, then 2^b p s' = high*s' + (exact
+    // residual of that product + low*s'), all in packed fp16
     f16x8 p4, p4l;
 #pragma unroll
     for (int e2 = 0; e2 < 8; ++e2) {
@@ -645,13 +698,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       p4[e2] = (_Float16)x;
       p4l[e2] = (_Float16)(x - float(p4[e2]));
     }
-    // v = (m' - 4 s') + (1 + c/4) 4 s'.  The min term, 4 times over:
-    // sum_t 4p m' + sum_t 4p (-4 s'), straight from the fp16 scales (-4 s'
-    // is exact; exact products; row = 32-channel group jr, rows >= D/32
-    // repeat and are not read).
+    // v = (m' - 2^b s') + (1 + c/2^b) 2^b s'.  The min term, 2^b times over:
+    // sum_t 2^b p m' + sum_t 2^b p (-2^b s'), straight from the fp16 scales
+    // (-2^b s' is exact; exact products; row = 32-channel group jr, rows >=
+    // D/32 repeat and are not read).
     {
       const int jr = hn & (D / 32 - 1);
-      const f16x8 vm8 = vm[4 * jr + g], vn8 = vs[4 * jr + g] * (_Float16)(-4.f);
+      const f16x8 vm8 = vm[4 * jr + g], vn8 = vs[4 * jr + g] * (_Float16)(-kCodeScale);
       st.ob = mfma_f16(vm8, p4, st.ob);
       st.ob = mfma_f16(vm8, p4l, st.ob);
       st.ob = mfma_f16(vn8, p4, st.ob);
@@ -666,8 +719,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       const f16x8 pl = __builtin_elementwise_fma(p4l, sv, __builtin_elementwise_fma(p4, sv, -ph));
 #pragma unroll
       for (int nb = 2 * ps * RG; nb < 2 * (ps + 1) * RG; ++nb) {
-        const f16x8 av = (nb & 1) ? decode_codes<1>(qq.vc[nb >> 1], kMaskR, kOneR)
-                                  : decode_codes<0>(qq.vc[nb >> 1], kMaskR, kOneR);
+        const f16x8 av = decode_chunk<BITS>(qq.vc, nb, kMaskR, kOneR);
         st.o[nb] = mfma_f16(av, ph, st.o[nb]);
         st.o[nb] = mfma_f16(av, pl, st.o[nb]);
       }
@@ -677,7 +729,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
 
   if (f_beg < f_end) build_list(TIER_F, f_beg, min(f_end, f_beg + kList), listf);
   if (q_beg < q_end) build_list(TIER_Q, q_beg, min(q_end, q_beg + kList), listq);
-  FB FA;   // the wave's first bf16 tile, in flight while INT2 tiles are decoded
+  // The wave's first bf16 tile, in flight while INT2 tiles are decoded - but
+  // not beside two 8-bit tiles, whose code words leave no room for it.
+  constexpr bool kEarlyF = BITS != 8;
+  FB FA;
   // ---------------------------------------------------------- INT2 tiles
   // two tiles in flight; a buffer is refilled as soon as its tile is consumed
   // (sched_barrier keeps the loads ahead of the next tile's math).  Instanced
@@ -777,13 +832,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   // (head groups of more than four need the registers of their wider B
   // operands: they keep the tiers apart)
   bool mixed = false;
-  if constexpr (GP == 4) {
+  if constexpr (GP == 4 && BITS == 2) {
     const int nq_all = q_end - q_beg, nf_all = f_end - f_beg;
     mixed = nq_all >= kMixedList && nq_all + nf_all <= kList;
     if (mixed) mixed_tiles();
   }
   if (!mixed) {
-    if (f_beg < f_end)
+    if (f_beg < f_end && kEarlyF)
       int2_tiles(std::true_type{});
     else
       int2_tiles(std::false_type{});
@@ -794,7 +849,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     const int ce = min(f_end, cb + kList), nt = ce - cb;
     const int i0 = cb == f_beg ? f_done : 0;   // FA holds tile i0 after the mixed loop
     if (cb != f_beg) build_list(TIER_F, cb, ce, listf);
-    if (cb != f_beg) load_f(FA, 0, nt);   // (else requested among the INT2 tiles)
+    if (cb != f_beg || !kEarlyF) load_f(FA, 0, nt);   // (else requested among the INT2 tiles)
     FB Bf;
     load_f(Bf, i0 + 1, nt);
     __builtin_amdgcn_sched_barrier(0);
@@ -842,7 +897,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
 #pragma unroll
     for (int v = 0; v < kAttnWaves; ++v) {
       const float sc = s_wm[v][h] == -INFINITY ? 0.f : fast_exp2(s_wm[v][h] - M);
-      acc += sc * fmaf(0.25f, s_wb[v][h][d >> 5], s_wo[v][h][d]);   // s_wb: 4 x the min term
+      acc += sc * fmaf(1.f / kCodeScale, s_wb[v][h][d >> 5], s_wo[v][h][d]);   // s_wb: 2^b x the min term
     }
     part[idx] = acc;
   }
@@ -1104,15 +1159,15 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   }
 }
 
-template <int D, int GP>
+template <int D, int GP, int BITS>
 static hipError_t launch_attn_kernel(const PoolView& pv, const AttnArgs& a, size_t shm, hipStream_t s) {
   const uint32_t* pl = pv.pages + size_t(a.layer) * pv.B * pv.maxw;
   const int32_t* tl = pv.tokens + size_t(a.layer) * pv.B;
   if (a.ev_start || a.ev_stop) {
-    hipExtLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
+    hipExtLaunchKernelGGL((attn_kernel<D, GP, BITS>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
                           a.ev_start, a.ev_stop, 0u, pl, tl, pv.maxw, pv, a);
   } else {
-    hipLaunchKernelGGL((attn_kernel<D, GP>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pl, tl, pv.maxw,
+    hipLaunchKernelGGL((attn_kernel<D, GP, BITS>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pl, tl, pv.maxw,
                        pv, a);
   }
   return hipGetLastError();
@@ -1121,7 +1176,13 @@ static hipError_t launch_attn_kernel(const PoolView& pv, const AttnArgs& a, size
 template <int D>
 static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream_t s) {
   const size_t shm = (2 * size_t(a.plan_words) + (pv.nb + 31) / 32) * 4;
-  const hipError_t e = pv.G <= 4 ? launch_attn_kernel<D, 4>(pv, a, shm, s) : launch_attn_kernel<D, 8>(pv, a, shm, s);
+  hipError_t e;
+  if (pv.lbits == 2)
+    e = pv.G <= 4 ? launch_attn_kernel<D, 4, 2>(pv, a, shm, s) : launch_attn_kernel<D, 8, 2>(pv, a, shm, s);
+  else if (pv.lbits == 4)
+    e = pv.G <= 4 ? launch_attn_kernel<D, 4, 4>(pv, a, shm, s) : launch_attn_kernel<D, 8, 4>(pv, a, shm, s);
+  else
+    e = pv.G <= 4 ? launch_attn_kernel<D, 4, 8>(pv, a, shm, s) : launch_attn_kernel<D, 8, 8>(pv, a, shm, s);
   if (e != hipSuccess) return e;
   const int mass_blocks = (a.mass || a.acc_scores) ? (pv.maxw + kMassWindows - 1) / kMassWindows : 0;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(pv.Hkv * (D / 32) + mass_blocks, pv.B), dim3(256),

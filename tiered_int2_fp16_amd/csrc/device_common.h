@@ -24,20 +24,21 @@ __host__ __device__ inline uint32_t pe_make(int tier, bool has_ledger, int bslot
 // Everything a kernel needs to address the pool's arena.
 struct PoolView {
   uint16_t* bf16;     // bf16 window slots
-  uint8_t* ledger;    // INT2 ledger entries
+  uint8_t* ledger;    // ledger entries ((lbits+1)*W*D/4 bytes each)
   uint32_t* pages;    // [segment][max_windows]
   float* scores;      // [segment][max_windows]
   int32_t* tokens;    // [segment]
   int32_t* work;      // work region (int32 units)
   int32_t* err;       // device error word
   int B, L, Hq, Hkv, D, W, maxw, R, nb, nl, G;
+  int lbits;          // ledger code width: 2, 4 or 8
   int work_items, work_counts, attn_counters, seg_counters;  // int32 offsets into work
 
   __device__ uint16_t* block(int seg, int slot, int kvh) const {
     return bf16 + ((size_t(seg) * nb + slot) * Hkv + kvh) * size_t(2 * W * D);
   }
   __device__ uint8_t* entry(int seg, int slot, int kvh) const {
-    return ledger + ((size_t(seg) * nl + slot) * Hkv + kvh) * size_t(3 * W * D / 4);
+    return ledger + ((size_t(seg) * nl + slot) * Hkv + kvh) * (size_t(lbits + 1) * W * D / 4);
   }
 };
 

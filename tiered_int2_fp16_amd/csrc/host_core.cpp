@@ -30,16 +30,19 @@ bool geometry_init(const kv_pool_config& c, Geometry* g, std::string* err) {
     return bad(err, "bf16_slots must be in [1, 16383]");
   if (c.ledger_slots < 0 || c.ledger_slots > kMaxLedgerSlots)
     return bad(err, "ledger_slots must be in [0, 32767]");
+  if (c.ledger_bits != 0 && c.ledger_bits != 2 && c.ledger_bits != 4 && c.ledger_bits != 8)
+    return bad(err, "ledger_bits must be 0 (= 2), 2, 4 or 8");
   const double segs = double(c.batch) * c.layers;
   if (segs > 1e7) return bad(err, "too many segments");
 
   Geometry r;
   r.cfg = c;
+  r.cfg.ledger_bits = c.ledger_bits == 0 ? 2 : c.ledger_bits;
   r.group = grp;
   r.segments = c.batch * c.layers;
   const size_t wd = size_t(c.window) * c.head_dim;
   r.bf16_block = 2 * wd * 2;
-  r.entry = 3 * wd / 4;
+  r.entry = size_t(r.cfg.ledger_bits + 1) * wd / 4;
   const size_t per_seg_heads = size_t(c.kv_heads);
   r.size[KV_REGION_BF16] = size_t(r.segments) * c.bf16_slots * per_seg_heads * r.bf16_block;
   r.size[KV_REGION_LEDGER] = size_t(r.segments) * c.ledger_slots * per_seg_heads * r.entry;
@@ -90,13 +93,14 @@ AttnWorkspace attn_workspace(const Geometry& g, int splits) {
   return w;
 }
 
-void tier_counts(int n, int n_recent, double budget_frac, double hi_frac, int* n_hi, int* n_lo) {
+void tier_counts(int n, int n_recent, double budget_frac, double hi_frac, int ledger_bits, int* n_hi,
+                 int* n_lo) {
   volatile double a = hi_frac * double(n);   // volatile: no contraction across steps
   int hi = std::min(n, std::max(n_recent, int(std::floor(a))));
   volatile double b = budget_frac * double(n);
   volatile double c = b - double(hi);
   volatile double d = c * 16.0;
-  volatile double e = d / 3.0;
+  volatile double e = d / double(ledger_bits + 1);
   int lo = std::max(0, std::min(n - hi, int(std::floor(e))));
   *n_hi = hi;
   *n_lo = lo;

@@ -10,7 +10,7 @@
 
 namespace kvtier {
 
-constexpr int kTile = 32;            // tokens per attention tile = INT2 group length
+constexpr int kTile = 32;            // tokens per attention tile = ledger group length
 constexpr int kMaxWindows = 4096;    // page-table entries per segment (LDS bound)
 constexpr int kMaxTiles = 8192;      // 32-token tiles per segment (LDS bound)
 constexpr int kMaxBf16Slots = 16383; // 14-bit slot field
@@ -19,11 +19,11 @@ constexpr int kAttnThreads = 256;    // 4 wave64 per attention workgroup
 constexpr int kAttnWaves = kAttnThreads / 64;
 
 struct Geometry {
-  kv_pool_config cfg{};
+  kv_pool_config cfg{};       // ledger_bits normalised: 2, 4 or 8
   int group = 0;              // q heads per kv head
   int segments = 0;           // layers * batch
   size_t bf16_block = 0;      // bytes of one (slot, kv head) bf16 block: K+V
-  size_t entry = 0;           // bytes of one (slot, kv head) ledger entry
+  size_t entry = 0;           // bytes of one (slot, kv head) ledger entry: (b+1)*W*D/4
   size_t off[KV_REGION_COUNT]{};
   size_t size[KV_REGION_COUNT]{};
   size_t total = 0;
@@ -51,9 +51,11 @@ struct AttnWorkspace {
 };
 AttnWorkspace attn_workspace(const Geometry& g, int splits);
 
-// Tier counts of a segment with n windows (the router's formula; double
-// precision, evaluated in the documented order).
-void tier_counts(int n, int n_recent, double budget_frac, double hi_frac, int* n_hi, int* n_lo);
+// Tier counts of a segment with n windows and a ledger of ledger_bits-bit
+// codes (the router's formula; double precision, evaluated in the documented
+// order).
+void tier_counts(int n, int n_recent, double budget_frac, double hi_frac, int ledger_bits, int* n_hi,
+                 int* n_lo);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

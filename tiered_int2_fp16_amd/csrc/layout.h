@@ -1,4 +1,4 @@
-// Physical layouts of bf16 windows and INT2 ledger entries.
+// Physical layouts of bf16 windows and b-bit (2, 4, 8) ledger entries.
 //
 // Both are built around one wave64 matrix-core operand shape (16x16x32 MFMA on
 // gfx950): lane l of a wave holds 8 consecutive values of row l%16 at column
@@ -17,14 +17,22 @@
 //   K part (32*D): chunk (cmb, lane), cmb = blk*(D/32) + kk, holds
 //                  K[qk_token(blk, lane%16)][32*kk + 8*(lane/16) + e], e = 0..7
 //   V part (32*D): chunk (nb, lane) holds V[8*(lane/16) + e][16*nb + lane%16]
-// INT2 ledger entry (per slot, per kv head): W/32 tiles of 24*D bytes, each
-//   Kc (8*D B) | Vc (8*D B) | Ks (2*D B) | Km (2*D B) | Vs (2*D B) | Vm (2*D B)
-//   Kc, Vc: lane l owns D/8 bytes = D/32 little-endian 32-bit words; word w
-//     carries the codes of chunks cmb = 2w (sel 0) and 2w+1 (sel 1); within the
-//     word, field f (bits 2f..2f+1) is element e = 2*(f%4) + f/8 of chunk
-//     2w + (f/4)%2.  Chunk numbering is that of the bf16 tile (K: cmb, V: nb).
-//     Fields (r + 4*sel, r + 4*sel + 8) sit 16 bits apart, so one shift and one
-//     mask place a pair of codes as the two halves of a 32-bit register.
+// Ledger entry of b-bit codes (per slot, per kv head): W/32 tiles of
+// 8*(b+1)*D bytes, each
+//   Kc (4*b*D B) | Vc (4*b*D B) | Ks (2*D B) | Km (2*D B) | Vs (2*D B) | Vm (2*D B)
+//   Kc, Vc: lane l owns b*D/16 bytes = b*D/64 little-endian 32-bit words; the
+//   8 codes of a chunk go where one or two register operations turn a pair
+//   of them into the two fp16 halves of a 32-bit register:
+//   b = 2: word w carries the codes of chunks cmb = 2w (sel 0) and 2w+1
+//     (sel 1); field f (bits 2f..2f+1) is element e = 2*(f%4) + f/8 of chunk
+//     2w + (f/4)%2.  Fields (r + 4*sel, r + 4*sel + 8) sit 16 bits apart, so
+//     one shift and one mask place a pair of codes in the two halves.
+//   b = 4: word w is chunk w; field f (bits 4f..4f+3) is element
+//     e = 2*(f%4) + f/4 (fields r and r + 4, 16 bits apart, are elements 2r
+//     and 2r + 1).
+//   b = 8: words 2c and 2c+1 are chunk c; byte e of that pair is element e
+//     (a byte permute spreads elements 2r, 2r + 1 over the two halves).
+//   Chunk numbering is that of the bf16 tile (K: cmb, V: nb).
 //   Ks, Km: fp16 [D] scale / min of the tile's K group of each channel.
 //   Vs, Vm: fp16 [D/32][32] scale / min of each token's V group j (channels
 //     32j..32j+31), indexed [j][token].
@@ -78,29 +86,52 @@ KV_HD void field_elem(int w, int f, int* cmb, int* e) {
   *e = 2 * (f & 3) + (f >> 3);
 }
 
-// ---- ledger tile: byte offsets within one 24*D-byte tile
+// element e of field f of code word w (b-bit codes): its chunk and element
+KV_HD void field_elem_b(int bits, int w, int f, int* cmb, int* e) {
+  if (bits == 2) {
+    field_elem(w, f, cmb, e);
+  } else if (bits == 4) {
+    *cmb = w;
+    *e = 2 * (f & 3) + (f >> 2);
+  } else {
+    *cmb = w >> 1;
+    *e = 4 * (w & 1) + f;
+  }
+}
+
+// ---- ledger tile: byte offsets within one 8*(b+1)*D-byte tile
 struct LedgerTile {
   int kc, vc, ks, km, vs, vm, bytes;
-  KV_HD explicit LedgerTile(int D)
-      : kc(0), vc(8 * D), ks(16 * D), km(18 * D), vs(20 * D), vm(22 * D), bytes(24 * D) {}
+  KV_HD LedgerTile(int D, int bits)
+      : kc(0), vc(4 * bits * D), ks(8 * bits * D), km(8 * bits * D + 2 * D), vs(8 * bits * D + 4 * D),
+        vm(8 * bits * D + 6 * D), bytes(8 * (bits + 1) * D) {}
 };
 
 // Code position of a chunk element: byte offset of its 32-bit word within the
 // Kc (or Vc) area of the tile, and its bit position inside that word.
-KV_HD void code_pos(int cmb, int lane, int e, int D, int* word_byte, int* bit) {
-  const int w = cmb >> 1, sel = cmb & 1;
-  const int f = (e >> 1) + 4 * sel + 8 * (e & 1);
-  *word_byte = lane * (D / 8) + 4 * w;
-  *bit = 2 * f;
+KV_HD void code_pos(int cmb, int lane, int e, int D, int bits, int* word_byte, int* bit) {
+  const int lane_bytes = bits * D / 16;
+  if (bits == 2) {
+    const int w = cmb >> 1, sel = cmb & 1;
+    const int f = (e >> 1) + 4 * sel + 8 * (e & 1);
+    *word_byte = lane * lane_bytes + 4 * w;
+    *bit = 2 * f;
+  } else if (bits == 4) {
+    *word_byte = lane * lane_bytes + 4 * cmb;
+    *bit = 4 * ((e >> 1) + 4 * (e & 1));
+  } else {
+    *word_byte = lane * lane_bytes + 4 * (2 * cmb + (e >> 2));
+    *bit = 8 * (e & 3);
+  }
 }
 // K code of (token t of the tile, dim d)
-KV_HD void k_code_pos(int t, int d, int D, int* word_byte, int* bit) {
+KV_HD void k_code_pos(int t, int d, int D, int bits, int* word_byte, int* bit) {
   const int blk = (t >> 2) & 1, m = 4 * (t >> 3) + (t & 3);
-  code_pos(blk * (D >> 5) + (d >> 5), 16 * ((d >> 3) & 3) + m, d & 7, D, word_byte, bit);
+  code_pos(blk * (D >> 5) + (d >> 5), 16 * ((d >> 3) & 3) + m, d & 7, D, bits, word_byte, bit);
 }
 // V code of (token t of the tile, dim d)
-KV_HD void v_code_pos(int t, int d, int D, int* word_byte, int* bit) {
-  code_pos(d >> 4, 16 * (t >> 3) + (d & 15), t & 7, D, word_byte, bit);
+KV_HD void v_code_pos(int t, int d, int D, int bits, int* word_byte, int* bit) {
+  code_pos(d >> 4, 16 * (t >> 3) + (d & 15), t & 7, D, bits, word_byte, bit);
 }
 
 }  // namespace layout

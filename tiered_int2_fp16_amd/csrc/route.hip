@@ -2,16 +2,17 @@
 //
 // QEvict technical summary: window importance is the attention score
 // accumulated over time ("Kernmechanismen", cumulative scoring); windows are
-// routed among full precision, recoverable INT2 and evicted within a fixed
+// routed among full precision, the recoverable low-bit tier and evicted within a fixed
 // byte budget ("Methodologie: QEvict"; "Kernbijdragen" item 2); evicted
 // windows are gone for good.
 //
 // Readings where the pages are silent: the R newest windows always stay bf16;
 // tier counts come from the budget as
 //   n_hi = min(n, max(R, floor(phi*n))),
-//   n_lo = max(0, min(n - n_hi, floor((beta*n - n_hi)*16/3)))
-// in double precision in that order (16/3 = bf16 bytes over INT2 bytes of a
-// window); ranking is score descending, then window index ascending.
+//   n_lo = max(0, min(n - n_hi, floor((beta*n - n_hi)*16/(b+1))))
+// in double precision in that order (16/(b+1) = bf16 bytes over the bytes of
+// a window's b-bit ledger entry, 16/3 for INT2); ranking is score descending,
+// then window index ascending.
 #include "launch.h"
 
 namespace kvtier {
@@ -41,12 +42,12 @@ __global__ __launch_bounds__(256) void score_kernel(PoolView pv, int layer, cons
 
 // Tier counts, IEEE double in the documented order (explicit roundings: no
 // contraction into fused multiply-adds).
-__device__ inline void device_tier_counts(int n, int R, double beta, double phi, int* hi, int* lo) {
+__device__ inline void device_tier_counts(int n, int R, int lbits, double beta, double phi, int* hi, int* lo) {
   const double a = __dmul_rn(phi, double(n));
   int h = int(floor(a));
   h = h > R ? h : R;
   h = h < n ? h : n;
-  const double x = __ddiv_rn(__dmul_rn(__dsub_rn(__dmul_rn(beta, double(n)), double(h)), 16.0), 3.0);
+  const double x = __ddiv_rn(__dmul_rn(__dsub_rn(__dmul_rn(beta, double(n)), double(h)), 16.0), double(lbits + 1));
   int l = int(floor(x));
   l = l < n - h ? l : n - h;
   l = l > 0 ? l : 0;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
   const int n = windows_of(len, pv.W);
   const int fr = n - pv.R > 0 ? n - pv.R : 0;  // first recent window
   int n_hi, n_lo;
-  device_tier_counts(n, pv.R, beta, phi, &n_hi, &n_lo);
+  device_tier_counts(n, pv.R, pv.lbits, beta, phi, &n_hi, &n_lo);
   int nf = n_hi - (n - fr);
   nf = nf > 0 ? nf : 0;
   uint32_t* gp = pv.pages + size_t(seg) * maxw;

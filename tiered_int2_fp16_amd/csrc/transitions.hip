@@ -1,5 +1,6 @@
-// Window transitions for gfx950: prefill, demote (INT2 quantise into the
-// write-once ledger), promote (dequantise back to bf16), canonical read-back.
+// Window transitions for gfx950: prefill, demote (b-bit quantise into the
+// write-once ledger, b = 2, 4 or 8), promote (dequantise back to bf16),
+// canonical read-back.
 //
 // QEvict technical summary, "Kernmechanismen": a bf16 window whose importance
 // drops is demoted to the quantised tier; a quantised window whose cumulative
@@ -71,12 +72,15 @@ hipError_t launch_prefill(const PoolView& pv, int layer, const uint16_t* k, cons
 }
 
 // -------------------------------------------------------------- the codec
-// One group of 32 values: asymmetric min/max INT2.  Signed zeros are made +0,
-// s = fp16((max - min) / 3), m = fp16(min); codes use the stored fp16 values:
-// c = clamp(rint_even((x - m) / s), 0, 3), or 0 when s == 0.  float32 IEEE
-// arithmetic throughout (correctly rounded divide, no contraction).
+// One group of 32 values: asymmetric min/max with L = 2^b - 1 levels.
+// Signed zeros are made +0, s = fp16((max - min) / L), m = fp16(min); codes
+// use the stored fp16 values: c = clamp(rint_even((x - m) / s), 0, L), or 0
+// when s == 0.  float32 IEEE arithmetic throughout (correctly rounded divide,
+// no contraction).
+template <int BITS>
 __device__ inline void quant_group(const float* xp, int xstride, uint8_t* cp, int cstride, uint16_t* s_out,
                                    uint16_t* m_out) {
+  constexpr float kTop = float((1 << BITS) - 1);
   float x[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -90,30 +94,31 @@ __device__ inline void quant_group(const float* xp, int xstride, uint8_t* cp, in
     mx = fmaxf(mx, x[i]);
   }
   const float d = mx - mn;
-  const float s32 = __fdiv_rn(d, 3.0f);
+  const float s32 = __fdiv_rn(d, kTop);
   const _Float16 hs = (_Float16)s32;
   const _Float16 hm = (_Float16)mn;
   const float s = (float)hs, m = (float)hm;
-  // rint(fl(u / s)) from u * rcp(s).  Only the ties 1/2, 3/2, 5/2 decide a
-  // code (the clamp absorbs the rest), and near them the two quotients
-  // differ by under 1e-6, so the codes agree unless a quotient lies within
-  // 1e-5 of some k + 1/2: such values are redone with the exact division in
-  // a separate, rolled loop (it runs rarely; kept out of line, its code is
-  // not fetched with the common path).
+  // rint(fl(u / s)) from u * rcp(s).  Only the ties k + 1/2 (k < L) decide
+  // a code (the clamp absorbs the rest), and the two quotients differ by
+  // under 2e-7 relative (rcp within one ulp, one rounding of the product),
+  // so the codes agree unless a quotient r lies within 1e-5 * (1 + r) of
+  // some k + 1/2: such values are redone with the exact division in a
+  // separate, rolled loop (it runs rarely; kept out of line, its code is not
+  // fetched with the common path).
   const float rcp = s == 0.f ? 0.f : __builtin_amdgcn_rcpf(s);
   uint32_t near = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const float r = (x[i] - m) * rcp;
-    near |= uint32_t(s != 0.f && fabsf(r - floorf(r) - 0.5f) < 1e-5f) << i;
-    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(r), 0.f), 3.f));
+    near |= uint32_t(s != 0.f && fabsf(r - floorf(r) - 0.5f) < 1e-5f * (1.f + fabsf(r))) << i;
+    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(r), 0.f), kTop));
   }
   while (near) {
     const int i = __builtin_ctz(near);
     near &= near - 1;
     const float v = xp[i * xstride];
     const float u = ((v == 0.f) ? 0.f : v) - m;
-    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(__fdiv_rn(u, s)), 0.f), 3.f));
+    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(__fdiv_rn(u, s)), 0.f), kTop));
   }
   *s_out = __builtin_bit_cast(uint16_t, hs);
   *m_out = __builtin_bit_cast(uint16_t, hm);
@@ -240,15 +245,15 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 // Demote data kernel: quantise one tile of a bf16 window into its ledger
 // entry.  K groups are the tile's channels (32 tokens each), V groups each
 // token's 32-channel blocks.
-// (D, the head dimension, is a template parameter: the chunk and field index
-// arithmetic below then reduces to shifts and masks)
-template <int D>
+// (D, the head dimension, and BITS, the code width, are template parameters:
+// the chunk and field index arithmetic below then reduces to shifts and masks)
+template <int D, int BITS>
 __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
   __shared__ float xs[2][32][129];          // K, V of one tile, canonical [token][dim]
   __shared__ uint8_t cs[2][32][132];        // their codes (rows padded: no bank conflicts)
   const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
   const int seg = layer * pv.B + b;
-  const layout::LedgerTile LT(D);
+  const layout::LedgerTile LT(D, BITS);
   const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
   // the first unit's work item is read together with the count (the item
   // list always has room for it; it is used only if the count covers it)
@@ -290,29 +295,31 @@ __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
     uint16_t* vm = reinterpret_cast<uint16_t*>(et + LT.vm);
     for (int g = tid; g < D + D; g += blockDim.x) {
       if (g < D)   // K group: channel g over the tile's 32 tokens
-        quant_group(&xs[0][0][g], 129, &cs[0][0][g], 132, ks + g, km + g);
+        quant_group<BITS>(&xs[0][0][g], 129, &cs[0][0][g], 132, ks + g, km + g);
       else {       // V group: token t, channels 32j..32j+31
         const int t = (g - D) / (D / 32), j = (g - D) % (D / 32);
-        quant_group(&xs[1][t][32 * j], 1, &cs[1][t][32 * j], 1, vs + j * 32 + t, vm + j * 32 + t);
+        quant_group<BITS>(&xs[1][t][32 * j], 1, &cs[1][t][32 * j], 1, vs + j * 32 + t, vm + j * 32 + t);
       }
     }
     __syncthreads();
-    // pack: one 32-bit code word per thread step (64 lanes x D/32 words per part)
-    const int words = 64 * (D / 32);
+    // pack: one 32-bit code word per thread step (64 lanes x BITS*D/64 words
+    // per part, 32/BITS fields per word)
+    constexpr int CWB = BITS * D / 64;
+    constexpr int words = 64 * CWB;
     for (int x = tid; x < 2 * words; x += blockDim.x) {
       const bool is_v = x >= words;
       const int q = is_v ? x - words : x;
-      const int lane = q / (D / 32), w = q % (D / 32);
+      const int lane = q / CWB, w = q % CWB;
       uint32_t word = 0;
 #pragma unroll
-      for (int f = 0; f < 16; ++f) {
+      for (int f = 0; f < 32 / BITS; ++f) {
         int cmb, e, t, d;
-        layout::field_elem(w, f, &cmb, &e);
+        layout::field_elem_b(BITS, w, f, &cmb, &e);
         if (is_v) layout::v_chunk_elem(cmb, lane, e, &t, &d);
         else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
-        word |= uint32_t(cs[is_v][t][d]) << (2 * f);
+        word |= uint32_t(cs[is_v][t][d]) << (BITS * f);
       }
-      reinterpret_cast<uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + w] = word;
+      reinterpret_cast<uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * CWB + w] = word;
     }
     __syncthreads();
   }
@@ -320,14 +327,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
 
 // Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of one tile.
 // A ledger chunk (lane, cmb) and the bf16 chunk (cmb, lane) hold the same 8
-// values, so each thread step turns one code half-word into one 16-byte chunk;
-// the tile's scale block is staged in LDS first.
-template <int D>
+// values, so each thread step turns one chunk's codes (one or two code words)
+// into one 16-byte chunk; the tile's scale block is staged in LDS first.
+template <int D, int BITS>
 __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
   __shared__ uint4 s_sc[64];   // Ks | Km | Vs | Vm of one tile (8 D bytes, D <= 128)
   const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
   const int seg = layer * pv.B + b;
-  const layout::LedgerTile LT(D);
+  const layout::LedgerTile LT(D, BITS);
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
   const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
   // the first unit's work item is read together with the count (used only if
   // the count covers it)
@@ -347,14 +355,18 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
     // code word of each of this thread's chunks
     if (tid < D / 2) s_sc[tid] = reinterpret_cast<const uint4*>(et + LT.ks)[tid];
     constexpr int kMaxChunks = 4;   // 8 * D / 256 for D <= 128
-    uint32_t words[kMaxChunks];
+    uint32_t words[kMaxChunks], words_hi[kMaxChunks];   // a chunk's code words (8 bits: two)
 #pragma unroll
     for (int j = 0; j < kMaxChunks; ++j) {
       const int c = tid + j * 256;
       if (c < 8 * D) {
         const bool is_v = c >= 4 * D;
         const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
-        words[j] = reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * (D / 32) + (cmb >> 1)];
+        int wb, bit;
+        layout::code_pos(cmb, lane, 0, D, BITS, &wb, &bit);
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc) + wb);
+        words[j] = cw[0];
+        words_hi[j] = BITS == 8 ? cw[1] : 0u;
       }
     }
     __syncthreads();
@@ -364,7 +376,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
       if (c >= 8 * D) break;
       const bool is_v = c >= 4 * D;
       const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
-      const uint32_t word = words[j];
       uint32_t out[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -372,8 +383,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e = 2 * e2 + h;
-          const int f = e2 + 4 * (cmb & 1) + 8 * h;
-          const float code = float((word >> (2 * f)) & 3u);
+          int wb, bit;
+          layout::code_pos(cmb, lane, e, D, BITS, &wb, &bit);
+          const uint32_t word = (BITS == 8 && e >= 4) ? words_hi[j] : words[j];
+          const float code = float((word >> bit) & kMask);
           int t, d;
           float sc, mn;
           if (is_v) {
@@ -410,12 +423,15 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   long gx = (1024 + pv.B - 1) / pv.B;
   if (gx > max_units) gx = max_units;
   if (gx < 1) gx = 1;
-  if (promote)
-    hipLaunchKernelGGL(pv.D == 64 ? dequant_kernel<64> : dequant_kernel<128>, dim3(unsigned(gx), pv.B), dim3(256),
-                       0, s, pv, layer);
-  else
-    hipLaunchKernelGGL(pv.D == 64 ? quantize_kernel<64> : quantize_kernel<128>, dim3(unsigned(gx), pv.B),
-                       dim3(256), 0, s, pv, layer);
+  const int wi = pv.lbits == 2 ? 0 : (pv.lbits == 4 ? 1 : 2);
+  const int di = pv.D == 64 ? 0 : 1;
+  typedef void (*Kern)(PoolView, int);
+  static const Kern kDequant[2][3] = {{dequant_kernel<64, 2>, dequant_kernel<64, 4>, dequant_kernel<64, 8>},
+                                      {dequant_kernel<128, 2>, dequant_kernel<128, 4>, dequant_kernel<128, 8>}};
+  static const Kern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
+                                    {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
+  hipLaunchKernelGGL(promote ? kDequant[di][wi] : kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv,
+                     layer);
   return hipGetLastError();
 }
 
@@ -431,15 +447,16 @@ hipError_t launch_promote(const PoolView& pv, int layer, const int32_t* items, i
 
 // ---------------------------------------------------------------- read-back
 // Canonical copies for inspection: bf16 K then V [kv_head][2][W][D]; ledger
-// entries as Kc, Vc [W][D/4] (code of (t, d) in byte d/4, bits 2*(d%4)), Ks,
-// Km fp16 [W/32][D], Vs, Vm fp16 [W][D/32].
+// entries as Kc, Vc [W][D*b/8] (b-bit code of (t, d) in byte d*b/8, bits
+// (d*b)%8 .. +b-1), Ks, Km fp16 [W/32][D], Vs, Vm fp16 [W][D/32].
 __global__ __launch_bounds__(256) void read_kernel(PoolView pv, int layer, int b, int w, int ledger,
                                                    uint8_t* dst) {
   const int seg = layer * pv.B + b, W = pv.W, D = pv.D;
   const uint32_t e = (w >= 0 && w < pv.maxw) ? pv.pages[size_t(seg) * pv.maxw + w] : 0u;
   const bool ok = ledger ? (pe_tier(e) != TIER_E && pe_has_ledger(e)) : (pe_tier(e) == TIER_F);
   if (!ok && threadIdx.x == 0) set_err(pv.err, KV_ERR_READ_MISSING);
-  const layout::LedgerTile LT(D);
+  const int BITS = pv.lbits, per = 8 / BITS, row = D * BITS / 8;   // codes per byte, bytes per row
+  const layout::LedgerTile LT(D, BITS);
   for (int kvh = 0; kvh < pv.Hkv; ++kvh) {
     if (!ledger) {
       uint16_t* out = reinterpret_cast<uint16_t*>(dst) + size_t(kvh) * 2 * W * D;
@@ -450,26 +467,26 @@ __global__ __launch_bounds__(256) void read_kernel(PoolView pv, int layer, int b
         out[W * D + x] = ok ? blk[layout::bf16_window_v(t, d, D)] : uint16_t(0);
       }
     } else {
-      uint8_t* out = dst + size_t(kvh) * (3 * W * D / 4);
+      uint8_t* out = dst + size_t(kvh) * (size_t(BITS + 1) * W * D / 4);
       const uint8_t* E = ok ? pv.entry(seg, pe_lslot(e), kvh) : nullptr;
       uint8_t* kc = out;
-      uint8_t* vc = out + W * D / 4;
-      uint16_t* ks = reinterpret_cast<uint16_t*>(out + W * D / 2);
+      uint8_t* vc = out + W * row;
+      uint16_t* ks = reinterpret_cast<uint16_t*>(out + 2 * W * row);
       uint16_t* km = ks + (W / 32) * D;
       uint16_t* vs = km + (W / 32) * D;
       uint16_t* vm = vs + W * (D / 32);
-      for (int x = threadIdx.x; x < W * D / 4; x += blockDim.x) {
-        const int t = x / (D / 4), d0 = 4 * (x % (D / 4));
+      const uint32_t mask = (1u << BITS) - 1u;
+      for (int x = threadIdx.x; x < W * row; x += blockDim.x) {
+        const int t = x / row, d0 = per * (x % row);
         uint32_t kb = 0, vb = 0;
         if (ok) {
           const uint8_t* et = E + size_t(t / 32) * LT.bytes;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
+          for (int q = 0; q < per; ++q) {
             int wb, bit;
-            layout::k_code_pos(t % 32, d0 + q, D, &wb, &bit);
-            kb |= ((*reinterpret_cast<const uint32_t*>(et + LT.kc + wb) >> bit) & 3u) << (2 * q);
-            layout::v_code_pos(t % 32, d0 + q, D, &wb, &bit);
-            vb |= ((*reinterpret_cast<const uint32_t*>(et + LT.vc + wb) >> bit) & 3u) << (2 * q);
+            layout::k_code_pos(t % 32, d0 + q, D, BITS, &wb, &bit);
+            kb |= ((*reinterpret_cast<const uint32_t*>(et + LT.kc + wb) >> bit) & mask) << (BITS * q);
+            layout::v_code_pos(t % 32, d0 + q, D, BITS, &wb, &bit);
+            vb |= ((*reinterpret_cast<const uint32_t*>(et + LT.vc + wb) >> bit) & mask) << (BITS * q);
           }
         }
         kc[x] = uint8_t(kb);
