@@ -111,3 +111,39 @@ def test_head_group_shapes(name, seed, hq, hkv, d, w, bits):
             p.route(0, c.budget_frac, c.hi_frac)
             p.check_state(0)
     log("%s, %d-bit ledger: out err %.2e mass err %.2e" % (name, bits, *worst))
+
+
+@pytest.mark.parametrize("bits,n_lo", [(4, 24), (8, 13)])
+def test_qwen_32k(bits, n_lo):
+    """The Qwen2.5-7B shape (batch 8, groups of 7 query heads, 4 K outlier
+    channels x10) at a 5 % budget: 5 bf16 windows per sequence and the ledger
+    windows the rest buys at b + 1 bits per value; one step, every output."""
+    c = CONFIGS["qwen7b_32k"]
+    p = Pair(c, bits=bits)
+    p.load(0)
+    _, cnt = p.route(0, c.budget_frac, c.hi_frac)
+    assert (cnt[0] == n_lo).all() and (cnt[2] == c.n_windows - 5 - n_lo).all()
+    p.check_state(0, ledger_sample=6, window_sample=3, rng=np.random.default_rng(10 + bits))
+    _, _, _, errs = p.step(0, 0)
+    log("qwen 32K, %d-bit ledger: out err %.2e mass err %.2e" % (bits, *errs))
+
+
+@pytest.mark.timeout(900)
+def test_llama_128k_loop_4bit_sampled():
+    """The 128K loop shape with a 4-bit ledger (102 bf16 / 328 ledger windows
+    per sequence): 17 decode steps appending a token each (the first opens
+    window 1024), scores every step, routing after step 16; two of the four
+    sequences compared in full against the oracle."""
+    c = CONFIGS["llama8b_128k_loop"]
+    p = Pair(c, seqs=[1, 2], bits=4)
+    p.load(0)
+    _, cnt = p.route(0, c.budget_frac, c.hi_frac)
+    assert (cnt[0] == 328).all()
+    p.check_state(0, ledger_sample=8, window_sample=4, rng=np.random.default_rng(14))
+    for s in range(17):
+        _, mass, o_mass, errs = p.step(0, s, append=True)
+        p.add_scores(0, mass, o_mass)
+        log("128K 4-bit step %d: out err %.2e mass err %.2e" % (s, *errs))
+        if (s + 1) % c.route_every == 0:
+            p.route(0, c.budget_frac, c.hi_frac)
+            p.check_state(0, ledger_sample=8, window_sample=4, rng=np.random.default_rng(15))
