@@ -144,11 +144,17 @@ __device__ inline uint2 load8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// (m & y) | (~m & c) in one instruction (v_bfi_b32)
-__device__ inline uint32_t bit_select(uint32_t m, uint32_t y, uint32_t c) {
-  uint32_t r;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(y), "v"(c));
-  return r;
+// (m & y) | (~m & c): one v_bfi_b32 when m and c sit in VGPRs the optimiser
+// cannot see into (see opaque()).  Written as plain operations, not inline
+// assembly: the compiler then knows the instruction's VGPR write and inserts
+// the wait states a matrix-core read of the result needs.
+__device__ inline uint32_t bit_select(uint32_t m, uint32_t y, uint32_t c) { return (m & y) | (~m & c); }
+// x in a VGPR, its value hidden from constant folding (no instruction is
+// emitted): two constants of a bit select stay register operands of one
+// instruction instead of being folded into two literal operations.
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Eight INT2 codes of one operand chunk -> fp16 (1 + c/4).  Word X holds the
@@ -171,13 +177,14 @@ __device__ inline f16x8 decode_codes(uint32_t X, uint32_t mask, uint32_t one) {
 // Eight 4-bit codes of one chunk (word X, field f = element 2(f%4) + f/4)
 // -> fp16 (1 + c/16): register j takes fields j and j + 4, 16 bits apart; one
 // shift puts both at mantissa bits 6-9, a bit select adds the exponent of 1.0.
-__device__ inline f16x8 decode_codes4(uint32_t X) {
+// `mask` = 0x03C003C0 and `one` = 0x3C003C00 come in registers.
+__device__ inline f16x8 decode_codes4(uint32_t X, uint32_t mask, uint32_t one) {
   uint32_t r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int sh = 4 * j;
     const uint32_t y = sh <= 6 ? (X << (6 - sh)) : (X >> (sh - 6));
-    r[j] = bit_select(0x03C003C0u, y, 0x3C003C00u);
+    r[j] = bit_select(mask, y, one);
   }
   return __builtin_bit_cast(f16x8, make_uint4(r[0], r[1], r[2], r[3]));
 }
@@ -203,7 +210,7 @@ __device__ inline f16x8 decode_chunk(const uint32_t (&w)[CW], int c, uint32_t ma
   if constexpr (BITS == 2)
     return (c & 1) ? decode_codes<1>(w[c >> 1], mask, one) : decode_codes<0>(w[c >> 1], mask, one);
   else if constexpr (BITS == 4)
-    return decode_codes4(w[c]);
+    return decode_codes4(w[c], mask, one);
   else
     return decode_codes8(w[2 * c], w[2 * c + 1]);
 }
@@ -324,18 +331,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   // ------------------------------------------------------------ the query
   // issued first: it does not depend on the plan.  Lane (g, hn) holds channels
   // 32kk + 8g .. 32kk + 8g + 7 of head hh: the B operand of the QK products.
+  // Buffer loads without a branch (lanes of heads past G read zeros), so the
+  // plan's wait for the page table is exact and does not wait for the query,
+  // whose address comes later (from the kernel arguments in memory).
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e / sqrtf(float(D));
   bf16x8 qb[KK];    // q (bf16)
   {
-    const uint16_t* qp = a.q + (size_t(b) * pv.Hq + size_t(kvh) * G + hh) * D + 8 * g;
+    const auto rq = tile_rsrc(a.q + (size_t(b) * pv.Hq + size_t(kvh) * G) * D, G * D * 2);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (hh < G) u = *reinterpret_cast<const uint4*>(qp + 32 * kk);
-      qb[kk] = as_bf16x8(u);
-    }
+    for (int kk = 0; kk < KK; ++kk) qb[kk] = as_bf16x8(load16(rq, boff(hh < G, (hh * D + 32 * kk + 8 * g) * 2)));
   }
+  __builtin_amdgcn_sched_barrier(0);   // the page table, token count and query loads stay in this order
 
   // ------------------------------------------------ tile plan (workgroup)
   // The page table goes to LDS once per workgroup: thread t takes windows
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     auto stage = [&](const uint32_t (&e4)[4], int j0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (j0 + j < JR) {
+        if ((j0 == 0 && j == 0) || j0 + j < JR) {   // JR >= 1: the first group always stages
           const int w = 256 * (j0 + j) + tid;
           const int c = tiles_of(e4[j], w);
           const int incl = wave_incl_scan(c);
@@ -595,23 +602,27 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     if (rec_mass) rec[t][hn] = make_float2(rs, st.m_run);
   };
 
-  const uint32_t kMaskR = 0x03000300u, kOneR = 0x3C003C00u;   // INT2 decode constants
-  // 2^b q in fp16 (4q for INT2), formed here so it never shares registers
-  // with the bf16 buffers
+  // decode constants (mask of a code pair's fields, exponent of 1.0), held in
+  // VGPRs for the bit selects
+  const uint32_t kMaskR = opaque(BITS == 2 ? 0x03000300u : 0x03C003C0u), kOneR = opaque(0x3C003C00u);
+  // 2^b q in fp16 (4q for INT2) and this lane's slices of the tile constant
+  // (q4[jc + i * NREP], zero past KK); formed once the wave's first tile loads
+  // are out, so the wait for the query never holds them back
   f16x8 q4[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(kCodeScale * float(qb[kk][e]));
-  // this lane's slices of the tile constant: q4[jc + i * NREP], zero past KK
   f16x8 q4s[NKK];
-#pragma unroll
-  for (int i = 0; i < NKK; ++i) {
-    q4s[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  auto make_q4 = [&]() {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      if (jc + i * NREP == kk) q4s[i] = q4[kk];
-  }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q4[kk][e] = (_Float16)(kCodeScale * float(qb[kk][e]));
+#pragma unroll
+    for (int i = 0; i < NKK; ++i) {
+      q4s[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        if (jc + i * NREP == kk) q4s[i] = q4[kk];
+    }
+  };
   const layout::LedgerTile LT(D, BITS);
   struct QB {
     uint32_t kc[CW], vc[CW], sc[SCW];
@@ -743,6 +754,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     QB A, Bq;
     load_q(A, 0, nt);
     load_q(Bq, 1, nt);
+    __builtin_amdgcn_sched_barrier(0);
+    make_q4();
     int i0 = 0;
     if constexpr (decltype(early_f)::value) {
       // The bf16 tile is requested once the first INT2 tile is in: all waves'
@@ -803,6 +816,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     __builtin_amdgcn_sched_barrier(0);
     load_f(FA, 0, nf);
     __builtin_amdgcn_sched_barrier(0);
+    make_q4();
     // whole groups of four (the tiles past the end load nothing and are not
     // computed): the loop has no early exit, so every path into its head has
     // the same loads in flight in the same order
@@ -943,6 +957,16 @@ __device__ inline float2 head_mz(float m0, float l0, float m1, float l1) {
   return make_float2(M, z);
 }
 
+// Materialise uniform values (kernel arguments) in SGPRs at this point.
+template <typename T>
+__device__ inline void in_sgpr(const T& x) {
+  asm volatile("" ::"s"(x));
+}
+template <typename... T>
+__device__ inline void in_sgprs(const T&... x) {
+  (in_sgpr(x), ...);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, int acc_scores) {
   constexpr int kSlice = 32, NO = D / kSlice;
@@ -952,16 +976,38 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   __shared__ int s_win[kMassWindows];
   extern __shared__ float s_dynf[];   // mass blocks: M, 1/Z [Hq], masses [kMassWindows][Hq], appended [Hq]
   const int b = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
-  const int G = pv.G, Hkv = pv.Hkv, Hq = pv.Hq, S = a.splits, W = pv.W, maxw = pv.maxw;
-  const int TPW = W / 32, seg = a.layer * pv.B + b;
-  const int32_t* info = a.app_info + 8 * b;
+  // Every kernel argument that either kind of block reads is fetched in one
+  // batch here: left to itself, the compiler requests a branch's arguments
+  // only once the branch is taken, a dependent round trip each.
+  uint16_t* const bf16_p = pv.bf16;
+  uint32_t* const pages_p = pv.pages;
+  float* const scores_p = pv.scores;
+  int32_t* const tokens_p = pv.tokens;
+  const float* const part_p = a.partials;
+  const float2* const ml_p = a.ml;
+  float* const out_p = a.out;
+  const uint16_t* const kn_p = a.k_new;
+  const uint16_t* const vn_p = a.v_new;
+  const int32_t* const info_p = a.app_info;
+  const float2* const tm_p = a.tile_mass;
+  const float2* const am_p = a.app_mass;
+  float* const mass_p = a.mass;
+  const int G = pv.G, Hkv = pv.Hkv, Hq = pv.Hq, S = a.splits, W = pv.W, maxw = pv.maxw, nb = pv.nb;
+  const int layer = a.layer, B = pv.B;
+  in_sgprs(bf16_p, pages_p, scores_p, tokens_p, part_p, ml_p, out_p, kn_p, vn_p, info_p, tm_p, am_p, mass_p);
+  in_sgprs(G, Hkv, Hq, S, W, maxw, nb, layer, B, acc_scores);
+  const int TPW = W / 32, seg = layer * B + b;
+  const int32_t* info = info_p + 8 * b;
   const int c32 = tid & 31, r8 = tid >> 5;   // (split lane, row of 32 threads)
+  // the step's append decision (app, slot, row, new window, tokens before),
+  // read as vector loads among each block's other loads
+  const auto rinfo = tile_rsrc(info, 5 * 4);
 
   if (x < Hkv * NO) {
     // -------------------------------------------------------- output slice
     const int kvh = x / NO, sl = x % NO;
-    const auto rp = tile_rsrc(a.partials + (size_t(b) * Hkv + kvh) * S * G * D, S * G * D * 4);
-    const auto rml = tile_rsrc(a.ml + (size_t(b) * Hq + size_t(kvh) * G) * S, G * S * 8);
+    const auto rp = tile_rsrc(part_p + (size_t(b) * Hkv + kvh) * S * G * D, S * G * D * 4);
+    const auto rml = tile_rsrc(ml_p + (size_t(b) * Hq + size_t(kvh) * G) * S, G * S * 8);
     const int items = G * (kSlice / 4);   // (head, 4 channels)
     const int groups = 256 / items;       // split groups, >= 4
     const int it = tid % items, grp = tid / items;
@@ -980,6 +1026,8 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
     const bool v0 = r8 < G && c32 < S, v1 = r8 < G && c32 + 32 < S;
     const float2 u0 = as_f2(load8(rml, boff(v0, (r8 * S + c32) * 8)));
     const float2 u1 = as_f2(load8(rml, boff(v1, (r8 * S + c32 + 32) * 8)));
+    const uint4 inf4 = load16(rinfo, 0);   // needed only at the end
+    const uint32_t i4 = load4(rinfo, 16);
     const float m0 = v0 ? u0.x : -INFINITY, l0 = u0.y, m1 = v1 ? u1.x : -INFINITY, l1 = u1.y;
     if (v0) s_m[c32 * G + r8] = m0;
     if (v1) s_m[(c32 + 32) * G + r8] = m1;
@@ -1012,29 +1060,30 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
         t4.x += u.x; t4.y += u.y; t4.z += u.z; t4.w += u.w;
       }
       const float Z = s_hz[h], iz = Z > 0.f ? 1.f / Z : 0.f;
-      *reinterpret_cast<float4*>(a.out + (size_t(b) * Hq + size_t(kvh) * G + h) * D + d) =
+      *reinterpret_cast<float4*>(out_p + (size_t(b) * Hq + size_t(kvh) * G + h) * D + d) =
           make_float4(t4.x * iz, t4.y * iz, t4.z * iz, t4.w * iz);
     }
-    const int app = info[0], slot = info[1], row = info[2], newwin = info[3], len_old = info[4];
+    const int app = uniform(int(inf4.x)), slot = uniform(int(inf4.y)), row = uniform(int(inf4.z));
+    const int newwin = uniform(int(inf4.w)), len_old = uniform(int(i4));
     if (app && sl == 0) {
       // the appended token joins its window (no kernel of this step reads it)
       const int len = len_old + 1;
       const int n_old = windows_of(len_old, W);
-      uint16_t* dst = pv.block(seg, slot, kvh);
+      uint16_t* dst = bf16_p + ((size_t(seg) * nb + slot) * Hkv + kvh) * size_t(2 * W * D);
       for (int dd = tid; dd < D; dd += 256) {
-        dst[layout::bf16_window_k(row, dd, D)] = a.k_new[(size_t(b) * Hkv + kvh) * D + dd];
-        dst[layout::bf16_window_v(row, dd, D)] = a.v_new[(size_t(b) * Hkv + kvh) * D + dd];
+        dst[layout::bf16_window_k(row, dd, D)] = kn_p[(size_t(b) * Hkv + kvh) * D + dd];
+        dst[layout::bf16_window_v(row, dd, D)] = vn_p[(size_t(b) * Hkv + kvh) * D + dd];
       }
       if (kvh == 0 && tid == 0) {
-        if (newwin) pv.pages[size_t(seg) * maxw + n_old] = pe_make(TIER_F, false, slot, 0);
-        pv.tokens[seg] = len;
+        if (newwin) pages_p[size_t(seg) * maxw + n_old] = pe_make(TIER_F, false, slot, 0);
+        tokens_p[seg] = len;
       }
     }
     return;
   }
 
   // ---------------------------------------------------------- window masses
-  if (!a.mass && !acc_scores) return;
+  if (!mass_p && !acc_scores) return;
   const int w0 = (x - Hkv * NO) * kMassWindows;
   if (w0 >= maxw) return;
   float* s_M = s_dynf;             // [Hq]
@@ -1047,10 +1096,10 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   constexpr int kPairs = 4, kTiles = 8;   // pairs per batch; tiles per window at most
   const int npairs = Hq * kMassWindows;
   const int bpairs = min(kPairs, (npairs + 255) / 256);   // pairs of a thread in one batch
-  const auto rtm = tile_rsrc(a.tile_mass + size_t(b) * maxw * TPW * Hq, maxw * TPW * Hq * 8);
-  const auto rml = tile_rsrc(a.ml + size_t(b) * Hq * S, Hq * S * 8);
-  const auto rpg = tile_rsrc(pv.pages + size_t(seg) * maxw, maxw * 4);
-  const auto rsc = tile_rsrc(pv.scores + size_t(seg) * maxw, maxw * 4);
+  const auto rtm = tile_rsrc(tm_p + size_t(b) * maxw * TPW * Hq, maxw * TPW * Hq * 8);
+  const auto rml = tile_rsrc(ml_p + size_t(b) * Hq * S, Hq * S * 8);
+  const auto rpg = tile_rsrc(pages_p + size_t(seg) * maxw, maxw * 4);
+  const auto rsc = tile_rsrc(scores_p + size_t(seg) * maxw, maxw * 4);
   auto tile_masses = [&](int p0, float2 (&t)[kPairs][kTiles]) {
 #pragma unroll
     for (int i = 0; i < kPairs; ++i) {
@@ -1063,26 +1112,21 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       }
     }
   };
-  // loads of the first batch in flight together: tile masses, the page entries
-  // and scores of the block's windows, the appended token's records and the
-  // (m, l) pairs of the per-head reductions
-  // the step's append info as vector loads, issued first (the records do not
-  // depend on it)
-  const auto rinfo = tile_rsrc(info, 5 * 4);
-  const uint32_t i0 = load4(rinfo, 0), i4 = load4(rinfo, 16);
+  // One round of loads, all in flight together: the append info (above),
+  // the tile masses, the page entries and scores of the block's windows, the
+  // appended token's records and the (m, l) pairs of the per-head reductions.
+  // Nothing waits for the append info: entries past the window count are
+  // loaded too and ignored.
+  const uint4 inf4 = load16(rinfo, 0);
+  const uint32_t i4 = load4(rinfo, 16);
   float2 t1[kPairs][kTiles];
   tile_masses(0, t1);
-  const int app = uniform(int(i0)), len_old = uniform(int(i4));
-  const int len = len_old + (app ? 1 : 0);
-  const int n_old = windows_of(len_old, W), n_win = windows_of(len, W);
   const int wt = w0 + tid;   // thread tid < kMassWindows: its window's page entry and score
-  const bool tin = tid < kMassWindows && wt < n_win;
-  const uint32_t pe = load4(rpg, boff(tin && wt < n_old, wt * 4));
-  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tin, wt * 4)));
-  if (app) {
-    const auto rap = tile_rsrc(a.app_mass + size_t(b) * Hq, Hq * 8);
-    for (int h = tid; h < Hq; h += 256) s_app[h] = as_f2(load8(rap, h * 8));
-  }
+  const bool tw = tid < kMassWindows && wt < maxw;
+  const uint32_t pe = load4(rpg, boff(tw, wt * 4));
+  const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tw, wt * 4)));
+  const auto rap = tile_rsrc(am_p + size_t(b) * Hq, Hq * 8);
+  const float2 appm = as_f2(load8(rap, boff(tid < Hq, tid * 8)));
   for (int h0 = 0; h0 < Hq; h0 += 32) {
     float2 mr[4][2];
 #pragma unroll
@@ -1103,6 +1147,14 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
         s_Zh[h] = mz.y > 0.f ? 1.f / mz.y : 0.f;   // reciprocal of the normaliser
       }
     }
+  }
+  const int app = uniform(int(inf4.x)), len_old = uniform(int(i4));
+  const int len = len_old + (app ? 1 : 0);
+  const int n_old = windows_of(len_old, W), n_win = windows_of(len, W);
+  const bool tin = tid < kMassWindows && wt < n_win;
+  if (app) {
+    if (tid < Hq) s_app[tid] = appm;
+    for (int h = tid + 256; h < Hq; h += 256) s_app[h] = as_f2(load8(rap, h * 8));
   }
   // liveness and valid tiles of the block's windows
   if (tid < kMassWindows) {
@@ -1146,16 +1198,16 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   }
   __syncthreads();
   // masses out in window order (16 consecutive windows per head)
-  if (a.mass) {
+  if (mass_p) {
     for (int idx = tid; idx < npairs; idx += 256) {
       const int h = idx / kMassWindows, ww = idx % kMassWindows;
-      if (w0 + ww < n_win) a.mass[(size_t(b) * Hq + h) * maxw + w0 + ww] = s_mv[ww * Hq + h];
+      if (w0 + ww < n_win) mass_p[(size_t(b) * Hq + h) * maxw + w0 + ww] = s_mv[ww * Hq + h];
     }
   }
   if (acc_scores && tin && s_win[tid]) {
     float ssum = 0.f;
     for (int h = 0; h < Hq; ++h) ssum += s_mv[tid * Hq + h];   // heads in order
-    pv.scores[size_t(seg) * maxw + wt] = s_old + ssum;
+    scores_p[size_t(seg) * maxw + wt] = s_old + ssum;
   }
 }
 
