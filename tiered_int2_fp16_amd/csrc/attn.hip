@@ -945,9 +945,9 @@ __device__ inline float half_reduce(float x, Op op) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
 // Max and normaliser of one query head over the splits: lane c of a 32-lane
 // half-wave takes splits c and c + 32 (raw m, l pairs of the workgroups).
+// (The output blocks use it: 4 - 8 rows of 32 lanes reduce their heads at once.)
 __device__ inline float2 head_mz(float m0, float l0, float m1, float l1) {
   const float M = half_reduce(fmaxf(m0, m1), [](float u, float v) { return fmaxf(u, v); });
   float z = 0.f;
@@ -956,6 +956,14 @@ __device__ inline float2 head_mz(float m0, float l0, float m1, float l1) {
   z = half_reduce(z, [](float u, float v) { return u + v; });
   return make_float2(M, z);
 }
+// x combined over the 8 lanes of its group (DPP xor 1, xor 2, half-row mirror)
+template <typename Op>
+__device__ inline float oct_reduce(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  return op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+}
+
 
 // Materialise uniform values (kernel arguments) in SGPRs at this point.
 template <typename T>
@@ -998,7 +1006,6 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   in_sgprs(G, Hkv, Hq, S, W, maxw, nb, layer, B, acc_scores);
   const int TPW = W / 32, seg = layer * B + b;
   const int32_t* info = info_p + 8 * b;
-  const int c32 = tid & 31, r8 = tid >> 5;   // (split lane, row of 32 threads)
   // the step's append decision (app, slot, row, new window, tokens before),
   // read as vector loads among each block's other loads
   const auto rinfo = tile_rsrc(info, 5 * 4);
@@ -1022,6 +1029,7 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       const uint4 u = load16(rp, boff(act && sp < S, ((sp * G + h) * D + d) * 4));
       v4[j] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     }
+    const int c32 = tid & 31, r8 = tid >> 5;   // (split lane, row of 32 threads)
     // row r8 (< G) reduces head r8: splits c32 and c32 + 32
     const bool v0 = r8 < G && c32 < S, v1 = r8 < G && c32 + 32 < S;
     const float2 u0 = as_f2(load8(rml, boff(v0, (r8 * S + c32) * 8)));
@@ -1127,24 +1135,32 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tw, wt * 4)));
   const auto rap = tile_rsrc(am_p + size_t(b) * Hq, Hq * 8);
   const float2 appm = as_f2(load8(rap, boff(tid < Hq, tid * 8)));
-  for (int h0 = 0; h0 < Hq; h0 += 32) {
-    float2 mr[4][2];
+  // max and 1 / normaliser of every query head over the splits: 8 lanes per
+  // head, lane c8 taking splits c8, c8 + 8, ... (S <= 64), 32 heads a pass
+  {
+    const int c8 = tid & 7, hr = tid >> 3;
+    for (int h0 = 0; h0 < Hq; h0 += 32) {
+      const int h = h0 + hr;
+      float2 v[kMaxSplits / 8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int h = h0 + p * 8 + r8;
-      const bool v0 = h < Hq && c32 < S, v1 = h < Hq && c32 + 32 < S;
-      mr[p][0] = as_f2(load8(rml, boff(v0, (h * S + c32) * 8)));
-      mr[p][1] = as_f2(load8(rml, boff(v1, (h * S + c32 + 32) * 8)));
-      if (!v0) mr[p][0].x = -INFINITY;
-      if (!v1) mr[p][1].x = -INFINITY;
-    }
+      for (int j = 0; j < kMaxSplits / 8; ++j) {
+        const int sp = c8 + 8 * j;
+        const bool ok = h < Hq && sp < S;
+        v[j] = as_f2(load8(rml, boff(ok, (h * S + sp) * 8)));
+        if (!ok) v[j].x = -INFINITY;
+      }
+      float m = v[0].x;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int h = h0 + p * 8 + r8;
-      const float2 mz = head_mz(mr[p][0].x, mr[p][0].y, mr[p][1].x, mr[p][1].y);
-      if (h < Hq && c32 == 0) {
-        s_M[h] = mz.x;
-        s_Zh[h] = mz.y > 0.f ? 1.f / mz.y : 0.f;   // reciprocal of the normaliser
+      for (int j = 1; j < kMaxSplits / 8; ++j) m = fmaxf(m, v[j].x);
+      m = oct_reduce(m, [](float u, float w) { return fmaxf(u, w); });
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxSplits / 8; ++j)
+        if (v[j].x != -INFINITY) z = fmaf(v[j].y, fast_exp2(v[j].x - m), z);
+      z = oct_reduce(z, [](float u, float w) { return u + w; });
+      if (c8 == 0 && h < Hq) {
+        s_M[h] = m;
+        s_Zh[h] = z > 0.f ? 1.f / z : 0.f;   // reciprocal of the normaliser
       }
     }
   }
