@@ -79,8 +79,15 @@ def test_llama_32k(bits, n_lo):
     _, cnt = p.route(0, c.budget_frac, c.hi_frac)
     assert cnt[0][0] == n_lo and cnt[2][0] == c.n_windows - 25 - n_lo
     p.check_state(0, ledger_sample=20, window_sample=6, rng=np.random.default_rng(bits))
-    _, _, _, errs = p.step(0, 0)
+    out, mass, _, errs = p.step(0, 0)
     log("llama 32K, %d-bit ledger: out err %.2e mass err %.2e" % (bits, *errs))
+    # the same step again gives the same bits (no run-to-run variation), also
+    # without the mass emission
+    q = dev(__import__("workload").query(c, 0, 0))
+    out2, mass2 = p.pool.attn(0, q)
+    assert torch.equal(out, out2) and torch.equal(mass, mass2)
+    out3, _ = p.pool.attn(0, q, want_mass=False)
+    assert torch.equal(out, out3)
 
 
 SHAPES = [
@@ -124,8 +131,10 @@ def test_qwen_32k(bits, n_lo):
     _, cnt = p.route(0, c.budget_frac, c.hi_frac)
     assert (cnt[0] == n_lo).all() and (cnt[2] == c.n_windows - 5 - n_lo).all()
     p.check_state(0, ledger_sample=6, window_sample=3, rng=np.random.default_rng(10 + bits))
-    _, _, _, errs = p.step(0, 0)
+    out, mass, _, errs = p.step(0, 0)
     log("qwen 32K, %d-bit ledger: out err %.2e mass err %.2e" % (bits, *errs))
+    out2, mass2 = p.pool.attn(0, dev(__import__("workload").query(c, 0, 0)))
+    assert torch.equal(out, out2) and torch.equal(mass, mass2)
 
 
 @pytest.mark.timeout(900)
