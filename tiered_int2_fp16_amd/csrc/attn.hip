@@ -1120,11 +1120,11 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       }
     }
   };
-  // One round of loads, all in flight together: the append info (above),
-  // the tile masses, the page entries and scores of the block's windows, the
-  // appended token's records and the (m, l) pairs of the per-head reductions.
-  // Nothing waits for the append info: entries past the window count are
-  // loaded too and ignored.
+  // One round of loads, all in flight together: the append info, the tile
+  // masses, the page entries and scores of the block's windows, the appended
+  // token's records and the (m, l) pairs of the per-head reductions.  Nothing
+  // waits for the append info: entries past the window count are loaded too
+  // and ignored.
   const uint4 inf4 = load16(rinfo, 0);
   const uint32_t i4 = load4(rinfo, 16);
   float2 t1[kPairs][kTiles];
