@@ -13,7 +13,7 @@ import dataclasses
 import numpy as np
 import pytest
 
-from workload import CONFIGS
+from workload import CONFIGS, query
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,7 @@ def test_llama_32k(bits, n_lo):
     log("llama 32K, %d-bit ledger: out err %.2e mass err %.2e" % (bits, *errs))
     # the same step again gives the same bits (no run-to-run variation), also
     # without the mass emission
-    q = dev(__import__("workload").query(c, 0, 0))
+    q = dev(query(c, 0, 0))
     out2, mass2 = p.pool.attn(0, q)
     assert torch.equal(out, out2) and torch.equal(mass, mass2)
     out3, _ = p.pool.attn(0, q, want_mass=False)
@@ -133,7 +133,7 @@ def test_qwen_32k(bits, n_lo):
     p.check_state(0, ledger_sample=6, window_sample=3, rng=np.random.default_rng(10 + bits))
     out, mass, _, errs = p.step(0, 0)
     log("qwen 32K, %d-bit ledger: out err %.2e mass err %.2e" % (bits, *errs))
-    out2, mass2 = p.pool.attn(0, dev(__import__("workload").query(c, 0, 0)))
+    out2, mass2 = p.pool.attn(0, dev(query(c, 0, 0)))
     assert torch.equal(out, out2) and torch.equal(mass, mass2)
 
 
