@@ -11,14 +11,18 @@
 // Three kernels, all dense 16x16x32 bf16 MFMA tiles (lane l holds 8
 // consecutive values of operand row l%16 at column block l/16; a result lane
 // holds rows 4*(l/16)+i of column l%16):
-//   1. row pass: each wave takes 16 queries and walks the keys 0..q in chunks
-//      of 32, keeping per-lane running (max, sum) in the log2 domain, merged
-//      over the 16 lanes of a row at the end: lse[q] = max + log2(sum);
-//   2. column pass: each wave takes 16 keys and walks the queries t..T-1 in
+//   1. row pass: each wave takes 64 queries (four 16-row operand blocks held
+//      in registers) and walks the keys 0..q in chunks of 32, each chunk's key
+//      operands serving all four blocks.  Per lane it keeps a running (max,
+//      sum) in the log2 domain, merged over the 16 lanes of a row at the end:
+//      lse[q] = max + log2(sum);
+//   2. column pass: each wave takes 64 keys and walks the queries t..T-1 in
 //      chunks of 32, adding exp2(s - lse[q]): w[t] per head;
 //   3. window sums: S[w] = sum over heads (in order) and the window's tokens
 //      (a fixed tree) of w.
 // The next chunk's operands are requested before the current chunk's math.
+// Chunks wholly inside the causal region skip the mask; in the row pass they
+// also leave the running max in place unless a score passes it by kSlack.
 #include "launch.h"
 
 namespace kvtier {
@@ -47,32 +51,40 @@ __device__ inline void merge_ms(float& m, float& l, float mo, float lo) {
   m = M;
 }
 
-constexpr int kRows = 16;     // queries (pass 1) or keys (pass 2) per wave
+constexpr int kRows = 16;     // queries (pass 1) or keys (pass 2) per operand block
+constexpr int kRowBlocks = 4; // operand blocks per wave: each loaded chunk serves 64 rows
+constexpr float kSlack = 8.f; // row pass: log2 headroom before the running max is moved
 constexpr int kChunk = 32;    // keys (pass 1) or queries (pass 2) per step
 constexpr int kWaves = 4;
 
-template <int D>
+template <int D, int RB>
 __global__ __launch_bounds__(256) void prefill_lse_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k, int T, int Hq,
                                                           int Hkv, float qscale, float* __restrict__ lse) {
   constexpr int KK = D / 32;
   const int b = blockIdx.z, h = blockIdx.y, kvh = h / (Hq / Hkv);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, g = lane >> 4, hn = lane & 15;
-  const int q0 = (blockIdx.x * kWaves + wid) * kRows;
+  const int lane = threadIdx.x & 63, g = lane >> 4, hn = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
+  const int q0 = (blockIdx.x * kWaves + wid) * kRows * RB;
   if (q0 >= T) return;   // the whole wave
   const auto qr = span_rsrc(q + (size_t(b) * Hq + h) * size_t(T) * D, T * D * 2);
   const auto kr = span_rsrc(k + (size_t(b) * Hkv + kvh) * size_t(T) * D, T * D * 2);
-  bf16x8 qa[KK];   // query row q0 + hn (zeros past T), dims 32 kk + 8 g ..
+  bf16x8 qa[RB][KK];   // query rows q0 + 16 r + hn (zeros past T), dims 32 kk + 8 g ..
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qa[kk] = load_row8(qr, ((q0 + hn) * D + 32 * kk + 8 * g) * 2);
-  float m[4], l[4];
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-  }
-  const int qlast = min(q0 + kRows, T) - 1;
-  // keys k0 + hn and k0 + 16 + hn (zeros past T; masked by causality)
+    for (int kk = 0; kk < KK; ++kk) qa[r][kk] = load_row8(qr, ((q0 + kRows * r + hn) * D + 32 * kk + 8 * g) * 2);
+  float m[RB][4], l[RB][4];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[r][i] = -INFINITY;
+      l[r][i] = 0.f;
+    }
+  const int qlast = min(q0 + kRows * RB, T) - 1;
+  // keys k0 + hn and k0 + 16 + hn (zeros past T; masked by causality), shared
+  // by the wave's RB blocks of 16 queries
   bf16x8 ka[KK], kb[KK];
   auto load_keys = [&](int k0) {
 #pragma unroll
@@ -83,39 +95,77 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(const uint16_t* __rest
   };
   load_keys(0);
   for (int k0 = 0; k0 <= qlast; k0 += kChunk) {
-    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 c0[RB], c1[RB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      c0 = mfma_bf16(qa[kk], ka[kk], c0);
-      c1 = mfma_bf16(qa[kk], kb[kk], c1);
+    for (int r = 0; r < RB; ++r) {
+      c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        c0[r] = mfma_bf16(qa[r][kk], ka[kk], c0[r]);
+        c1[r] = mfma_bf16(qa[r][kk], kb[kk], c1[r]);
+      }
     }
     if (k0 + kChunk <= qlast) load_keys(k0 + kChunk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = q0 + 4 * g + i;
-      const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
-      const float s0 = v0 ? c0[i] * qscale : -INFINITY, s1 = v1 ? c1[i] * qscale : -INFINITY;
-      const float mn = fmaxf(m[i], fmaxf(s0, s1));
-      if (mn != -INFINITY) {
-        l[i] = (m[i] == -INFINITY ? 0.f : l[i] * exp2_hw(m[i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
-               (v1 ? exp2_hw(s1 - mn) : 0.f);
-        m[i] = mn;
+    for (int r = 0; r < RB; ++r) {
+      if (k0 > q0 + kRows * r + kRows - 1) continue;   // the whole block is before these keys (uniform)
+      if (k0 + kChunk - 1 <= q0 + kRows * r) {
+        // every key of the chunk is at or before every row of the block: no
+        // mask.  The running max moves only when a score of the block passes
+        // it by more than kSlack (one vote per block); otherwise the chunk
+        // adds its terms against the old max, up to 2^kSlack each.
+        float e0[4], e1[4];
+        bool up = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          e0[i] = fmaf(c0[r][i], qscale, -m[r][i]);
+          e1[i] = fmaf(c1[r][i], qscale, -m[r][i]);
+          up |= fmaxf(e0[i], e1[i]) > kSlack;   // also true while m is -inf
+        }
+        if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float s0 = c0[r][i] * qscale, s1 = c1[r][i] * qscale;
+            const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
+            l[r][i] = fmaf(l[r][i], exp2_hw(m[r][i] - mn), exp2_hw(s0 - mn) + exp2_hw(s1 - mn));
+            m[r][i] = mn;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l[r][i] += exp2_hw(e0[i]) + exp2_hw(e1[i]);
+        }
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = q0 + kRows * r + 4 * g + i;
+        const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
+        const float s0 = v0 ? c0[r][i] * qscale : -INFINITY, s1 = v1 ? c1[r][i] * qscale : -INFINITY;
+        const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
+        if (mn != -INFINITY) {
+          l[r][i] = (m[r][i] == -INFINITY ? 0.f : l[r][i] * exp2_hw(m[r][i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
+                    (v1 ? exp2_hw(s1 - mn) : 0.f);
+          m[r][i] = mn;
+        }
       }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const float mo = __shfl_xor(m[i], off, 64), lo = __shfl_xor(l[i], off, 64);
-      merge_ms(m[i], l[i], mo, lo);
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float mo = __shfl_xor(m[r][i], off, 64), lo = __shfl_xor(l[r][i], off, 64);
+        merge_ms(m[r][i], l[r][i], mo, lo);
+      }
+      const int row = q0 + kRows * r + 4 * g + i;
+      if (hn == 0 && row < T) lse[(size_t(b) * Hq + h) * T + row] = m[r][i] + __log2f(l[r][i]);
     }
-    const int row = q0 + 4 * g + i;
-    if (hn == 0 && row < T) lse[(size_t(b) * Hq + h) * T + row] = m[i] + __log2f(l[i]);
-  }
 }
 
-template <int D>
+template <int D, int RB>
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k, int T, int Hq,
                                                              int Hkv, float qscale,
@@ -123,17 +173,25 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __r
                                                              float* __restrict__ wt) {
   constexpr int KK = D / 32;
   const int b = blockIdx.z, h = blockIdx.y, kvh = h / (Hq / Hkv);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, g = lane >> 4, hn = lane & 15;
-  const int t0 = (blockIdx.x * kWaves + wid) * kRows;
+  const int lane = threadIdx.x & 63, g = lane >> 4, hn = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
+  const int t0 = (blockIdx.x * kWaves + wid) * kRows * RB;
   if (t0 >= T) return;
   const auto qr = span_rsrc(q + (size_t(b) * Hq + h) * size_t(T) * D, T * D * 2);
   const auto kr = span_rsrc(k + (size_t(b) * Hkv + kvh) * size_t(T) * D, T * D * 2);
   const auto lr = span_rsrc(lse + (size_t(b) * Hq + h) * T, T * 4);
-  bf16x8 ka[KK];   // key row t0 + hn
+  bf16x8 ka[RB][KK];   // key rows t0 + 16 r + hn
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) ka[kk] = load_row8(kr, ((t0 + hn) * D + 32 * kk + 8 * g) * 2);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  // queries q0 + hn and q0 + 16 + hn (zeros and lse 0 past T; masked)
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) ka[r][kk] = load_row8(kr, ((t0 + kRows * r + hn) * D + 32 * kk + 8 * g) * 2);
+  float acc[RB][4];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
+  // queries q0 + hn and q0 + 16 + hn (zeros and lse 0 past T; masked), shared
+  // by the wave's RB blocks of 16 keys
   bf16x8 qa[KK], qb[KK];
   float la, lb;
   auto load_queries = [&](int q0) {
@@ -148,30 +206,49 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __r
   const int qstart = t0 & ~(kChunk - 1);
   load_queries(qstart);
   for (int q0 = qstart; q0 < T; q0 += kChunk) {
-    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 c0[RB], c1[RB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      c0 = mfma_bf16(ka[kk], qa[kk], c0);
-      c1 = mfma_bf16(ka[kk], qb[kk], c1);
+    for (int r = 0; r < RB; ++r) {
+      c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        c0[r] = mfma_bf16(ka[r][kk], qa[kk], c0[r]);
+        c1[r] = mfma_bf16(ka[r][kk], qb[kk], c1[r]);
+      }
     }
     const float l0 = la, l1 = lb;
     if (q0 + kChunk < T) load_queries(q0 + kChunk);
     const int qa_i = q0 + hn, qb_i = q0 + 16 + hn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = t0 + 4 * g + i;
-      if (qa_i >= key && qa_i < T) acc[i] += exp2_hw(fmaf(c0[i], qscale, -l0));
-      if (qb_i >= key && qb_i < T) acc[i] += exp2_hw(fmaf(c1[i], qscale, -l1));
+    for (int r = 0; r < RB; ++r) {
+      if (q0 + kChunk <= T && q0 >= t0 + kRows * r + kRows - 1) {
+        // every query of the chunk exists and is at or after every key of the block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
+          acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
+        }
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = t0 + kRows * r + 4 * g + i;
+        if (qa_i >= key && qa_i < T) acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
+        if (qb_i >= key && qb_i < T) acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float x = acc[i];
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
-    const int key = t0 + 4 * g + i;
-    if (hn == 0 && key < T) wt[(size_t(b) * Hq + h) * T + key] = x;
-  }
+    for (int i = 0; i < 4; ++i) {
+      float x = acc[r][i];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+      const int key = t0 + kRows * r + 4 * g + i;
+      if (hn == 0 && key < T) wt[(size_t(b) * Hq + h) * T + key] = x;
+    }
 }
 
 // S[w] of sequence b: the window's token weights of every head (heads in
@@ -203,15 +280,17 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(PoolView pv, int la
 hipError_t launch_prefill_scores(const PoolView& pv, int layer, const uint16_t* q, const uint16_t* k,
                                  int T, float* lse, float* wt, hipStream_t s) {
   const float qscale = 1.4426950408889634f / sqrtf(float(pv.D));
-  const dim3 grid((T + kWaves * kRows - 1) / (kWaves * kRows), pv.Hq, pv.B);
+  const dim3 grid((T + kWaves * kRows * kRowBlocks - 1) / (kWaves * kRows * kRowBlocks), pv.Hq, pv.B);
   if (pv.D == 128) {
-    hipLaunchKernelGGL((prefill_lse_kernel<128>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale, lse);
-    hipLaunchKernelGGL((prefill_colsum_kernel<128>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale,
-                       lse, wt);
+    hipLaunchKernelGGL((prefill_lse_kernel<128, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+                       qscale, lse);
+    hipLaunchKernelGGL((prefill_colsum_kernel<128, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+                       qscale, lse, wt);
   } else {
-    hipLaunchKernelGGL((prefill_lse_kernel<64>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale, lse);
-    hipLaunchKernelGGL((prefill_colsum_kernel<64>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv, qscale,
-                       lse, wt);
+    hipLaunchKernelGGL((prefill_lse_kernel<64, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+                       qscale, lse);
+    hipLaunchKernelGGL((prefill_colsum_kernel<64, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+                       qscale, lse, wt);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
