@@ -20,9 +20,12 @@
 //      chunks of 32, adding exp2(s - lse[q]): w[t] per head;
 //   3. window sums: S[w] = sum over heads (in order) and the window's tokens
 //      (a fixed tree) of w.
-// The next chunk's operands are requested before the current chunk's math.
-// Chunks wholly inside the causal region skip the mask; in the row pass they
-// also leave the running max in place unless a score passes it by kSlack.
+// The four waves of a workgroup hold adjacent 64-row ranges and walk the same
+// chunks, so each chunk is loaded once per workgroup into a double-buffered
+// LDS tile (one barrier per chunk) and read from there by every wave; the
+// next chunk is requested before the current chunk's math.  Chunks wholly
+// inside the causal region skip the mask; in the row pass they also leave the
+// running max in place unless a score passes it by kSlack.
 #include "launch.h"
 
 namespace kvtier {
@@ -31,6 +34,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -51,22 +55,58 @@ __device__ inline void merge_ms(float& m, float& l, float mo, float lo) {
   m = M;
 }
 
+constexpr int kChunk = 32;    // keys (pass 1) or queries (pass 2) per step
+constexpr int kWaves = 4;      // waves per workgroup; the workgroup shares each chunk
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 16;     // queries (pass 1) or keys (pass 2) per operand block
 constexpr int kRowBlocks = 4; // operand blocks per wave: each loaded chunk serves 64 rows
 constexpr float kSlack = 8.f; // row pass: log2 headroom before the running max is moved
-constexpr int kChunk = 32;    // keys (pass 1) or queries (pass 2) per step
-constexpr int kWaves = 4;
+
+// One 32-row chunk of a [T, D] bf16 operand, loaded once per workgroup (kPer
+// 16-byte pieces per thread) into one of two LDS tiles.  Rows are padded by
+// 16 bytes, so the MFMA operand reads (16 rows, 16 bytes per lane) fall in
+// distinct banks.  Rows past T read zeros.
+template <int D>
+struct ChunkTiles {
+  static constexpr int kRowB = D * 2 + 16;
+  static constexpr int kTileB = kChunk * kRowB;
+  static constexpr int kPieces = kChunk * D / 8;
+  static constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
+  unsigned char* lds;   // two tiles of kTileB bytes
+  u32x4 stage[kPer];
+  __device__ void fetch(__amdgpu_buffer_rsrc_t r, int row0) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int pc = threadIdx.x + kThreads * p, row = pc / (D / 8), col = pc % (D / 8);
+      if (kPieces % kThreads == 0 || pc < kPieces)
+        stage[p] = __builtin_amdgcn_raw_buffer_load_b128(r, ((row0 + row) * D + 8 * col) * 2, 0, 0);
+    }
+  }
+  __device__ void stash(int t) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int pc = threadIdx.x + kThreads * p, row = pc / (D / 8), col = pc % (D / 8);
+      if (kPieces % kThreads == 0 || pc < kPieces)
+        *reinterpret_cast<u32x4*>(lds + t * kTileB + row * kRowB + col * 16) = stage[p];
+    }
+  }
+  // operand row `row` of tile t, values 32 kk + 8 g .. + 8
+  __device__ bf16x8 operand(int t, int row, int kk, int g) const {
+    return *reinterpret_cast<const bf16x8*>(lds + t * kTileB + row * kRowB + (32 * kk + 8 * g) * 2);
+  }
+};
 
 template <int D, int RB>
-__global__ __launch_bounds__(256) void prefill_lse_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads) void prefill_lse_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k, int T, int Hq,
                                                           int Hkv, float qscale, float* __restrict__ lse) {
   constexpr int KK = D / 32;
   const int b = blockIdx.z, h = blockIdx.y, kvh = h / (Hq / Hkv);
   const int lane = threadIdx.x & 63, g = lane >> 4, hn = lane & 15;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
-  const int q0 = (blockIdx.x * kWaves + wid) * kRows * RB;
-  if (q0 >= T) return;   // the whole wave
+  const int wq0 = blockIdx.x * kWaves * kRows * RB;                    // the workgroup's first query
+  if (wq0 >= T) return;   // the whole workgroup
+  const int q0 = wq0 + wid * kRows * RB;
   const auto qr = span_rsrc(q + (size_t(b) * Hq + h) * size_t(T) * D, T * D * 2);
   const auto kr = span_rsrc(k + (size_t(b) * Hkv + kvh) * size_t(T) * D, T * D * 2);
   bf16x8 qa[RB][KK];   // query rows q0 + 16 r + hn (zeros past T), dims 32 kk + 8 g ..
@@ -82,74 +122,91 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(const uint16_t* __rest
       m[r][i] = -INFINITY;
       l[r][i] = 0.f;
     }
-  const int qlast = min(q0 + kRows * RB, T) - 1;
-  // keys k0 + hn and k0 + 16 + hn (zeros past T; masked by causality), shared
-  // by the wave's RB blocks of 16 queries
-  bf16x8 ka[KK], kb[KK];
-  auto load_keys = [&](int k0) {
+  // A wave past T has no rows; it still loads and synchronises with the others.
+  const int qlast = q0 < T ? min(q0 + kRows * RB, T) - 1 : -1;
+  const int wlast = min(wq0 + kWaves * kRows * RB, T) - 1;   // the workgroup walks keys 0..wlast
+  // Each 32-key chunk is loaded once per workgroup into LDS; one barrier per chunk.
+  __shared__ __attribute__((aligned(16))) unsigned char ktiles[2 * ChunkTiles<D>::kTileB];
+  ChunkTiles<D> kc{ktiles};
+  kc.fetch(kr, 0);
+  kc.stash(0);
+  // the query operands are complete here, so no wait in the loop counts them
+  // (it would also wait for the next chunk's fetch)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      ka[kk] = load_row8(kr, ((k0 + hn) * D + 32 * kk + 8 * g) * 2);
-      kb[kk] = load_row8(kr, ((k0 + 16 + hn) * D + 32 * kk + 8 * g) * 2);
-    }
-  };
-  load_keys(0);
-  for (int k0 = 0; k0 <= qlast; k0 += kChunk) {
-    f32x4 c0[RB], c1[RB];
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qa[r][kk]));
+  __syncthreads();
+  int t = 0;
+  for (int k0 = 0; k0 <= wlast; k0 += kChunk, t ^= 1) {
+    const bool more = k0 + kChunk <= wlast;
+    if (more) kc.fetch(kr, k0 + kChunk);
+    if (k0 <= qlast) {
+      // keys k0 + hn and k0 + 16 + hn (masked by causality past T), shared by
+      // the wave's RB blocks of 16 queries
+      bf16x8 ka[KK], kb[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        c0[r] = mfma_bf16(qa[r][kk], ka[kk], c0[r]);
-        c1[r] = mfma_bf16(qa[r][kk], kb[kk], c1[r]);
+        ka[kk] = kc.operand(t, hn, kk, g);
+        kb[kk] = kc.operand(t, 16 + hn, kk, g);
       }
-    }
-    if (k0 + kChunk <= qlast) load_keys(k0 + kChunk);
+      f32x4 c0[RB], c1[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      if (k0 > q0 + kRows * r + kRows - 1) continue;   // the whole block is before these keys (uniform)
-      if (k0 + kChunk - 1 <= q0 + kRows * r) {
-        // every key of the chunk is at or before every row of the block: no
-        // mask.  The running max moves only when a score of the block passes
-        // it by more than kSlack (one vote per block); otherwise the chunk
-        // adds its terms against the old max, up to 2^kSlack each.
-        float e0[4], e1[4];
-        bool up = false;
+      for (int r = 0; r < RB; ++r) {
+        c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e0[i] = fmaf(c0[r][i], qscale, -m[r][i]);
-          e1[i] = fmaf(c1[r][i], qscale, -m[r][i]);
-          up |= fmaxf(e0[i], e1[i]) > kSlack;   // also true while m is -inf
+        for (int kk = 0; kk < KK; ++kk) {
+          c0[r] = mfma_bf16(qa[r][kk], ka[kk], c0[r]);
+          c1[r] = mfma_bf16(qa[r][kk], kb[kk], c1[r]);
         }
-        if (__builtin_amdgcn_ballot_w64(up)) {
+      }
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (k0 > q0 + kRows * r + kRows - 1) continue;   // the whole block is before these keys (uniform)
+        if (k0 + kChunk - 1 <= q0 + kRows * r) {
+          // every key of the chunk is at or before every row of the block: no
+          // mask.  The running max moves only when a score of the block passes
+          // it by more than kSlack (one vote per block); otherwise the chunk
+          // adds its terms against the old max, up to 2^kSlack each.
+          float e0[4], e1[4];
+          bool up = false;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float s0 = c0[r][i] * qscale, s1 = c1[r][i] * qscale;
-            const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
-            l[r][i] = fmaf(l[r][i], exp2_hw(m[r][i] - mn), exp2_hw(s0 - mn) + exp2_hw(s1 - mn));
+            e0[i] = fmaf(c0[r][i], qscale, -m[r][i]);
+            e1[i] = fmaf(c1[r][i], qscale, -m[r][i]);
+            up |= fmaxf(e0[i], e1[i]) > kSlack;   // also true while m is -inf
+          }
+          if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float s0 = c0[r][i] * qscale, s1 = c1[r][i] * qscale;
+              const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
+              l[r][i] = fmaf(l[r][i], exp2_hw(m[r][i] - mn), exp2_hw(s0 - mn) + exp2_hw(s1 - mn));
+              m[r][i] = mn;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l[r][i] += exp2_hw(e0[i]) + exp2_hw(e1[i]);
+          }
+          continue;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = q0 + kRows * r + 4 * g + i;
+          const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
+          const float s0 = v0 ? c0[r][i] * qscale : -INFINITY, s1 = v1 ? c1[r][i] * qscale : -INFINITY;
+          const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
+          if (mn != -INFINITY) {
+            l[r][i] = (m[r][i] == -INFINITY ? 0.f : l[r][i] * exp2_hw(m[r][i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
+                      (v1 ? exp2_hw(s1 - mn) : 0.f);
             m[r][i] = mn;
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) l[r][i] += exp2_hw(e0[i]) + exp2_hw(e1[i]);
-        }
-        continue;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = q0 + kRows * r + 4 * g + i;
-        const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
-        const float s0 = v0 ? c0[r][i] * qscale : -INFINITY, s1 = v1 ? c1[r][i] * qscale : -INFINITY;
-        const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
-        if (mn != -INFINITY) {
-          l[r][i] = (m[r][i] == -INFINITY ? 0.f : l[r][i] * exp2_hw(m[r][i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
-                    (v1 ? exp2_hw(s1 - mn) : 0.f);
-          m[r][i] = mn;
         }
       }
     }
+    if (more) kc.stash(t ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -166,7 +223,7 @@ __global__ __launch_bounds__(256) void prefill_lse_kernel(const uint16_t* __rest
 }
 
 template <int D, int RB>
-__global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k, int T, int Hq,
                                                              int Hkv, float qscale,
                                                              const float* __restrict__ lse,
@@ -175,8 +232,9 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __r
   const int b = blockIdx.z, h = blockIdx.y, kvh = h / (Hq / Hkv);
   const int lane = threadIdx.x & 63, g = lane >> 4, hn = lane & 15;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
-  const int t0 = (blockIdx.x * kWaves + wid) * kRows * RB;
-  if (t0 >= T) return;
+  const int wt0 = blockIdx.x * kWaves * kRows * RB;                    // the workgroup's first key
+  if (wt0 >= T) return;   // the whole workgroup
+  const int t0 = wt0 + wid * kRows * RB;
   const auto qr = span_rsrc(q + (size_t(b) * Hq + h) * size_t(T) * D, T * D * 2);
   const auto kr = span_rsrc(k + (size_t(b) * Hkv + kvh) * size_t(T) * D, T * D * 2);
   const auto lr = span_rsrc(lse + (size_t(b) * Hq + h) * T, T * 4);
@@ -190,54 +248,76 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(const uint16_t* __r
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
-  // queries q0 + hn and q0 + 16 + hn (zeros and lse 0 past T; masked), shared
-  // by the wave's RB blocks of 16 keys
-  bf16x8 qa[KK], qb[KK];
-  float la, lb;
-  auto load_queries = [&](int q0) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qa[kk] = load_row8(qr, ((q0 + hn) * D + 32 * kk + 8 * g) * 2);
-      qb[kk] = load_row8(qr, ((q0 + 16 + hn) * D + 32 * kk + 8 * g) * 2);
-    }
-    la = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + hn) * 4, 0, 0));
-    lb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + 16 + hn) * 4, 0, 0));
+  // Each 32-query chunk (and its 32 lse values) is loaded once per workgroup
+  // into LDS, one barrier per chunk; the workgroup walks queries wt0..T-1.
+  // Queries past T read zeros and lse 0 and are masked.
+  __shared__ __attribute__((aligned(16))) unsigned char qtiles[2 * ChunkTiles<D>::kTileB];
+  __shared__ float ltiles[2][kChunk];
+  ChunkTiles<D> qc{qtiles};
+  float lstage = 0.f;
+  auto fetch = [&](int q0) {
+    qc.fetch(qr, q0);
+    if (threadIdx.x < kChunk)
+      lstage = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + threadIdx.x) * 4, 0, 0));
   };
-  const int qstart = t0 & ~(kChunk - 1);
-  load_queries(qstart);
-  for (int q0 = qstart; q0 < T; q0 += kChunk) {
-    f32x4 c0[RB], c1[RB];
+  auto stash = [&](int t) {
+    qc.stash(t);
+    if (threadIdx.x < kChunk) ltiles[t][threadIdx.x] = lstage;
+  };
+  fetch(wt0);
+  stash(0);
+  // the key operands are complete here, so no wait in the loop counts them
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(ka[r][kk]));
+  __syncthreads();
+  int t = 0;
+  for (int q0 = wt0; q0 < T; q0 += kChunk, t ^= 1) {
+    const bool more = q0 + kChunk < T;
+    if (more) fetch(q0 + kChunk);
+    if (q0 + kChunk - 1 >= t0 && t0 < T) {   // some query of the chunk is at or after the wave's first key
+      // queries q0 + hn and q0 + 16 + hn, shared by the wave's RB blocks of 16 keys
+      bf16x8 qa[KK], qb[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        c0[r] = mfma_bf16(ka[r][kk], qa[kk], c0[r]);
-        c1[r] = mfma_bf16(ka[r][kk], qb[kk], c1[r]);
+        qa[kk] = qc.operand(t, hn, kk, g);
+        qb[kk] = qc.operand(t, 16 + hn, kk, g);
       }
-    }
-    const float l0 = la, l1 = lb;
-    if (q0 + kChunk < T) load_queries(q0 + kChunk);
-    const int qa_i = q0 + hn, qb_i = q0 + 16 + hn;
+      const float l0 = ltiles[t][hn], l1 = ltiles[t][16 + hn];
+      f32x4 c0[RB], c1[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      if (q0 + kChunk <= T && q0 >= t0 + kRows * r + kRows - 1) {
-        // every query of the chunk exists and is at or after every key of the block
+      for (int r = 0; r < RB; ++r) {
+        c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          c0[r] = mfma_bf16(ka[r][kk], qa[kk], c0[r]);
+          c1[r] = mfma_bf16(ka[r][kk], qb[kk], c1[r]);
+        }
+      }
+      const int qa_i = q0 + hn, qb_i = q0 + 16 + hn;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (q0 + kChunk <= T && q0 >= t0 + kRows * r + kRows - 1) {
+          // every query of the chunk exists and is at or after every key of the block
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
+            acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
+          }
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
-          acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
+          const int key = t0 + kRows * r + 4 * g + i;
+          if (qa_i >= key && qa_i < T) acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
+          if (qb_i >= key && qb_i < T) acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
         }
-        continue;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = t0 + kRows * r + 4 * g + i;
-        if (qa_i >= key && qa_i < T) acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
-        if (qb_i >= key && qb_i < T) acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
       }
     }
+    if (more) stash(t ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int r = 0; r < RB; ++r)
@@ -282,14 +362,14 @@ hipError_t launch_prefill_scores(const PoolView& pv, int layer, const uint16_t* 
   const float qscale = 1.4426950408889634f / sqrtf(float(pv.D));
   const dim3 grid((T + kWaves * kRows * kRowBlocks - 1) / (kWaves * kRows * kRowBlocks), pv.Hq, pv.B);
   if (pv.D == 128) {
-    hipLaunchKernelGGL((prefill_lse_kernel<128, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+    hipLaunchKernelGGL((prefill_lse_kernel<128, kRowBlocks>), grid, dim3(kThreads), 0, s, q, k, T, pv.Hq, pv.Hkv,
                        qscale, lse);
-    hipLaunchKernelGGL((prefill_colsum_kernel<128, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+    hipLaunchKernelGGL((prefill_colsum_kernel<128, kRowBlocks>), grid, dim3(kThreads), 0, s, q, k, T, pv.Hq, pv.Hkv,
                        qscale, lse, wt);
   } else {
-    hipLaunchKernelGGL((prefill_lse_kernel<64, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+    hipLaunchKernelGGL((prefill_lse_kernel<64, kRowBlocks>), grid, dim3(kThreads), 0, s, q, k, T, pv.Hq, pv.Hkv,
                        qscale, lse);
-    hipLaunchKernelGGL((prefill_colsum_kernel<64, kRowBlocks>), grid, dim3(256), 0, s, q, k, T, pv.Hq, pv.Hkv,
+    hipLaunchKernelGGL((prefill_colsum_kernel<64, kRowBlocks>), grid, dim3(kThreads), 0, s, q, k, T, pv.Hq, pv.Hkv,
                        qscale, lse, wt);
   }
   hipError_t e = hipGetLastError();
