@@ -16,14 +16,15 @@
 //      operands serving all four blocks.  Per lane it keeps a running (max,
 //      sum) in the log2 domain, merged over the 16 lanes of a row at the end:
 //      lse[q] = max + log2(sum);
-//   2. column pass: each wave takes 64 keys and walks the queries t..T-1 in
-//      chunks of 32, adding exp2(s - lse[q]): w[t] per head;
+//   2. column pass: each wave takes 64 keys and walks the queries T-1 down to
+//      t in chunks of 32, adding exp2(s - lse[q]): w[t] per head (downwards,
+//      so that the workgroups in flight read the same query chunks from L2);
 //   3. window sums: S[w] = sum over heads (in order) and the window's tokens
 //      (a fixed tree) of w.
 // The four waves of a workgroup hold adjacent 64-row ranges and walk the same
-// chunks, so each chunk is loaded once per workgroup into a double-buffered
-// LDS tile (one barrier per chunk) and read from there by every wave; the
-// next chunk is requested before the current chunk's math.  Chunks wholly
+// chunks, so each stage of two chunks is loaded once per workgroup into a
+// double-buffered LDS tile (one barrier per stage) and read from there by
+// every wave; the next stage is requested before the current stage's math.  Chunks wholly
 // inside the causal region skip the mask; in the row pass they also leave the
 // running max in place unless a score passes it by kSlack.
 #include "launch.h"
@@ -56,21 +57,23 @@ __device__ inline void merge_ms(float& m, float& l, float mo, float lo) {
 }
 
 constexpr int kChunk = 32;    // keys (pass 1) or queries (pass 2) per step
+constexpr int kSub = 2;       // steps per LDS stage (one barrier per stage)
+constexpr int kStage = kChunk * kSub;
 constexpr int kWaves = 4;      // waves per workgroup; the workgroup shares each chunk
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 16;     // queries (pass 1) or keys (pass 2) per operand block
 constexpr int kRowBlocks = 4; // operand blocks per wave: each loaded chunk serves 64 rows
 constexpr float kSlack = 8.f; // row pass: log2 headroom before the running max is moved
 
-// One 32-row chunk of a [T, D] bf16 operand, loaded once per workgroup (kPer
-// 16-byte pieces per thread) into one of two LDS tiles.  Rows are padded by
+// One stage (kStage rows) of a [T, D] bf16 operand, loaded once per workgroup
+// (kPer 16-byte pieces per thread) into one of two LDS tiles.  Rows are padded by
 // 16 bytes, so the MFMA operand reads (16 rows, 16 bytes per lane) fall in
 // distinct banks.  Rows past T read zeros.
 template <int D>
 struct ChunkTiles {
   static constexpr int kRowB = D * 2 + 16;
-  static constexpr int kTileB = kChunk * kRowB;
-  static constexpr int kPieces = kChunk * D / 8;
+  static constexpr int kTileB = kStage * kRowB;
+  static constexpr int kPieces = kStage * D / 8;
   static constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
   unsigned char* lds;   // two tiles of kTileB bytes
   u32x4 stage[kPer];
@@ -125,82 +128,86 @@ __global__ __launch_bounds__(kThreads) void prefill_lse_kernel(const uint16_t* _
   // A wave past T has no rows; it still loads and synchronises with the others.
   const int qlast = q0 < T ? min(q0 + kRows * RB, T) - 1 : -1;
   const int wlast = min(wq0 + kWaves * kRows * RB, T) - 1;   // the workgroup walks keys 0..wlast
-  // Each 32-key chunk is loaded once per workgroup into LDS; one barrier per chunk.
+  // Each stage of keys is loaded once per workgroup into LDS; one barrier per stage.
   __shared__ __attribute__((aligned(16))) unsigned char ktiles[2 * ChunkTiles<D>::kTileB];
   ChunkTiles<D> kc{ktiles};
   kc.fetch(kr, 0);
   kc.stash(0);
   // the query operands are complete here, so no wait in the loop counts them
-  // (it would also wait for the next chunk's fetch)
+  // (it would also wait for the next stage's fetch)
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qa[r][kk]));
   __syncthreads();
   int t = 0;
-  for (int k0 = 0; k0 <= wlast; k0 += kChunk, t ^= 1) {
-    const bool more = k0 + kChunk <= wlast;
-    if (more) kc.fetch(kr, k0 + kChunk);
-    if (k0 <= qlast) {
-      // keys k0 + hn and k0 + 16 + hn (masked by causality past T), shared by
-      // the wave's RB blocks of 16 queries
-      bf16x8 ka[KK], kb[KK];
+  for (int k0s = 0; k0s <= wlast; k0s += kStage, t ^= 1) {
+    const bool more = k0s + kStage <= wlast;
+    if (more) kc.fetch(kr, k0s + kStage);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        ka[kk] = kc.operand(t, hn, kk, g);
-        kb[kk] = kc.operand(t, 16 + hn, kk, g);
-      }
-      f32x4 c0[RB], c1[RB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int k0 = k0s + kChunk * sub;
+      if (k0 <= qlast) {
+        // keys k0 + hn and k0 + 16 + hn (masked by causality past T), shared by
+        // the wave's RB blocks of 16 queries
+        bf16x8 ka[KK], kb[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          c0[r] = mfma_bf16(qa[r][kk], ka[kk], c0[r]);
-          c1[r] = mfma_bf16(qa[r][kk], kb[kk], c1[r]);
+          ka[kk] = kc.operand(t, kChunk * sub + hn, kk, g);
+          kb[kk] = kc.operand(t, kChunk * sub + 16 + hn, kk, g);
         }
-      }
+        f32x4 c0[RB], c1[RB];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (k0 > q0 + kRows * r + kRows - 1) continue;   // the whole block is before these keys (uniform)
-        if (k0 + kChunk - 1 <= q0 + kRows * r) {
-          // every key of the chunk is at or before every row of the block: no
-          // mask.  The running max moves only when a score of the block passes
-          // it by more than kSlack (one vote per block); otherwise the chunk
-          // adds its terms against the old max, up to 2^kSlack each.
-          float e0[4], e1[4];
-          bool up = false;
+        for (int r = 0; r < RB; ++r) {
+          c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+          c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            e0[i] = fmaf(c0[r][i], qscale, -m[r][i]);
-            e1[i] = fmaf(c1[r][i], qscale, -m[r][i]);
-            up |= fmaxf(e0[i], e1[i]) > kSlack;   // also true while m is -inf
+          for (int kk = 0; kk < KK; ++kk) {
+            c0[r] = mfma_bf16(qa[r][kk], ka[kk], c0[r]);
+            c1[r] = mfma_bf16(qa[r][kk], kb[kk], c1[r]);
           }
-          if (__builtin_amdgcn_ballot_w64(up)) {
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          if (k0 > q0 + kRows * r + kRows - 1) continue;   // the whole block is before these keys (uniform)
+          if (k0 + kChunk - 1 <= q0 + kRows * r) {
+            // every key of the chunk is at or before every row of the block: no
+            // mask.  The running max moves only when a score of the block passes
+            // it by more than kSlack (one vote per block); otherwise the chunk
+            // adds its terms against the old max, up to 2^kSlack each.
+            float e0[4], e1[4];
+            bool up = false;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float s0 = c0[r][i] * qscale, s1 = c1[r][i] * qscale;
-              const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
-              l[r][i] = fmaf(l[r][i], exp2_hw(m[r][i] - mn), exp2_hw(s0 - mn) + exp2_hw(s1 - mn));
+              e0[i] = fmaf(c0[r][i], qscale, -m[r][i]);
+              e1[i] = fmaf(c1[r][i], qscale, -m[r][i]);
+              up |= fmaxf(e0[i], e1[i]) > kSlack;   // also true while m is -inf
+            }
+            if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float s0 = c0[r][i] * qscale, s1 = c1[r][i] * qscale;
+                const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
+                l[r][i] = fmaf(l[r][i], exp2_hw(m[r][i] - mn), exp2_hw(s0 - mn) + exp2_hw(s1 - mn));
+                m[r][i] = mn;
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) l[r][i] += exp2_hw(e0[i]) + exp2_hw(e1[i]);
+            }
+            continue;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = q0 + kRows * r + 4 * g + i;
+            const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
+            const float s0 = v0 ? c0[r][i] * qscale : -INFINITY, s1 = v1 ? c1[r][i] * qscale : -INFINITY;
+            const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
+            if (mn != -INFINITY) {
+              l[r][i] = (m[r][i] == -INFINITY ? 0.f : l[r][i] * exp2_hw(m[r][i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
+                        (v1 ? exp2_hw(s1 - mn) : 0.f);
               m[r][i] = mn;
             }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) l[r][i] += exp2_hw(e0[i]) + exp2_hw(e1[i]);
-          }
-          continue;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = q0 + kRows * r + 4 * g + i;
-          const bool v0 = k0 + hn <= row, v1 = k0 + 16 + hn <= row;
-          const float s0 = v0 ? c0[r][i] * qscale : -INFINITY, s1 = v1 ? c1[r][i] * qscale : -INFINITY;
-          const float mn = fmaxf(m[r][i], fmaxf(s0, s1));
-          if (mn != -INFINITY) {
-            l[r][i] = (m[r][i] == -INFINITY ? 0.f : l[r][i] * exp2_hw(m[r][i] - mn)) + (v0 ? exp2_hw(s0 - mn) : 0.f) +
-                      (v1 ? exp2_hw(s1 - mn) : 0.f);
-            m[r][i] = mn;
           }
         }
       }
@@ -248,23 +255,25 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(const uint16_t
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
-  // Each 32-query chunk (and its 32 lse values) is loaded once per workgroup
-  // into LDS, one barrier per chunk; the workgroup walks queries wt0..T-1.
+  // Each stage of queries (and their lse values) is loaded once per workgroup
+  // into LDS, one barrier per stage; the workgroup walks the query stages from
+  // the last one down to wt0.
   // Queries past T read zeros and lse 0 and are masked.
   __shared__ __attribute__((aligned(16))) unsigned char qtiles[2 * ChunkTiles<D>::kTileB];
-  __shared__ float ltiles[2][kChunk];
+  __shared__ float ltiles[2][kStage];
   ChunkTiles<D> qc{qtiles};
   float lstage = 0.f;
   auto fetch = [&](int q0) {
     qc.fetch(qr, q0);
-    if (threadIdx.x < kChunk)
+    if (threadIdx.x < kStage)
       lstage = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + threadIdx.x) * 4, 0, 0));
   };
   auto stash = [&](int t) {
     qc.stash(t);
-    if (threadIdx.x < kChunk) ltiles[t][threadIdx.x] = lstage;
+    if (threadIdx.x < kStage) ltiles[t][threadIdx.x] = lstage;
   };
-  fetch(wt0);
+  const int qtop = (T - 1) & ~(kStage - 1);   // the walk runs down from the last stage to wt0
+  fetch(qtop);
   stash(0);
   // the key operands are complete here, so no wait in the loop counts them
 #pragma unroll
@@ -273,46 +282,50 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(const uint16_t
     for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(ka[r][kk]));
   __syncthreads();
   int t = 0;
-  for (int q0 = wt0; q0 < T; q0 += kChunk, t ^= 1) {
-    const bool more = q0 + kChunk < T;
-    if (more) fetch(q0 + kChunk);
-    if (q0 + kChunk - 1 >= t0 && t0 < T) {   // some query of the chunk is at or after the wave's first key
-      // queries q0 + hn and q0 + 16 + hn, shared by the wave's RB blocks of 16 keys
-      bf16x8 qa[KK], qb[KK];
+  for (int q0s = qtop; q0s >= wt0; q0s -= kStage, t ^= 1) {
+    const bool more = q0s - kStage >= wt0;
+    if (more) fetch(q0s - kStage);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        qa[kk] = qc.operand(t, hn, kk, g);
-        qb[kk] = qc.operand(t, 16 + hn, kk, g);
-      }
-      const float l0 = ltiles[t][hn], l1 = ltiles[t][16 + hn];
-      f32x4 c0[RB], c1[RB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int q0 = q0s + kChunk * sub;
+      if (q0 + kChunk - 1 >= t0 && t0 < T) {   // some query of the chunk is at or after the wave's first key
+        // queries q0 + hn and q0 + 16 + hn, shared by the wave's RB blocks of 16 keys
+        bf16x8 qa[KK], qb[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          c0[r] = mfma_bf16(ka[r][kk], qa[kk], c0[r]);
-          c1[r] = mfma_bf16(ka[r][kk], qb[kk], c1[r]);
+          qa[kk] = qc.operand(t, kChunk * sub + hn, kk, g);
+          qb[kk] = qc.operand(t, kChunk * sub + 16 + hn, kk, g);
         }
-      }
-      const int qa_i = q0 + hn, qb_i = q0 + 16 + hn;
+        const float l0 = ltiles[t][kChunk * sub + hn], l1 = ltiles[t][kChunk * sub + 16 + hn];
+        f32x4 c0[RB], c1[RB];
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (q0 + kChunk <= T && q0 >= t0 + kRows * r + kRows - 1) {
-          // every query of the chunk exists and is at or after every key of the block
+        for (int r = 0; r < RB; ++r) {
+          c0[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+          c1[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            c0[r] = mfma_bf16(ka[r][kk], qa[kk], c0[r]);
+            c1[r] = mfma_bf16(ka[r][kk], qb[kk], c1[r]);
+          }
+        }
+        const int qa_i = q0 + hn, qb_i = q0 + 16 + hn;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          if (q0 + kChunk <= T && q0 >= t0 + kRows * r + kRows - 1) {
+            // every query of the chunk exists and is at or after every key of the block
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
+              acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
+            }
+            continue;
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
-            acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
+            const int key = t0 + kRows * r + 4 * g + i;
+            if (qa_i >= key && qa_i < T) acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
+            if (qb_i >= key && qb_i < T) acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
           }
-          continue;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t0 + kRows * r + 4 * g + i;
-          if (qa_i >= key && qa_i < T) acc[r][i] += exp2_hw(fmaf(c0[r][i], qscale, -l0));
-          if (qb_i >= key && qb_i < T) acc[r][i] += exp2_hw(fmaf(c1[r][i], qscale, -l1));
         }
       }
     }
