@@ -3,8 +3,9 @@
 
 Shapes span head groups of 1, 2, 4, 7 and 8, head_dim 64 and 128, windows of
 64 and 128 and ragged token counts (last window partial, last query block
-partial), a single token, token counts at and one past the kernels' workgroup
-span (256 rows); one case has the Llama-3.1-8B head layout at 2048 tokens.  Token weights and
+partial), a single token, token counts at and one past the kernels' 64-row
+stages and 192-row workgroups; one case has the Llama-3.1-8B head layout at
+2048 tokens.  Token weights and
 window scores are float sums of up to T probabilities per token: the bar is
 relative 1e-5 plus T * 1e-6 absolute (float32 accumulation), checked against
 the oracle in float64.  Routing on the library's scores is then bit-exact
@@ -34,9 +35,12 @@ CASES = [
     ("g4_d64_w64", 33, 2, 4, 1, 64, 64, 257),
     ("g1_d64_w64", 34, 1, 2, 2, 64, 64, 33),
     ("llama_2k", 35, 1, 32, 8, 128, 128, 2048),
-    # workgroup and LDS-stage edges: one token; exactly one 256-row workgroup;
-    # exactly two; one row past two at head_dim 64 (64-row stages, 4 waves of 64 rows)
+    # edges of the kernels' 64-row LDS stages and 192-row workgroups (4 waves
+    # of 48 rows): one token; exactly one workgroup; one row past two; whole
+    # stages (256, 512) and one row past (513, head_dim 64)
     ("g4_d128_t1", 36, 1, 4, 1, 128, 64, 1),
+    ("g4_d128_t192", 40, 1, 8, 2, 128, 64, 192),
+    ("g4_d64_t385", 41, 2, 4, 1, 64, 64, 385),
     ("g8_d128_t256", 37, 1, 8, 1, 128, 64, 256),
     ("g4_d128_t512", 38, 1, 8, 2, 128, 128, 512),
     ("g2_d64_t513", 39, 2, 4, 2, 64, 64, 513),
