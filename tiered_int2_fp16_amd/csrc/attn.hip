@@ -682,6 +682,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
         cs = __builtin_amdgcn_fdot2(qq2, f16x2{s8[2 * e2], s8[2 * e2 + 1]}, cs, false);
       }
     }
+    // A wave raises its priority for the QK and PV sections (code decode and
+    // MFMA), so the SIMD's two waves take turns: one there while the other
+    // runs its softmax (attention 1.5 % faster at 32K; on the bf16 tiles it
+    // made no measurable difference and is not used).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const f16x8 s8 = ks[4 * kk + g];
@@ -695,6 +700,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       s1 = mfma_f16(a1, qh, s1);
       s1 = mfma_f16(a1, ql, s1);
     }
+    __builtin_amdgcn_s_setprio(0);
     // the MFMA result lanes (g, hn) hold head hh, as the B operand lanes do
     const float bias0 = sum_rows(sum_groups_t<NREP>(fmaf(cm, 1.f / kCodeScale, -cs)));
     const float z[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -713,6 +719,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     // sum_t 2^b p m' + sum_t 2^b p (-2^b s'), straight from the fp16 scales
     // (-2^b s' is exact; exact products; row = 32-channel group jr, rows >=
     // D/32 repeat and are not read).
+    __builtin_amdgcn_s_setprio(1);
     {
       const int jr = hn & (D / 32 - 1);
       const f16x8 vm8 = vm[4 * jr + g], vn8 = vs[4 * jr + g] * (_Float16)(-kCodeScale);
@@ -735,6 +742,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
         st.o[nb] = mfma_f16(av, pl, st.o[nb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (rec_mass) rec[rt][hn] = make_float2(rs, st.m_run);
   };
 
