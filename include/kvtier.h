@@ -219,6 +219,23 @@ kv_status kv_decode_step(kv_pool* pool, int32_t layer, const void* q,
                          float* out, float* mass,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* kv_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The attention workspace is a static
+ * device array of KV_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held
+ * until the process ends; its device address is looked up once per device by
+ * kv_pool_create.  The call allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine) and returns KV_ENOMEM, enqueuing nothing, when
+ * kv_attn_workspace_bytes(pool) exceeds KV_NOALLOC_SCRATCH_BYTES.  Every call
+ * on one GPU shares that GPU's array, and its contents are those the last
+ * call left (nothing in it needs to start at zero): calls that overlap on one
+ * GPU, from any pool or stream, race and must be serialised by the caller.
+ * Other arguments, results and errors as kv_decode_step. */
+enum { KV_NOALLOC_SCRATCH_BYTES = 16 << 20 };
+kv_status kv_decode_step_noalloc(kv_pool* pool, int32_t layer, const void* q,
+                                 const void* k_new, const void* v_new,
+                                 float* out, float* mass, void* stream);
+
 /* Kernel timing of kv_tiered_decode_attn and kv_decode_step (a profiling aid).  capacity > 0
  * makes each later attention dispatch carry its own start/stop events
  * (hipExtLaunchKernel), for up to `capacity` dispatches between reads;

@@ -29,7 +29,7 @@ EXPORTS = [
     "kv_attn_workspace_bytes", "kv_tiered_decode_attn", "kv_score_route", "kv_read_ledger",
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
     "kv_attn_profile", "kv_attn_timings", "kv_decode_step", "kv_route_diagnostics",
-    "kv_prefill_scores_workspace_bytes", "kv_prefill_scores",
+    "kv_prefill_scores_workspace_bytes", "kv_prefill_scores", "kv_decode_step_noalloc",
 ]
 
 
@@ -66,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "kv_attn_workspace_bytes": (SZ, [P]),
         "kv_tiered_decode_attn": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
+        "kv_decode_step_noalloc": (I32, [P, I32, P, P, P, P, P, P]),
         "kv_score_route": (I32, [P, I32, P, I32, D, D, P, P, P]),
         "kv_route_diagnostics": (I32, [P, I32, P, P, P, P]),
         "kv_prefill_scores_workspace_bytes": (SZ, [P, I32]),
@@ -173,6 +174,14 @@ def kv_tiered_decode_attn(h, layer, q, out, mass, workspace, k_new=None, v_new=N
 def kv_decode_step(h, layer, q, out, mass, workspace, k_new=None, v_new=None, stream=None):
     _ck(LIB.kv_decode_step(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(mass),
                            _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def kv_decode_step_noalloc(h, layer, q, out, mass, k_new=None, v_new=None, stream=None):
+    _ck(LIB.kv_decode_step_noalloc(h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(mass),
+                                   _stream(stream)))
+
+
+KV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def kv_score_route(h, layer, mass, do_route, budget_frac, hi_frac, transitions=None, counts=None,

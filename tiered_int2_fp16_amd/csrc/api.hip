@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -71,6 +72,36 @@ PoolView view(const kv_pool* p) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+}  // namespace
+
+// Attention workspace of kv_decode_step_noalloc: a static device array, one
+// copy per GPU the library runs on.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels and copies get the device address that
+// hipGetSymbolAddress returns for the current device, kept per device below.
+static __device__ __align__(256) uint8_t scratch[KV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (which must be current),
+// looked up on the first call for that device.
+kv_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(KV_EDEVICE, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(KV_EDEVICE, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KV_OK;
+}
+
 kv_status check_pool_layer(const kv_pool* p, int32_t layer) {
   if (!p) return fail(KV_EINVAL, "pool is NULL");
   if (layer < 0 || layer >= p->g.cfg.layers) return fail(KV_EINVAL, "layer out of range");
@@ -130,6 +161,9 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* arena, size_t arena_by
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  // set-up of kv_decode_step_noalloc: this device's scratch address, once
+  void* scratch_ptr = nullptr;
+  if (kv_status st = scratch_address(dev, &scratch_ptr)) return st;
   // clear page table, scores, token counts, work region and error word
   char* base = static_cast<char*>(arena);
   const size_t meta0 = g.off[KV_REGION_PAGES];
@@ -291,6 +325,23 @@ kv_status kv_decode_step(kv_pool* pool, int32_t layer, const void* q, const void
                          const void* v_new, float* out, float* mass, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return attention(pool, layer, q, k_new, v_new, out, mass, workspace, workspace_bytes, 1, stream);
+}
+
+kv_status kv_decode_step_noalloc(kv_pool* pool, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, float* out, float* mass, void* stream) {
+  kv_status st = check_pool_layer(pool, layer);
+  if (st) return st;
+  const size_t need = attn_workspace(pool->g, pool->splits).total;
+  if (need > size_t(KV_NOALLOC_SCRATCH_BYTES))
+    return fail(KV_ENOMEM, "the step needs " + std::to_string(need) + " bytes of workspace; the static scratch holds " +
+                               std::to_string(size_t(KV_NOALLOC_SCRATCH_BYTES)) + " (use kv_decode_step)");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ws = (pool->device >= 0 && pool->device < kMaxDevices) ? g_scratch_ptr[pool->device] : nullptr;
+  }
+  if (!ws) return fail(KV_EDEVICE, "no scratch address for the pool's device");
+  return attention(pool, layer, q, k_new, v_new, out, mass, ws, size_t(KV_NOALLOC_SCRATCH_BYTES), 1, stream);
 }
 
 kv_status kv_attn_profile(kv_pool* pool, int32_t capacity) {
