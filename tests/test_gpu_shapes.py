@@ -3,6 +3,8 @@
 * Query-head group sizes 1, 2, 7 and 8 at head_dim 64 and 128: the attention
   kernel lays the group's heads out differently for G <= 4 and G > 4 (column
   groups of the MFMA operands), and head_dim 64 halves the channel groups.
+* Windows of 32, 96, 160 and 256 tokens (one, three, five and eight 32-token
+  tiles), with INT2 and 4-bit ledgers.
 * More than 64 tiles of one tier per wave: at 64 sequences x 8 kv heads the
   kernel runs one split per (sequence, kv head), so a wave walks its tile list
   in chunks of 64 - first for INT2 tiles, then (after promotions) for bf16.
@@ -55,6 +57,44 @@ def test_head_group_shapes(name, seed, hq, hkv, d, w):
             p.route(0, c.budget_frac, c.hi_frac)
             p.check_state(0)
     log("%s: out err %.2e mass err %.2e" % (name, *worst))
+
+
+# (name, seed, q_heads, kv_heads, head_dim, window): windows of one tile (32),
+# of a tile count that is not a power of two (96, 160) and of eight tiles (256,
+# the most a window may have: the tile field of the attention's tile lists and
+# the combine's per-window loop)
+WINDOWS = [
+    ("w32_g4_d128", 16, 8, 2, 128, 32),
+    ("w96_g4_d64", 17, 4, 1, 64, 96),
+    ("w160_g8_d128", 18, 16, 2, 128, 160),
+    ("w256_g4_d128", 19, 8, 2, 128, 256),
+    ("w256_g7_d64", 20, 7, 1, 64, 256),
+]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("name,seed,hq,hkv,d,w", WINDOWS, ids=[s[0] for s in WINDOWS])
+def test_window_sizes(name, seed, hq, hkv, d, w, bits):
+    """Route, then 40 decode steps with appends (new windows open at W = 32),
+    routing every 16 steps, with an INT2 and a 4-bit ledger; the routed state
+    (tiers, ledger bytes, bf16 windows) is compared bit for bit after every
+    routing event."""
+    c = dataclasses.replace(CONFIGS["tiny"], name=name, seed=seed, batch=2, q_heads=hq, kv_heads=hkv,
+                            head_dim=d, window=w, context=24 * w - 17, budget_frac=0.3, hi_frac=0.2,
+                            steps=40, route_every=16, append=True)
+    p = Pair(c, bits=bits)
+    p.load(0)
+    p.route(0, c.budget_frac, c.hi_frac)
+    p.check_state(0)
+    worst = (0.0, 0.0)
+    for s in range(c.steps):
+        _, mass, o_mass, errs = p.step(0, s, append=True)
+        worst = (max(worst[0], errs[0]), max(worst[1], errs[1]))
+        p.add_scores(0, mass, o_mass)
+        if (s + 1) % c.route_every == 0:
+            p.route(0, c.budget_frac, c.hi_frac)
+            p.check_state(0)
+    log("%s, %d-bit ledger: out err %.2e mass err %.2e" % (name, bits, *worst))
 
 
 def test_many_tiles_per_wave():

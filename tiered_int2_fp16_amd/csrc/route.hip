@@ -40,14 +40,20 @@ __global__ __launch_bounds__(256) void score_kernel(PoolView pv, int layer, cons
   pv.scores[size_t(seg) * pv.maxw + w] += acc;
 }
 
-// Tier counts, IEEE double in the documented order (explicit roundings: no
-// contraction into fused multiply-adds).
+// Tier counts, IEEE double in the documented order, every operation rounded
+// on its own.  HIP compiles with fp-contract=fast, which would fuse
+// beta * n - n_hi into one fused multiply-add (the __d*_rn functions are the
+// plain operators, contractible, in this toolchain): at n = 25, beta = 0.3
+// and a 4-bit ledger that gives floor(7.999..) = 7 ledger windows where the
+// formula gives 8.  Contraction is off for the operators below.
 __device__ inline void device_tier_counts(int n, int R, int lbits, double beta, double phi, int* hi, int* lo) {
-  const double a = __dmul_rn(phi, double(n));
+#pragma clang fp contract(off)
+  const double a = phi * double(n);
   int h = int(floor(a));
   h = h > R ? h : R;
   h = h < n ? h : n;
-  const double x = __ddiv_rn(__dmul_rn(__dsub_rn(__dmul_rn(beta, double(n)), double(h)), 16.0), double(lbits + 1));
+  const double bn = beta * double(n);
+  const double x = ((bn - double(h)) * 16.0) / double(lbits + 1);
   int l = int(floor(x));
   l = l < n - h ? l : n - h;
   l = l > 0 ? l : 0;
