@@ -73,7 +73,8 @@ enum {
  * q_heads / kv_heads in {1, 2, 4, 7, 8}; head_dim in {64, 128}; window a
  * multiple of 32 in [32, 256]; 1 <= max_windows <= 4096 with
  * max_windows * window / 32 <= 8192; bf16_slots <= 16383
- * and ledger_slots <= 32767 per segment; n_recent >= 0; ledger_bits 0 (= 2),
+ * and ledger_slots <= 32767 per segment; n_recent >= 1 (the newest window,
+ * which appends write into, always stays bf16); ledger_bits 0 (= 2),
  * 2, 4 or 8.
  * ledger_bits is the code width of the pool's quantised tier: INT2 is the
  * width of the QEvict summary's experiments ("Methodologie: QEvict", tier 2);
@@ -126,9 +127,15 @@ size_t kv_pool_arena_bytes(const kv_pool_config* cfg);
 size_t kv_ledger_entry_bytes(int32_t window, int32_t head_dim, int32_t ledger_bits);
 
 /* Create a pool over a caller-owned device arena of at least
- * kv_pool_arena_bytes(cfg) bytes, 256-byte aligned.  Enqueues the clearing of
- * the metadata regions (every window evicted, no tokens, zero scores, zero
- * error word) on `stream`.  *out receives the handle. */
+ * kv_pool_arena_bytes(cfg) bytes, 256-byte aligned: the window pool of the
+ * three-tier cache ("Technische Samenvatting: QEvict", "Methodologie: QEvict":
+ * consecutive windows, each in the full-precision, recoverable quantised or
+ * evicted tier under a fixed budget; "Kernmechanismen", window-level routing
+ * and the write-once quantisation ledger), with a page table (window -> tier,
+ * bf16 slot, ledger slot) per segment.  Enqueues the clearing of the metadata
+ * regions (every window evicted, no tokens, zero scores, zero error word) on
+ * `stream`.  Also looks up, once per device, the address of the static
+ * scratch of kv_decode_step_noalloc.  *out receives the handle. */
 kv_status kv_pool_create(const kv_pool_config* cfg, void* arena, size_t arena_bytes,
                          void* stream, kv_pool** out);
 
@@ -193,7 +200,14 @@ size_t kv_attn_workspace_bytes(const kv_pool* pool);
 /* One decode step of grouped-query attention for every sequence of `layer`
  * over its bf16 and ledger windows; evicted windows take no part (the softmax
  * normaliser runs over the remaining tokens).  Query head h reads kv head
- * h / (q_heads / kv_heads).
+ * h / (q_heads / kv_heads).  ("Technische Samenvatting: QEvict",
+ * "Methodologie: QEvict": quantised windows stay reachable by attention, only
+ * evicted ones are gone; "Kernmechanismen", Implementatie: grouped-query
+ * attention; Cumulatieve Scoring: the attention each window receives is what
+ * the scores accumulate, emitted here as `mass`.  Ledger tiles are decoded in
+ * registers inside the kernel rather than dequantised into a rebuilt cache
+ * first, the cost the summary's "Resultaten" names for its FlashAttention-2
+ * path.)
  *   q      bf16 [batch][q_heads][D]
  *   k_new, v_new  bf16 [batch][kv_heads][D], the token this step appends (it
  *          is attended and then stored in the newest window, opening a new
@@ -211,7 +225,9 @@ kv_status kv_tiered_decode_attn(kv_pool* pool, int32_t layer, const void* q,
 
 /* One decode step: kv_tiered_decode_attn, with the cumulative score update of
  * kv_score_route (S[w] += sum over the layer's query heads of mass[h][w],
- * heads in order, for live windows) fused into its combining kernel.  Same
+ * heads in order, for live windows) fused into its combining kernel
+ * ("Technische Samenvatting: QEvict", "Kernmechanismen", Cumulatieve Scoring:
+ * a window's importance is its attention accumulated over time).  Same
  * arguments; mass may be NULL (the scores are still updated).  S ends up
  * bit-identical to kv_tiered_decode_attn followed by kv_score_route. */
 kv_status kv_decode_step(kv_pool* pool, int32_t layer, const void* q,
@@ -308,6 +324,21 @@ kv_status kv_read_window(kv_pool* pool, int32_t layer, int32_t b, int32_t window
  * on the host in the same double-precision order. [host, pure] */
 kv_status kv_tier_counts(int32_t n, int32_t n_recent, double budget_frac, double hi_frac,
                          int32_t ledger_bits, int32_t* n_hi, int32_t* n_lo);
+
+/* Streaming-read probe, a measurement aid and not a step of the method: the
+ * rate one cold launch of a plain read reaches on this GPU, the attainable
+ * ceiling beside the nominal HBM peak for a decode step that re-reads its
+ * cache ("Technische Samenvatting: RDKV", 1 Probleemstelling).  Enqueues
+ * `count` launches back to back on `stream`; launch i reads `bytes` bytes at
+ * src + i * stride with `workgroups` workgroups of 256 threads (each
+ * workgroup a contiguous share, 16-byte loads, 16 per thread in flight) and
+ * stores one word per wave into sink (uint32 [workgroups * 4], device).  With
+ * ms != NULL [host, count entries] every launch carries start/stop events
+ * (hipExtLaunchKernel); the call then synchronises the stream and writes each
+ * launch's duration in milliseconds.  KV_EINVAL for NULL src or sink, bytes
+ * or count < 1, workgroups outside [1, 65536] or a share above 2 GiB. */
+kv_status kv_stream_probe(const void* src, size_t bytes, size_t stride, int32_t count,
+                          int32_t workgroups, uint32_t* sink, void* stream, float* ms);
 
 /* Synchronise `stream`, read and clear the device error word.  Returns KV_OK or
  * KV_ESTATE (kv_last_error lists the bits); *bits (may be NULL) gets them. */

@@ -50,3 +50,26 @@ def window_scores(w: np.ndarray, window: int) -> np.ndarray:
     n = -(-t // window)
     per_token = w.sum(axis=0)
     return np.array([per_token[i * window: (i + 1) * window].sum() for i in range(n)])
+
+
+def head_token_weights(q: np.ndarray, k: np.ndarray, block: int = 1024) -> np.ndarray:
+    """w [T] of one query head: q [T][D] its prefill queries, k [T][D] the keys
+    of its kv head (float64 values).
+
+    The same column sums as token_weights, w_t = sum over tau >= t of a_{tau,t},
+    taken over blocks of `block` query rows: every row's causal softmax lies
+    wholly inside its block, and the blocks' column sums are added, so a long
+    prefill (32K tokens: a 32K x 32K attention matrix per head) fits in memory.
+    """
+    t, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    w = np.zeros(t)
+    for r0 in range(0, t, block):
+        r1 = min(t, r0 + block)
+        z = (q[r0:r1] @ k[:r1].T) * scale                 # rows tau in [r0, r1), keys 0..r1-1
+        causal = np.arange(r1)[None, :] <= np.arange(r0, r1)[:, None]
+        z = np.where(causal, z, -np.inf)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        w[:r1] += p.sum(axis=0)
+    return w

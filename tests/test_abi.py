@@ -68,7 +68,7 @@ def test_arena_size_matches_layout(B):
 @pytest.mark.parametrize("field,value", [
     ("q_heads", 30), ("head_dim", 96), ("window", 48), ("max_windows", 0),
     ("max_windows", 5000), ("bf16_slots", 0), ("bf16_slots", 20000), ("kv_heads", 0),
-    ("ledger_bits", 3), ("ledger_bits", 16), ("ledger_bits", -2)])
+    ("ledger_bits", 3), ("ledger_bits", 16), ("ledger_bits", -2), ("n_recent", 0)])
 def test_invalid_configs_are_rejected(B, field, value):
     cfg = _cfg(B, CONFIGS["tiny"])
     setattr(cfg, field, value)

@@ -96,6 +96,54 @@ def test_device_state_errors_are_reported():
     assert p.pool.check() & 64
 
 
+def test_device_state_errors_demote_slots_append_capacity():
+    """The other four error bits, each forced through the C ABI (or, for an
+    append into a window that is not bf16 - a state no call of the library
+    produces, since the newest window always stays bf16 - by writing that
+    page-table entry of the caller-owned arena from the host).  Each bit is
+    read and cleared by kv_pool_check, and the offending item is skipped."""
+    from workload import new_kv
+    one = dev(np.array([1], np.int32))
+    # 1 DEMOTE_STATE: a window already in the ledger tier, then the newest,
+    # partial window
+    c = dataclasses.replace(CONFIGS["tiny"], context=2048 - 17)
+    p = Pair(c)
+    p.load(0)
+    w3 = dev(np.array([[3]], np.int32))
+    p.pool.demote(0, w3, one)
+    assert p.pool.check() == 0
+    p.pool.demote(0, w3, one)
+    assert p.pool.check() == 1
+    p.pool.demote(0, dev(np.array([[31]], np.int32)), one)
+    assert p.pool.check() == 1
+    pages = p.pool.pages(0).cpu().numpy().view(np.uint32)[0]
+    assert pages[31] & 3 == F and pages[3] & 3 == Q
+    # 16 APPEND_STATE: the partial window 31 set to the ledger tier (window 3's
+    # entry) from the host; the step's token is not stored
+    p.pool.pages(0)[0, 31] = int((pages[3] & ~np.uint32(0x1FFF8)))   # tier Q, has-ledger, slot of window 3
+    kn, vn = new_kv(c, 0, 0)
+    p.pool.attn(0, dev(__import__("workload").query(c, 0, 0)), dev(kn), dev(vn))
+    assert p.pool.check() == 16
+    assert int(p.pool.tokens(0)[0]) == c.context
+    # 4 NO_BF16_SLOT: a full context whose 32 windows take every bf16 slot;
+    # the append that opens window 32 finds none
+    ca = dataclasses.replace(CONFIGS["tiny"], steps=1, append=True)
+    p = Pair(ca, bf16_slots=32)
+    p.load(0)
+    kn, vn = new_kv(ca, 0, 0)
+    p.pool.attn(0, dev(__import__("workload").query(ca, 0, 0)), dev(kn), dev(vn))
+    assert p.pool.check() == 4
+    assert int(p.pool.tokens(0)[0]) == ca.context
+    # 128 CAPACITY: the page table has no room for window 32
+    p = Pair(CONFIGS["tiny"])
+    assert p.maxw == 32
+    p.load(0)
+    p.pool.attn(0, dev(__import__("workload").query(ca, 0, 0)), dev(kn), dev(vn))
+    assert p.pool.check() == 128
+    assert int(p.pool.tokens(0)[0]) == ca.context
+    assert p.pool.check() == 0
+
+
 def test_llama_32k_full():
     c = CONFIGS["llama8b_32k"]
     p = Pair(c)
@@ -166,11 +214,11 @@ def test_mistral_full_step_sampled():
     """The Mistral-7B full step at full size: 32 layers x 32 sequences, 16K
     context.  Per (layer, sequence): route to the pre-state (12 bf16 / 21 INT2 /
     95 evicted windows), demote the 8 non-recent bf16 windows (first
-    quantisation into the ledger), promote the 4 highest-score INT2 windows,
-    then one attention step.  The contexts are drawn on the device (they are
-    34 G values); the oracle checks sampled (layer, sequence) pairs on copies
-    of their inputs: routing bit-exact, ledger bytes, promoted bf16, output and
-    window mass."""
+    quantisation into the ledger), promote the 4 highest-score windows of the
+    pre-state INT2 tier (older ledger entries), then one attention step.  The
+    contexts are drawn on the device (they are 34 G values); the oracle checks
+    sampled (layer, sequence) pairs on copies of their inputs: routing
+    bit-exact, ledger bytes, promoted bf16, output and window mass."""
     from workload import kv_history_device
     c = CONFIGS["mistral7b_step"]
     checked = {0: [0, 31], 13: [7], 31: [0, 20]}
@@ -197,7 +245,9 @@ def test_mistral_full_step_sampled():
         assert (pages == F).sum(axis=1).tolist() == [12] * c.batch
         assert (pages == Q).sum(axis=1).tolist() == [21] * c.batch
         # the move set: demote the 8 non-recent bf16 windows, then promote the
-        # 4 highest-score INT2 windows (score descending, lower index first)
+        # 4 highest-score windows of the pre-state INT2 tier (score descending,
+        # lower index first), whose ledger entries were written by the
+        # pre-state routing - not the windows demoted a moment earlier
         S = p.pool.scores(layer).cpu().numpy()[:, :n]
         dem = np.zeros((c.batch, n), np.int32)
         pro = np.zeros((c.batch, n), np.int32)
@@ -205,8 +255,8 @@ def test_mistral_full_step_sampled():
             d = [w for w in range(n - R) if pages[b][w] == F]
             assert len(d) == c.demote_per_seg
             dem[b, : len(d)] = d
-            q_after = [w for w in range(n) if pages[b][w] == Q or w in d]
-            top = sorted(q_after, key=lambda w: (-float(S[b][w]), w))[: c.promote_per_seg]
+            q_pre = [w for w in range(n) if pages[b][w] == Q]   # ledger entries from the pre-state routing
+            top = sorted(q_pre, key=lambda w: (-float(S[b][w]), w))[: c.promote_per_seg]
             pro[b, : len(top)] = sorted(top)
         cnt_d = np.full(c.batch, c.demote_per_seg, np.int32)
         cnt_p = np.full(c.batch, c.promote_per_seg, np.int32)

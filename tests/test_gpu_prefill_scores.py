@@ -5,7 +5,7 @@ Shapes span head groups of 1, 2, 4, 7 and 8, head_dim 64 and 128, windows of
 64 and 128 and ragged token counts (last window partial, last query block
 partial), a single token, token counts at and one past the kernels' 64-row
 stages and 192-row workgroups; one case has the Llama-3.1-8B head layout at
-2048 tokens.  Token weights and
+2048 tokens, and the benchmark's 32768-token pass (two heads checked).  Token weights and
 window scores are float sums of up to T probabilities per token: the bar is
 relative 1e-5 plus T * 1e-6 absolute (float32 accumulation), checked against
 the oracle in float64.  Routing on the library's scores is then bit-exact
@@ -25,7 +25,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 from oracle.codec import bf16_to_f64  # noqa: E402
-from oracle.prefill_scores import token_weights, window_scores  # noqa: E402
+from oracle.prefill_scores import head_token_weights, token_weights, window_scores  # noqa: E402
 from tests.gpu_harness import Pair, dev, log  # noqa: E402
 
 # (name, seed, batch, q_heads, kv_heads, head_dim, window, tokens)
@@ -74,6 +74,34 @@ def test_prefill_scores(name, seed, batch, hq, hkv, d, w, T):
     # routing on the library's own scores: bit-exact tiers and transitions
     p.route(0, c.budget_frac, c.hi_frac)
     p.check_state(0)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_scores_llama_32k():
+    """The size the benchmark times: the Llama-3.1-8B head layout (32 query /
+    8 kv heads, head_dim 128) over a 32768-token prefill.  Query heads 0 and
+    31 (kv heads 0 and 7) against the oracle in float64, computed over blocks
+    of query rows; every head's weights sum to T; the window scores are the
+    window sums of the kernel's own token weights over all heads."""
+    c = dataclasses.replace(CONFIGS["llama8b_32k"], name="prefill_32k", seed=42)
+    T, n = c.context, c.n_windows
+    p = Pair(c, seqs=[])
+    k = kv_history(c, 0, 0)[0]
+    p.pool.prefill(0, dev(k[None]), dev(kv_history(c, 0, 0)[1][None]), T)
+    q = prefill_queries(c, 0, 0)
+    ws = p.pool.prefill_scores(0, dev(q[None]), dev(k[None]), T)
+    f = ws.view(torch.float32).cpu().numpy().reshape(2, 1, c.q_heads, T)
+    w_gpu = f[1][0].astype(np.float64)
+    np.testing.assert_allclose(w_gpu.sum(axis=1), T, rtol=1e-5)
+    s_gpu = p.pool.scores(0).cpu().numpy()[0][:n].astype(np.float64)
+    np.testing.assert_allclose(s_gpu, window_scores(w_gpu, c.window), rtol=1e-5)
+    for h in (0, c.q_heads - 1):
+        w_o = head_token_weights(bf16_to_f64(q[h]), bf16_to_f64(k[h // c.group]))
+        ew = np.abs(w_gpu[h] - w_o)
+        log("32K prefill, head %d: max token-weight error %.2e (relative %.2e), weights %.3g..%.3g"
+            % (h, ew.max(), (ew / w_o).max(), w_o.min(), w_o.max()))
+        assert (ew <= 1e-5 * w_o + 1e-6 * T).all(), (h, ew.max())
+    assert p.pool.check() == 0
 
 
 def test_prefill_scores_reject_bad_arguments():

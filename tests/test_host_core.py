@@ -89,6 +89,7 @@ int main() {
     {"max_windows 4097", [](kv_pool_config& c) { c.max_windows = 4097; }},
     {"tiles", [](kv_pool_config& c) { c.window = 256; c.max_windows = 1025; }},
     {"n_recent", [](kv_pool_config& c) { c.n_recent = -1; }},
+    {"n_recent 0", [](kv_pool_config& c) { c.n_recent = 0; }},
     {"bf16_slots 0", [](kv_pool_config& c) { c.bf16_slots = 0; }},
     {"bf16_slots", [](kv_pool_config& c) { c.bf16_slots = 16384; }},
     {"ledger_slots", [](kv_pool_config& c) { c.ledger_slots = 32768; }},

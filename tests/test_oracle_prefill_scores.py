@@ -1,13 +1,14 @@
 """Pins of the oracle's prefill token weights and initial window scores (CPU):
 rows of a causal softmax sum to one (so every head's weights sum to T), equal
 keys give harmonic-number weights in closed form, a scalar brute force on tiny
-inputs, and the window sums."""
+inputs, and the window sums.  The blocked one-head form (for long prefills)
+is pinned by the same closed form across block edges and by the full form."""
 import math
 
 import numpy as np
 import pytest
 
-from oracle.prefill_scores import token_weights, window_scores
+from oracle.prefill_scores import head_token_weights, token_weights, window_scores
 
 
 def test_weights_of_each_head_sum_to_the_number_of_queries():
@@ -58,3 +59,28 @@ def test_window_sums_cover_every_token_once():
     assert s.shape == (3,)
     np.testing.assert_allclose(s, [w[:, 0:8].sum(), w[:, 8:16].sum(), w[:, 16:21].sum()], rtol=1e-14)
     assert s.sum() == pytest.approx(w.sum(), rel=1e-14)
+
+
+def test_blocked_head_weights_equal_the_full_form():
+    """Blocks of query rows that do and do not divide T, and a block longer
+    than T, give the full form's weights for every head."""
+    rng = np.random.default_rng(6)
+    hq, hkv, T, D = 4, 2, 53, 16
+    q = rng.standard_normal((hq, T, D)) * 2
+    k = rng.standard_normal((hkv, T, D)) * 2
+    full = token_weights(q, k)
+    for block in (1, 7, 16, 53, 64):
+        for h in range(hq):
+            np.testing.assert_allclose(head_token_weights(q[h], k[h // 2], block), full[h], rtol=1e-12)
+
+
+def test_blocked_head_weights_harmonic_across_blocks():
+    """Equal keys: w_t = H_T - H_t, over 5000 tokens in blocks of 1024 (the
+    last block partial); the weights sum to T."""
+    T = 5000
+    q = np.random.default_rng(7).standard_normal((T, 8))
+    k = np.tile(np.random.default_rng(8).standard_normal((1, 8)), (T, 1))
+    w = head_token_weights(q, k, 1024)
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, T + 1))])
+    np.testing.assert_allclose(w, H[T] - H[np.arange(T)], rtol=1e-11)
+    assert w.sum() == pytest.approx(T, rel=1e-12)

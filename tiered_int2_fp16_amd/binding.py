@@ -30,6 +30,7 @@ EXPORTS = [
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
     "kv_attn_profile", "kv_attn_timings", "kv_decode_step", "kv_route_diagnostics",
     "kv_prefill_scores_workspace_bytes", "kv_prefill_scores", "kv_decode_step_noalloc",
+    "kv_stream_probe",
 ]
 
 
@@ -67,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "kv_tiered_decode_attn": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_decode_step_noalloc": (I32, [P, I32, P, P, P, P, P, P]),
+        "kv_stream_probe": (I32, [P, SZ, SZ, I32, I32, P, P, ctypes.POINTER(ctypes.c_float)]),
         "kv_score_route": (I32, [P, I32, P, I32, D, D, P, P, P]),
         "kv_route_diagnostics": (I32, [P, I32, P, P, P, P]),
         "kv_prefill_scores_workspace_bytes": (SZ, [P, I32]),
@@ -205,6 +207,19 @@ def kv_read_ledger(h, layer, b, window, dst, stream=None):
 
 def kv_read_window(h, layer, b, window, dst, stream=None):
     _ck(LIB.kv_read_window(h, layer, b, window, _ptr(dst), _stream(stream)))
+
+
+def kv_stream_probe(src: torch.Tensor, nbytes: int, stride: int, count: int, workgroups: int,
+                    sink: torch.Tensor, timed: bool = True, stream=None):
+    """`count` back-to-back streaming reads of `nbytes` at src + i * stride;
+    returns each launch's duration in milliseconds when `timed`."""
+    if (count - 1) * stride + nbytes > src.numel() * src.element_size():
+        raise ValueError("probe reads past the source tensor")
+    if sink.numel() * sink.element_size() < 16 * workgroups:
+        raise ValueError("sink needs 4 words per workgroup")
+    ms = (ctypes.c_float * count)() if timed else None
+    _ck(LIB.kv_stream_probe(_ptr(src), nbytes, stride, count, workgroups, _ptr(sink), _stream(stream), ms))
+    return [ms[i] for i in range(count)] if timed else None
 
 
 def kv_pool_check(h, stream=None) -> int:

@@ -20,13 +20,15 @@ OUT_DIR = os.path.join(HERE, "_lib")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(OUT_DIR, "libkvtier.so")
 
-SOURCES = ["api.hip", "attn.hip", "route.hip", "transitions.hip", "prefill_scores.hip", "host_core.cpp"]
+SOURCES = ["api.hip", "attn.hip", "route.hip", "transitions.hip", "prefill_scores.hip", "probe.hip",
+           "host_core.cpp"]
 ARCH = os.environ.get("KVTIER_ARCH", "gfx950")
 
 
 # Sources whose kernels take leading scalar arguments meant to be preloaded
-# (attn_kernel: page table, token counts, row length).
-KERNARG_PRELOAD = {"attn.hip": 3}
+# (attn_kernel: page table, token counts, row length, query, query heads,
+# head group).
+KERNARG_PRELOAD = {"attn.hip": 6}
 
 
 def hipcc() -> str:

@@ -434,6 +434,44 @@ kv_status kv_read_window(kv_pool* pool, int32_t layer, int32_t b, int32_t window
   return e == hipSuccess ? KV_OK : hip_fail(e, "read launch");
 }
 
+kv_status kv_stream_probe(const void* src, size_t bytes, size_t stride, int32_t count, int32_t workgroups,
+                          uint32_t* sink, void* stream, float* ms) {
+  if (!src || !sink) return fail(KV_EINVAL, "src and sink must not be NULL");
+  if (bytes < 1 || count < 1) return fail(KV_EINVAL, "bytes and count must be >= 1");
+  if (workgroups < 1 || workgroups > 65536) return fail(KV_EINVAL, "workgroups must be in [1, 65536]");
+  if ((bytes + size_t(workgroups) - 1) / size_t(workgroups) > (size_t(1) << 31))
+    return fail(KV_EINVAL, "a workgroup's share must stay within 2 GiB");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<hipEvent_t> ev(ms ? 2 * size_t(count) : 0, nullptr);
+  auto release = [&]() {
+    for (hipEvent_t e : ev)
+      if (e) hipEventDestroy(e);
+  };
+  for (hipEvent_t& e : ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      release();
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  const char* base = static_cast<const char*>(src);
+  for (int32_t i = 0; i < count; ++i) {
+    const hipError_t r = launch_stream_probe(base + size_t(i) * stride, bytes, workgroups, sink,
+                                             ms ? ev[2 * i] : nullptr, ms ? ev[2 * i + 1] : nullptr, s);
+    if (r != hipSuccess) {
+      release();
+      return hip_fail(r, "stream probe launch");
+    }
+  }
+  if (ms) {
+    hipError_t r = hipStreamSynchronize(s);
+    for (int32_t i = 0; r == hipSuccess && i < count; ++i) r = hipEventElapsedTime(&ms[i], ev[2 * i], ev[2 * i + 1]);
+    release();
+    if (r != hipSuccess) return hip_fail(r, "timing the stream probe");
+  }
+  return KV_OK;
+}
+
 kv_status kv_pool_check(kv_pool* pool, void* stream, int32_t* bits) {
   if (!pool) return fail(KV_EINVAL, "pool is NULL");
   kv_status st = set_device(pool);

@@ -23,7 +23,8 @@ bool geometry_init(const kv_pool_config& c, Geometry* g, std::string* err) {
     return bad(err, "window must be a multiple of 32 in [32, 256]");
   if (c.max_windows < 1 || c.max_windows > kMaxWindows)
     return bad(err, "max_windows must be in [1, 4096]");
-  if (c.n_recent < 0) return bad(err, "n_recent must be >= 0");
+  // the newest (partial) window must stay bf16: appends write into it
+  if (c.n_recent < 1) return bad(err, "n_recent must be >= 1");
   if (c.max_windows * (c.window / kTile) > kMaxTiles)
     return bad(err, "max_windows * window / 32 must be <= 8192 (tiles per segment)");
   if (c.bf16_slots < 1 || c.bf16_slots > kMaxBf16Slots)

@@ -45,4 +45,7 @@ hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, 
                               double budget_frac, double hi_frac, int32_t* transitions,
                               int32_t* counts, hipStream_t s);
 
+hipError_t launch_stream_probe(const void* src, uint64_t bytes, int workgroups, uint32_t* sink,
+                               hipEvent_t ev_start, hipEvent_t ev_stop, hipStream_t s);
+
 }  // namespace kvtier
