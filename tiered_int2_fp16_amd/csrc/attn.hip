@@ -102,6 +102,16 @@ __device__ inline float sum_groups_t(float x) {
   return x;
 }
 
+// Materialise uniform values (kernel arguments) in SGPRs at this point.
+template <typename T>
+__device__ inline void in_sgpr(const T& x) {
+  asm volatile("" ::"s"(x));
+}
+template <typename... T>
+__device__ inline void in_sgprs(const T&... x) {
+  (in_sgpr(x), ...);
+}
+
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -275,12 +285,14 @@ __device__ inline void softmax_tile(WaveState<NB>& st, const float (&s)[8], floa
 
 }  // namespace
 
-// The first three arguments (the layer's page table and token counts, the
-// page table's row length) come preloaded in SGPRs (the library is built with
-// kernarg preloading), so the plan's first loads need no kernel-argument load.
+// The first six arguments (the layer's page table and token counts, the page
+// table's row length, the query and its head counts) come preloaded in SGPRs
+// (the library is built with kernarg preloading), so the first loads - page
+// table, token count, query - need no kernel-argument load.
 template <int D, int GP, int BITS>
 __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict__ pages_layer,
                                                       const int32_t* __restrict__ tokens_layer, int maxw_arg,
+                                                      const uint16_t* __restrict__ q_arg, int hq_arg, int g_arg,
                                                       PoolView pv, AttnArgs a) {
   constexpr int KK = D / 32;   // 32-dim slices of the QK product
   constexpr int NB = D / 16;   // 16-channel blocks of the PV product (= code chunks per part)
@@ -294,8 +306,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   __shared__ float s_wo[kAttnWaves][kGMax][D];
   __shared__ float s_wb[kAttnWaves][kGMax][4];
   __shared__ __attribute__((aligned(16))) uint8_t s_scb[kAttnWaves][8 * D];  // ledger tile scales
-  __shared__ uint32_t s_listf[kAttnWaves][kList];                              // a wave's bf16 tiles
-  __shared__ uint32_t s_listq[kAttnWaves][kList];                              // and INT2 tiles
   __shared__ float2 s_rec[kAttnWaves][kList][kGMax];                           // their raw masses
   __shared__ int s_gt[kMaxWindows / 64];                                       // tiles per 64 windows
 
@@ -329,30 +339,42 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   const uint32_t len_raw = load4(tile_rsrc(tokens_layer, (b + 1) * 4), b * 4);
 
   // ------------------------------------------------------------ the query
-  // issued first: it does not depend on the plan.  Lane (g, hn) holds channels
-  // 32kk + 8g .. 32kk + 8g + 7 of head hh: the B operand of the QK products.
-  // Buffer loads without a branch (lanes of heads past G read zeros), so the
-  // plan's wait for the page table is exact and does not wait for the query,
-  // whose address comes later (from the kernel arguments in memory).
+  // also from preloaded arguments: it does not depend on the plan.  Lane
+  // (g, hn) holds channels 32kk + 8g .. 32kk + 8g + 7 of head hh: the B
+  // operand of the QK products.  Buffer loads without a branch (lanes of heads
+  // past G read zeros), so the plan's wait for the page table is exact.
   constexpr float kLog2e = 1.4426950408889634f;
   const float qscale = kLog2e / sqrtf(float(D));
   bf16x8 qb[KK];    // q (bf16)
   {
-    const auto rq = tile_rsrc(a.q + (size_t(b) * pv.Hq + size_t(kvh) * G) * D, G * D * 2);
+    const auto rq = tile_rsrc(q_arg + (size_t(b) * hq_arg + size_t(kvh) * g_arg) * D, g_arg * D * 2);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qb[kk] = as_bf16x8(load16(rq, boff(hh < G, (hh * D + 32 * kk + 8 * g) * 2)));
+    for (int kk = 0; kk < KK; ++kk)
+      qb[kk] = as_bf16x8(load16(rq, boff(hh < g_arg, (hh * D + 32 * kk + 8 * g) * 2)));
   }
   __builtin_amdgcn_sched_barrier(0);   // the page table, token count and query loads stay in this order
+  // Every other kernel argument the kernel reads, fetched in one batch while
+  // those loads are in flight.  Left to itself the compiler requests some
+  // before the page table (so the first HBM load waits for an argument round
+  // trip) and the plan's only after the page table arrives (a second one).
+  in_sgprs(pv.bf16, pv.ledger, pv.pages, pv.err, a.k_new, a.v_new, a.mass, a.partials, a.ml, a.tile_mass,
+           a.app_mass, a.app_info);
+  in_sgprs(pv.B, pv.Hq, pv.Hkv, pv.W, pv.maxw, pv.nb, pv.nl, pv.G, a.layer, a.splits, a.plan_words, a.acc_scores);
 
   // ------------------------------------------------ tile plan (workgroup)
   // The page table goes to LDS once per workgroup: thread t takes windows
   // t, t + 256, ...; their entries are loaded before the token count is known.
   // s_ex[w] holds the live tiles before window w within its 64-window group
   // (bf16 tiles in the low 16 bits, INT2 tiles in the high 16 bits) and
-  // s_gt[r] the total of group r; one barrier, then each wave reads the plan.
+  // s_gt[r] the total of group r.  After a barrier every thread writes the
+  // tile entries of its windows into s_tiles - all live bf16 tiles in window
+  // order, then all INT2 tiles - and after a second barrier each wave reads
+  // its share of that array as its tile lists.  (Having each wave search the
+  // table for its own tiles took about a microsecond of issue per wave.)
   uint32_t* s_pe = s_dyn;                                        // [roundup(maxw, 256)]
   int* s_ex = reinterpret_cast<int*>(s_dyn + a.plan_words);      // [roundup(maxw, 256)]
-  uint32_t* s_used = s_dyn + 2 * a.plan_words;                   // bf16 slot bitmap (append)
+  uint32_t* s_tiles = s_dyn + 2 * a.plan_words;                  // [maxw * W / 32]
+  uint32_t* s_used = s_tiles + maxw * TPW;                       // bf16 slot bitmap (append)
   const int len_old = uniform(int(len_raw));
   const uint32_t* gp = pv.pages + size_t(seg) * maxw;
   const int n_old = windows_of(len_old, W);
@@ -362,28 +384,38 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     const int vt = (min(W, len_old - w * W) + 31) / 32;
     return t == TIER_F ? vt : (t == TIER_Q ? (vt << 16) : 0);
   };
+  int ex_first[4];   // the first 1024 windows' prefixes, kept for the scatter below
   {
     const int JR = a.plan_words / 256;
-    auto stage = [&](const uint32_t (&e4)[4], int j0) {
+    auto stage = [&](const uint32_t (&e4)[4], int j0, int (&ex4)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        ex4[j] = 0;
         if ((j0 == 0 && j == 0) || j0 + j < JR) {   // JR >= 1: the first group always stages
           const int w = 256 * (j0 + j) + tid;
           const int c = tiles_of(e4[j], w);
           const int incl = wave_incl_scan(c);
           s_pe[w] = e4[j];
           s_ex[w] = incl - c;
+          ex4[j] = incl - c;
           if (lane == 63) s_gt[w >> 6] = incl;
         }
       }
     };
-    stage(e_first, 0);
-    const auto pt = tile_rsrc(gp, maxw * 4);   // lanes past the table read 0
-    for (int j0 = 4; j0 < JR; j0 += 4) {
-      uint32_t e4[4];
+    stage(e_first, 0, ex_first);
+    if (JR > 4) {   // a table of more than 1024 windows
+      const auto pt = tile_rsrc(gp, maxw * 4);   // lanes past the table read 0
+      for (int j0 = 4; j0 < JR; j0 += 4) {
+        uint32_t e4[4];
+        int ex4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) e4[j] = load4(pt, (256 * (j0 + j) + tid) * 4);
-      stage(e4, j0);
+        for (int j = 0; j < 4; ++j) e4[j] = load4(pt, (256 * (j0 + j) + tid) * 4);
+        stage(e4, j0, ex4);
+      }
+      // Nothing of this path is left pending: otherwise the compiler's wait
+      // analysis keeps these loads in flight on every path and waits for all
+      // loads (the query included) before reusing their registers.
+      drain_loads();
     }
   }
   __syncthreads();
@@ -397,47 +429,59 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     tot = __builtin_amdgcn_readlane(incl, 63);
   }
   const int NF = tot & 0xFFFF, NQ = tot >> 16;
+  {
+    // thread t places the tiles of windows t, t + 256, ...: window 256j + t
+    // lies in group 4j + wid (the same for the whole wave).  The first 1024
+    // windows' entries and prefixes are still in registers from the staging.
+    const int JR = a.plan_words / 256;
+    for (int j = 0; j < JR; ++j) {
+      const int grp = 4 * j + wid;
+      if (grp >= NG) break;
+      const int gb = __builtin_amdgcn_readlane(gbase, grp);
+      const int w = 256 * j + tid;
+      if (w < n_old) {
+        uint32_t e;
+        int ex;
+        if (j < 4) {
+          e = j == 0 ? e_first[0] : (j == 1 ? e_first[1] : (j == 2 ? e_first[2] : e_first[3]));
+          ex = j == 0 ? ex_first[0] : (j == 1 ? ex_first[1] : (j == 2 ? ex_first[2] : ex_first[3]));
+        } else {
+          e = s_pe[w];
+          ex = s_ex[w];
+        }
+        const int t = pe_tier(e);
+        if (t == TIER_F || t == TIER_Q) {
+          const int sh = t == TIER_F ? 0 : 16;
+          const int ti = ((gb >> sh) & 0xFFFF) + ((ex >> sh) & 0xFFFF) + (t == TIER_F ? 0 : NF);
+          const int vt = (min(W, len_old - w * W) + 31) / 32;
+          const int sl = t == TIER_F ? pe_bslot(e) : pe_lslot(e);
+          for (int k = 0; k < vt; ++k) s_tiles[ti + k] = te_make(sl, w, k);
+        }
+      }
+    }
+  }
+  __syncthreads();
   // Every wave takes an even share of the bf16 tiles and, separately, of the
   // INT2 tiles, so HBM bytes (mostly bf16) and decode work (mostly INT2) are
   // spread alike over all waves - and so over all SIMDs and CUs.
   const int nwaves = S * kAttnWaves, widx = split * kAttnWaves + wid;
   const int f_beg = widx * NF / nwaves, f_end = (widx + 1) * NF / nwaves;
   const int q_beg = widx * NQ / nwaves, q_end = (widx + 1) * NQ / nwaves;
-  uint32_t* listf = s_listf[wid];
-  uint32_t* listq = s_listq[wid];
-  // the wave lists the tiles [lo, hi) of tier `tier` into `list`: lane l takes
-  // window 64r + l of each group r whose tiles of that tier meet the range
-  auto build_list = [&](int tier, int lo, int hi, uint32_t* list) {
-    const int sh = tier == TIER_F ? 0 : 16;
-    for (int r = 0; r < NG; ++r) {
-      const int b0 = (__builtin_amdgcn_readlane(gbase, r) >> sh) & 0xFFFF;
-      const int b1 = r + 1 < NG ? (__builtin_amdgcn_readlane(gbase, r + 1) >> sh) & 0xFFFF
-                                : ((tot >> sh) & 0xFFFF);
-      if (b1 <= lo || b0 >= hi) continue;
-      const int w = 64 * r + lane;
-      if (w >= n_old) continue;
-      const uint32_t e = s_pe[w];
-      if (pe_tier(e) != tier) continue;
-      int ti = b0 + ((s_ex[w] >> sh) & 0xFFFF);
-      const int vt = (min(W, len_old - w * W) + 31) / 32;
-      const int sl = tier == TIER_F ? pe_bslot(e) : pe_lslot(e);
-      for (int k = 0; k < vt; ++k, ++ti)
-        if (ti >= lo && ti < hi) list[ti - lo] = te_make(sl, w, k);
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
+  // the wave's current chunk of each list (at most kList tiles of a tier)
+  const uint32_t* listf = s_tiles + f_beg;
+  const uint32_t* listq = s_tiles + NF + q_beg;
 
   // ------------------------------------------------- the append decision
   // Taken by wave 0 of split 0 of each (sequence, kv head); the combine kernel
   // stores the token and rewrites the page table after every workgroup read it.
-  int app_ok = 0, app_slot = 0, app_row = 0, app_new = 0;
+  int app_ok = 0, app_slot = 0, app_row = 0, app_new = 0, app_err = 0;
   if (a.k_new != nullptr && split == 0 && wid == 0) {
     if (len_old % W != 0) {
       const uint32_t e = s_pe[n_old - 1];
       app_ok = pe_tier(e) == TIER_F;
       app_slot = pe_bslot(e);
       app_row = len_old % W;
-      if (!app_ok && kvh == 0 && lane == 0) set_err(pv.err, KV_ERR_APPEND_STATE);
+      if (!app_ok) app_err = KV_ERR_APPEND_STATE;
     } else {
       // a new window opens: the lowest bf16 slot no live bf16 window holds
       const int words = (pv.nb + 31) / 32;
@@ -463,22 +507,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       app_ok = cap && slot != 0x7FFFFFFF;
       app_slot = app_ok ? slot : 0;
       app_new = 1;
-      if (!app_ok && kvh == 0 && lane == 0) set_err(pv.err, cap ? KV_ERR_NO_BF16_SLOT : KV_ERR_CAPACITY);
-    }
-    if (kvh == 0 && lane == 0) {
-      int32_t* info = a.app_info + 8 * b;
-      info[0] = app_ok;
-      info[1] = app_slot;
-      info[2] = app_row;
-      info[3] = app_new;
-      info[4] = len_old;
+      if (!app_ok) app_err = cap ? KV_ERR_NO_BF16_SLOT : KV_ERR_CAPACITY;
     }
   }
-  if (a.k_new == nullptr && split == 0 && kvh == 0 && tid == 0) {
-    int32_t* info = a.app_info + 8 * b;
-    info[0] = 0;
-    info[4] = len_old;
-  }
+  // (the decision and any error bits are stored at the end of the kernel: a
+  // store here would count among the loads in flight - loads and stores share
+  // one counter - and make the first tile wait for all of them)
 
   WaveState<NB> st;
   st.m_run = -INFINITY;
@@ -506,37 +540,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     }
     __builtin_amdgcn_wave_barrier();
   };
-
-  // ------------------------------------------- the appended token (VALU)
-  if (app_ok) {
-    const uint16_t* kn = a.k_new + (size_t(b) * pv.Hkv + kvh) * D;
-    const uint16_t* vn = a.v_new + (size_t(b) * pv.Hkv + kvh) * D;
-    float zp = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 kv = as_bf16x8(*reinterpret_cast<const uint4*>(kn + 32 * kk + 8 * g));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) zp = fmaf(float(qb[kk][e]), float(kv[e]), zp);
-    }
-    zp = sum_rows(zp);
-    // the token counts once: only lane group 0 carries it into the softmax;
-    // its probability then reaches the other groups' output channels
-    float z[8], p[8], rs;
-    z[0] = g == 0 ? zp : -INFINITY;
-#pragma unroll
-    for (int e = 1; e < 8; ++e) z[e] = -INFINITY;
-    softmax_tile<NB, 0>(st, z, qscale, 0.f, p, &rs);
-    const float p0 = __shfl(p[0], hn, 64);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint2 u = *reinterpret_cast<const uint2*>(vn + 16 * nb + 4 * g);
-      st.o[nb][0] = fmaf(p0, __uint_as_float(u.x << 16), st.o[nb][0]);
-      st.o[nb][1] = fmaf(p0, __uint_as_float(u.x & 0xFFFF0000u), st.o[nb][1]);
-      st.o[nb][2] = fmaf(p0, __uint_as_float(u.y << 16), st.o[nb][2]);
-      st.o[nb][3] = fmaf(p0, __uint_as_float(u.y & 0xFFFF0000u), st.o[nb][3]);
-    }
-    if (rec_mass) a.app_mass[size_t(b) * pv.Hq + size_t(kvh) * G + hn] = make_float2(rs, st.m_run);
-  }
 
   // ------------------------------------------------------------ tile loops
   // Issue order: the first two INT2 tiles, then the first bf16 tile, then the
@@ -655,11 +658,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   };
   uint8_t* scb = s_scb[wid];
   auto compute_q = [&](QB& qq, int t, int rt) {   // record row rt
-    // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer
+    // the tile's scale block (Ks | Km | Vs | Vm) into this wave's LDS buffer.
+    // Lanes read each other's words: wavefront-scope fences order the previous
+    // tile's reads before this store and this store before the reads below
+    // (the compiler may not move LDS accesses across them; they emit no
+    // instruction, since the LDS completes one wave's operations in order).
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     if constexpr (SCW == 4)
       reinterpret_cast<uint4*>(scb)[lane] = make_uint4(qq.sc[0], qq.sc[1], qq.sc[2], qq.sc[3]);
     else
       reinterpret_cast<uint2*>(scb)[lane] = make_uint2(qq.sc[0], qq.sc[1]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     const f16x8* ks = reinterpret_cast<const f16x8*>(scb);              // [D]
     const f16x8* km = reinterpret_cast<const f16x8*>(scb + 2 * D);      // [D]
     const f16x8* vs = reinterpret_cast<const f16x8*>(scb + 4 * D);      // [D/32][32]
@@ -746,8 +757,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     if (rec_mass) rec[rt][hn] = make_float2(rs, st.m_run);
   };
 
-  if (f_beg < f_end) build_list(TIER_F, f_beg, min(f_end, f_beg + kList), listf);
-  if (q_beg < q_end) build_list(TIER_Q, q_beg, min(q_end, q_beg + kList), listq);
   // The wave's first bf16 tile, in flight while INT2 tiles are decoded - but
   // not beside two 8-bit tiles, whose code words leave no room for it.
   constexpr bool kEarlyF = BITS != 8;
@@ -799,7 +808,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       nt = max(0, min(q_end, cb + kList) - cb);
       i0 = 0;
       if (nt > 0) {
-        build_list(TIER_Q, cb, cb + nt, listq);
+        listq = s_tiles + NF + cb;
         load_q(A, 0, nt);
         load_q(Bq, 1, nt);
         __builtin_amdgcn_sched_barrier(0);
@@ -851,15 +860,46 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     flush_masses(nq, listq, true);
     f_done = min(jf, nf);
   };
+  // A short share - at most three INT2 tiles and one bf16 tile, as at 32K
+  // context: all of its INT2 tiles are requested right after the plan, its
+  // bf16 tile once the first INT2 tile is in.  The INT2 decode sets the
+  // critical path here: requested together, the bf16 bytes delayed the INT2
+  // data by about a microsecond, while requested after the first INT2 tile
+  // they arrive during the decode of the others.  Each tile waits only for
+  // its own loads.
+  // (4-bit code words are larger: two INT2-tier tiles there)
+  constexpr int kShortQ = BITS == 2 ? 3 : 2;
+  auto short_tiles = [&]() {
+    const int nq = q_end - q_beg, nf = f_end - f_beg;
+    QB A, Bq, C;
+    load_q(A, 0, nq);
+    load_q(Bq, 1, nq);
+    if constexpr (kShortQ > 2) load_q(C, 2, nq);
+    __builtin_amdgcn_sched_barrier(0);
+    make_q4();
+    if (nq > 0) compute_q(A, 0, 0);
+    load_f(FA, 0, nf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nq > 1) compute_q(Bq, 1, 1);
+    if constexpr (kShortQ > 2)
+      if (nq > 2) compute_q(C, 2, 2);
+    flush_masses(nq, listq);
+    if (nf > 0) compute_f(FA, 0);
+    flush_masses(nf, listf);
+  };
   // (head groups of more than four need the registers of their wider B
   // operands: they keep the tiers apart)
-  bool mixed = false;
+  bool mixed = false, short_share = false;
+  if constexpr (BITS == 2 || D == 64) {
+    short_share = q_end - q_beg <= kShortQ && f_end - f_beg <= 1;
+    if (short_share) short_tiles();
+  }
   if constexpr (GP == 4 && BITS == 2) {
     const int nq_all = q_end - q_beg, nf_all = f_end - f_beg;
-    mixed = nq_all >= kMixedList && nq_all + nf_all <= kList;
+    mixed = !short_share && nq_all >= kMixedList && nq_all + nf_all <= kList;
     if (mixed) mixed_tiles();
   }
-  if (!mixed) {
+  if (!mixed && !short_share) {
     if (f_beg < f_end && kEarlyF)
       int2_tiles(std::true_type{});
     else
@@ -867,10 +907,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   }
 
   // ---------------------------------------------------------- bf16 tiles
-  for (int cb = f_beg; cb < f_end; cb += kList) {
+  for (int cb = short_share ? f_end : f_beg; cb < f_end; cb += kList) {
     const int ce = min(f_end, cb + kList), nt = ce - cb;
     const int i0 = cb == f_beg ? f_done : 0;   // FA holds tile i0 after the mixed loop
-    if (cb != f_beg) build_list(TIER_F, cb, ce, listf);
+    listf = s_tiles + cb;
     if (cb != f_beg || !kEarlyF) load_f(FA, 0, nt);   // (else requested among the INT2 tiles)
     FB Bf;
     load_f(Bf, i0 + 1, nt);
@@ -886,6 +926,54 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     }
     drain_loads();
     flush_masses(nt, listf);
+  }
+
+  // ------------------------------------------- the appended token (VALU)
+  // Taken after the tiles (the online softmax does not depend on the order of
+  // tokens): a block ahead of the tile loops made every wave wait for its
+  // query loads before requesting any tile.  (A wave-uniform branch.)
+  if (uniform(app_ok)) {
+    const uint16_t* kn = a.k_new + (size_t(b) * pv.Hkv + kvh) * D;
+    const uint16_t* vn = a.v_new + (size_t(b) * pv.Hkv + kvh) * D;
+    // the query again from memory (the one wave that takes this block): left
+    // in qb, its conversions were hoisted ahead of the tile loads
+    const auto rq = tile_rsrc(q_arg + (size_t(b) * hq_arg + size_t(kvh) * g_arg) * D, g_arg * D * 2);
+    float zp = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 kv = as_bf16x8(*reinterpret_cast<const uint4*>(kn + 32 * kk + 8 * g));
+      const bf16x8 qa = as_bf16x8(load16(rq, boff(hh < g_arg, (hh * D + 32 * kk + 8 * g) * 2)));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zp = fmaf(float(qa[e]), float(kv[e]), zp);
+    }
+    zp = sum_rows(zp);
+    // the token counts once: only lane group 0 carries it into the softmax;
+    // its probability then reaches the other groups' output channels
+    float z[8], p[8], rs;
+    z[0] = g == 0 ? zp : -INFINITY;
+#pragma unroll
+    for (int e = 1; e < 8; ++e) z[e] = -INFINITY;
+    softmax_tile<NB, 0>(st, z, qscale, 0.f, p, &rs);
+    const float p0 = __shfl(p[0], hn, 64);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint2 u = *reinterpret_cast<const uint2*>(vn + 16 * nb + 4 * g);
+      st.o[nb][0] = fmaf(p0, __uint_as_float(u.x << 16), st.o[nb][0]);
+      st.o[nb][1] = fmaf(p0, __uint_as_float(u.x & 0xFFFF0000u), st.o[nb][1]);
+      st.o[nb][2] = fmaf(p0, __uint_as_float(u.y << 16), st.o[nb][2]);
+      st.o[nb][3] = fmaf(p0, __uint_as_float(u.y & 0xFFFF0000u), st.o[nb][3]);
+    }
+    if (rec_mass) a.app_mass[size_t(b) * pv.Hq + size_t(kvh) * G + hn] = make_float2(rs, st.m_run);
+  }
+  // the step's append decision for the combine kernel, and its error bits
+  if (split == 0 && wid == 0 && kvh == 0 && lane == 0) {
+    int32_t* info = a.app_info + 8 * b;
+    info[0] = app_ok;
+    info[1] = app_slot;
+    info[2] = app_row;
+    info[3] = app_new;
+    info[4] = len_old;
+    if (app_err) set_err(pv.err, app_err);
   }
 
   // -------------------------------------------- combine the 4 waves in LDS
@@ -973,15 +1061,6 @@ __device__ inline float oct_reduce(float x, Op op) {
 }
 
 
-// Materialise uniform values (kernel arguments) in SGPRs at this point.
-template <typename T>
-__device__ inline void in_sgpr(const T& x) {
-  asm volatile("" ::"s"(x));
-}
-template <typename... T>
-__device__ inline void in_sgprs(const T&... x) {
-  (in_sgpr(x), ...);
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, int acc_scores) {
@@ -1241,17 +1320,17 @@ static hipError_t launch_attn_kernel(const PoolView& pv, const AttnArgs& a, size
   const int32_t* tl = pv.tokens + size_t(a.layer) * pv.B;
   if (a.ev_start || a.ev_stop) {
     hipExtLaunchKernelGGL((attn_kernel<D, GP, BITS>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), uint32_t(shm), s,
-                          a.ev_start, a.ev_stop, 0u, pl, tl, pv.maxw, pv, a);
+                          a.ev_start, a.ev_stop, 0u, pl, tl, pv.maxw, a.q, pv.Hq, pv.G, pv, a);
   } else {
     hipLaunchKernelGGL((attn_kernel<D, GP, BITS>), dim3(a.splits, pv.Hkv, pv.B), dim3(256), shm, s, pl, tl, pv.maxw,
-                       pv, a);
+                       a.q, pv.Hq, pv.G, pv, a);
   }
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream_t s) {
-  const size_t shm = (2 * size_t(a.plan_words) + (pv.nb + 31) / 32) * 4;
+  const size_t shm = (2 * size_t(a.plan_words) + size_t(pv.maxw) * (pv.W / 32) + (pv.nb + 31) / 32) * 4;
   hipError_t e;
   if (pv.lbits == 2)
     e = pv.G <= 4 ? launch_attn_kernel<D, 4, 2>(pv, a, shm, s) : launch_attn_kernel<D, 8, 2>(pv, a, shm, s);
