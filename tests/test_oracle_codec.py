@@ -302,3 +302,22 @@ def test_int8_requantize_can_drift():
         e2 = codec.quantize_window(*codec.promote_bits(e), 8)
         moved += int((e["Kc"] != e2["Kc"]).sum() + (e["Vc"] != e2["Vc"]).sum())
     assert moved > 0
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_edge_case_groups_have_their_defined_codes(bits):
+    """Ties exactly on the half-way points (round half to even), their bf16
+    neighbours, s == 0, fp16 overflow of the min (m = +-inf) and of the scale:
+    codes fixed by the definition alone (tests/codec_cases.py), the same groups
+    the GPU demote test feeds the kernel."""
+    from tests.codec_cases import edge_groups
+    pinned = 0
+    with np.errstate(over="ignore"):
+        for name, g, want in edge_groups(bits, np.random.default_rng(bits)):
+            got, _, _ = codec.quantize_groups(codec.bf16_to_f32(g)[None], bits)
+            if want is not None:
+                assert np.array_equal(got[0], want), name
+                pinned += 1
+            else:
+                assert got.max() <= (1 << bits) - 1, name
+    assert pinned >= 10

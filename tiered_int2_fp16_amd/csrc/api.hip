@@ -20,6 +20,7 @@ struct kv_pool {
   size_t arena_bytes = 0;
   int splits = 1;
   int device = 0;
+  int cus = 1;
   std::vector<hipEvent_t> ev_start, ev_stop;  // attention dispatch timing
   int ev_used = 0;
   ~kv_pool() {
@@ -67,6 +68,7 @@ PoolView view(const kv_pool* p) {
   v.work_counts = int(g.work_counts);
   v.attn_counters = int(g.attn_counters);
   v.seg_counters = int(g.seg_counters);
+  v.cus = p->cus;
   return v;
 }
 
@@ -175,6 +177,7 @@ kv_status kv_pool_create(const kv_pool_config* cfg, void* arena, size_t arena_by
   p->arena = base;
   p->arena_bytes = arena_bytes;
   p->splits = attn_splits(g, cus);
+  p->cus = cus > 0 ? cus : 1;
   p->device = dev;
   *out = p;
   return KV_OK;

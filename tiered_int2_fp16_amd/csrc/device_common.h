@@ -33,6 +33,7 @@ struct PoolView {
   int B, L, Hq, Hkv, D, W, maxw, R, nb, nl, G;
   int lbits;          // ledger code width: 2, 4 or 8
   int work_items, work_counts, attn_counters, seg_counters;  // int32 offsets into work
+  int cus;            // compute units of the pool's device (launch sizing)
 
   __device__ uint16_t* block(int seg, int slot, int kvh) const {
     return bf16 + ((size_t(seg) * nb + slot) * Hkv + kvh) * size_t(2 * W * D);

@@ -76,53 +76,9 @@ hipError_t launch_prefill(const PoolView& pv, int layer, const uint16_t* k, cons
 // Signed zeros are made +0, s = fp16((max - min) / L), m = fp16(min); codes
 // use the stored fp16 values: c = clamp(rint_even((x - m) / s), 0, L), or 0
 // when s == 0.  float32 IEEE arithmetic throughout (correctly rounded divide,
-// no contraction).
-template <int BITS>
-__device__ inline void quant_group(const float* xp, int xstride, uint8_t* cp, int cstride, uint16_t* s_out,
-                                   uint16_t* m_out) {
-  constexpr float kTop = float((1 << BITS) - 1);
-  float x[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float v = xp[i * xstride];
-    x[i] = (v == 0.f) ? 0.f : v;
-  }
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 32; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
-  }
-  const float d = mx - mn;
-  const float s32 = __fdiv_rn(d, kTop);
-  const _Float16 hs = (_Float16)s32;
-  const _Float16 hm = (_Float16)mn;
-  const float s = (float)hs, m = (float)hm;
-  // rint(fl(u / s)) from u * rcp(s).  Only the ties k + 1/2 (k < L) decide
-  // a code (the clamp absorbs the rest), and the two quotients differ by
-  // under 2e-7 relative (rcp within one ulp, one rounding of the product),
-  // so the codes agree unless a quotient r lies within 1e-5 * (1 + r) of
-  // some k + 1/2: such values are redone with the exact division in a
-  // separate, rolled loop (it runs rarely; kept out of line, its code is not
-  // fetched with the common path).
-  const float rcp = s == 0.f ? 0.f : __builtin_amdgcn_rcpf(s);
-  uint32_t near = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float r = (x[i] - m) * rcp;
-    near |= uint32_t(s != 0.f && fabsf(r - floorf(r) - 0.5f) < 1e-5f * (1.f + fabsf(r))) << i;
-    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(r), 0.f), kTop));
-  }
-  while (near) {
-    const int i = __builtin_ctz(near);
-    near &= near - 1;
-    const float v = xp[i * xstride];
-    const float u = ((v == 0.f) ? 0.f : v) - m;
-    cp[i * cstride] = uint8_t(fminf(fmaxf(rintf(__fdiv_rn(u, s)), 0.f), kTop));
-  }
-  *s_out = __builtin_bit_cast(uint16_t, hs);
-  *m_out = __builtin_bit_cast(uint16_t, hm);
-}
+// no contraction).  The sign of a zero x never changes x - m (m is never -0).
+// The demote kernel decides each code by exact comparisons of x - m with
+// half-way points (k + 1/2) s instead of dividing.
 
 // ------------------------------------------------------------------ demote
 struct WorkItem {
@@ -246,83 +202,287 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 // entry.  K groups are the tile's channels (32 tokens each), V groups each
 // token's 32-channel blocks.
 // (D, the head dimension, and BITS, the code width, are template parameters:
-// the chunk and field index arithmetic below then reduces to shifts and masks)
+// the chunk and field index arithmetic below then reduces to shifts, masks and
+// constants)
+//
+// Per unit (one 32-token tile of one kv head), three phases, two barriers
+// (alternate units use alternate LDS buffers):
+//  0. every thread writes its 16-byte chunks of the tile (loaded into
+//     registers while the previous unit was processed) to LDS with one store
+//     each: K as [token][channel], V as [channel][token];
+//  1. each group's min and max from two threads (16-bit pairs of LDS rows,
+//     one exchange across the wave's halves), its fp16 scale and min, and
+//     the parameters of its codes published in LDS;
+//  2. one thread per pair of packed code words whose values share their
+//     groups reads the words' values (16-byte LDS loads) and the groups'
+//     parameters, decides the codes and assembles the words in registers.
+// Each code word has one writer: no atomics.  A unit's results (scales, mins,
+// code words) stay in registers until the next unit has been written to LDS;
+// they are then stored, just before the loads of the unit after it are
+// issued, so those loads never wait behind freshly issued stores.
 template <int D, int BITS>
-__global__ __launch_bounds__(256) void quantize_kernel(PoolView pv, int layer) {
-  __shared__ float xs[2][32][129];          // K, V of one tile, canonical [token][dim]
-  __shared__ uint8_t cs[2][32][132];        // their codes (rows padded: no bank conflicts)
+__global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer,
+                                                         const WorkItem* __restrict__ items) {
+  constexpr int KP = D + 8;    // K rows [token][channel] (bf16), padded
+  constexpr int VP = 40;       // V rows [channel][token] (bf16), padded; 8 more per 32 rows
+  constexpr int CWB = BITS * D / 64;          // code words per lane per part
+  constexpr int NW = 64 * CWB;                // code words per part
+  constexpr int PPT = NW >= 256 ? NW / 256 : 1;   // code-word pairs per thread (NW pairs in all)
+  constexpr int NCH = 8 * D / 256;            // 16-byte chunks per thread (K and V)
+  constexpr int NCW = BITS == 2 ? 2 : 1;      // chunks per code word
+  constexpr float kTop = float((1 << BITS) - 1);
+  // two buffers, used by alternate units: a unit's first phase may then begin
+  // while slower threads still read the previous unit's data (two barriers
+  // per unit)
+  __shared__ __attribute__((aligned(16))) uint16_t sk2[2][32 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sv2[2][D * VP + (D / 32) * 8];
+  // group parameters (phase 1 to phase 2): K group of channel d at d, V group
+  // (token t, block j) at D + 32 j + t
+  __shared__ float4 pp2[2][2 * D];
+  auto vrow = [](int d) { return d * VP + (d >> 5) * 8; };   // (a wave's two 32-row blocks hit other banks)
   const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
+  const bool has_group = 2 * D >= 256 || tid < 2 * D;   // phase 1 threads (whole waves)
   const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D, BITS);
-  const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
-  // the first unit's work item is read together with the count (the item
-  // list always has room for it; it is used only if the count covers it)
-  const WorkItem first = work[blockIdx.x / (pv.Hkv * TPW)];
+  const WorkItem* work = items + size_t(b) * pv.maxw;   // (not written here: scalar loads)
   const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int i = u / (pv.Hkv * TPW), r = u % (pv.Hkv * TPW), kvh = r / TPW, tile = r % TPW;
-    const WorkItem it = u == int(blockIdx.x) ? first : work[i];
-    if (it.flag != 1) continue;
-    const uint16_t* tb = pv.block(seg, it.src, kvh) + size_t(tile) * 64 * D;
+  const int per_item = pv.Hkv * TPW;
+  // the unit's item (flag 1: move bytes; flag 0 past the list)
+  auto item_of = [&](int u) { return u < units ? work[u / per_item] : WorkItem{0, 0, 0, 0}; };
+  // the unit's tile chunks; a unit that moves nothing loads nothing (empty
+  // resource)
+  auto fetch = [&](int u, const WorkItem& it, uint4 (&qv)[NCH]) {
+    const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
+    const uint16_t* tb = pv.block(seg, it.flag == 1 ? it.src : 0, kvh) + size_t(tile) * 64 * D;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(tb), (short)0,
+                                                      it.flag == 1 ? 128 * D : 0, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+      qv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + 256 * j) * 16, 0, 0));
+  };
+  // pair i of this thread: its index x among the NW pairs (K pairs first)
+  // and its two code words (lane, w).  K: (lane, w) and (lane, w + CWB/2),
+  // the same channels in the two 16-token halves of the tile.  V, the same
+  // tokens and 32-channel block: INT2 (lane, w) and (lane + 8, w) (lane bit
+  // 3 clear), 4 bits (lane, w) and (lane, w + 1) (w even), 8 bits (lane, w)
+  // and (lane, w + 2) (w bit 1 clear).
+  auto pair_of = [&](int i, int (&lane)[2], int (&w)[2]) {
+    const int x = tid + 256 * i;
+    const int y = x >= NW / 2 ? x - NW / 2 : x;
+    lane[0] = lane[1] = y & 63;
+    if (x < NW / 2) {
+      w[0] = y >> 6;
+      w[1] = w[0] + CWB / 2;
+    } else if (BITS == 2) {
+      lane[0] = (y & 7) | ((y & 24) << 1);
+      lane[1] = lane[0] + 8;
+      w[0] = w[1] = y >> 5;
+    } else if (BITS == 4) {
+      w[0] = 2 * (y >> 6);
+      w[1] = w[0] + 1;
+    } else {
+      const int j = y >> 6;
+      w[0] = (j & 1) | ((j >> 1) << 2);
+      w[1] = w[0] + 2;
+    }
+    return x;
+  };
+  // the previous unit's results: entry tile (null: none), this thread's
+  // group (g, K or V) with its fp16 scale and min, and its code words
+  uint8_t* pend_et = nullptr;
+  int pend_g = 0;
+  bool pend_v = false;
+  uint16_t pend_s = 0, pend_m = 0;
+  uint32_t pend_w[2 * PPT];
+  auto flush = [&]() {
+    if (!pend_et) return;   // (the same for the whole workgroup)
+    if (has_group) {
+      reinterpret_cast<uint16_t*>(pend_et + (pend_v ? LT.vs : LT.ks))[pend_g] = pend_s;
+      reinterpret_cast<uint16_t*>(pend_et + (pend_v ? LT.vm : LT.km))[pend_g] = pend_m;
+    }
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      int lane[2], w[2];
+      const int x = pair_of(i, lane, w);
+      if (NW < 256 && x >= NW) break;
+      uint32_t* cw = reinterpret_cast<uint32_t*>(pend_et + (x >= NW / 2 ? LT.vc : LT.kc));
+      cw[lane[0] * CWB + w[0]] = pend_w[2 * i];
+      cw[lane[1] * CWB + w[1]] = pend_w[2 * i + 1];
+    }
+    pend_et = nullptr;
+  };
+
+  int u = blockIdx.x;
+  WorkItem it = item_of(u);
+  uint4 qv[NCH];
+  fetch(u, it, qv);
+  int par = 0;
+  for (; u < units; u += gridDim.x) {
+    const WorkItem itn = item_of(u + gridDim.x);
+    const bool move = it.flag == 1;   // (the same for the whole workgroup)
+    uint16_t* sk = sk2[par];
+    uint16_t* sv = sv2[par];
+    float4* pp = pp2[par];
+    const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
     uint8_t* et = pv.entry(seg, it.dst, kvh) + size_t(tile) * LT.bytes;
-    // the tile's 16-byte chunks, all requested first, into the canonical layout
-    constexpr int kMaxChunks = 4;   // 8 * D / 256 for D <= 128
-    uint4 qv[kMaxChunks];
+    // 0. chunks to LDS: chunk c < 4 D is K chunk (cmb, lane) = (c / 64, c % 64),
+    //    8 channels of one token; the rest V chunks, 8 tokens of one channel
+    if (move) {
 #pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
-      const int c = tid + j * 256;
-      if (c < 8 * D) qv[j] = reinterpret_cast<const uint4*>(tb)[c];
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
-      const int c = tid + j * 256;
-      if (c >= 8 * D) break;
-      const int part = c / (4 * D), cc = c % (4 * D), cmb = cc >> 6, lane = cc & 63;
-      const uint4 q = qv[j];
-      const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + 256 * j;
         int t, d;
-        if (part) layout::v_chunk_elem(cmb, lane, e, &t, &d);
-        else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
-        xs[part][t][d] = __uint_as_float((e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16));
+        if (256 * j < 4 * D) {
+          layout::k_chunk_elem(c >> 6, c & 63, 0, D, &t, &d);
+          *reinterpret_cast<uint4*>(&sk[t * KP + d]) = qv[j];
+        } else {
+          layout::v_chunk_elem((c - 4 * D) >> 6, c & 63, 0, &t, &d);
+          *reinterpret_cast<uint4*>(&sv[vrow(d) + t]) = qv[j];
+        }
       }
     }
+    flush();
+    fetch(u + gridDim.x, itn, qv);   // the next unit's bytes, in flight during the rest of this one
+    it = itn;
+    if (!move) continue;
+    par ^= 1;
     __syncthreads();
-    uint16_t* ks = reinterpret_cast<uint16_t*>(et + LT.ks);
-    uint16_t* km = reinterpret_cast<uint16_t*>(et + LT.km);
-    uint16_t* vs = reinterpret_cast<uint16_t*>(et + LT.vs);
-    uint16_t* vm = reinterpret_cast<uint16_t*>(et + LT.vm);
-    for (int g = tid; g < D + D; g += blockDim.x) {
-      if (g < D)   // K group: channel g over the tile's 32 tokens
-        quant_group<BITS>(&xs[0][0][g], 129, &cs[0][0][g], 132, ks + g, km + g);
-      else {       // V group: token t, channels 32j..32j+31
-        const int t = (g - D) / (D / 32), j = (g - D) % (D / 32);
-        quant_group<BITS>(&xs[1][t][32 * j], 1, &cs[1][t][32 * j], 1, vs + j * 32 + t, vm + j * 32 + t);
-      }
-    }
-    __syncthreads();
-    // pack: one 32-bit code word per thread step (64 lanes x BITS*D/64 words
-    // per part, 32/BITS fields per word)
-    constexpr int CWB = BITS * D / 64;
-    constexpr int words = 64 * CWB;
-    for (int x = tid; x < 2 * words; x += blockDim.x) {
-      const bool is_v = x >= words;
-      const int q = is_v ? x - words : x;
-      const int lane = q / CWB, w = q % CWB;
-      uint32_t word = 0;
+    // 1. group parameters.  The first D threads take the K groups, the next D
+    //    the V groups (whole waves each).  A thread reads 16 bf16 pairs: half
+    //    of each of two groups (K: channels 2p, 2p + 1 over 16 tokens; V:
+    //    tokens 2p', 2p' + 1 of a 32-channel block over 16 channels).  Lanes l
+    //    and l ^ 32 hold the two halves; after one exchange lane l finishes
+    //    the pair's first group and lane l ^ 32 its second.
+    if (has_group) {
+      const bool is_v = tid >= D;
+      const int idx = is_v ? tid - D : tid, l = idx & 63, h = l >> 5;
+      const int p = (idx >> 6) * 32 + (l & 31);   // the pair, 0 .. D/2 - 1
+      uint32_t x[16];
+      int g;   // the group this thread finishes: K channel, or 32 j + token for V
+      if (!is_v) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(sk + 16 * h * KP + 2 * p);
 #pragma unroll
-      for (int f = 0; f < 32 / BITS; ++f) {
-        int cmb, e, t, d;
-        layout::field_elem_b(BITS, w, f, &cmb, &e);
-        if (is_v) layout::v_chunk_elem(cmb, lane, e, &t, &d);
-        else layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
-        word |= uint32_t(cs[is_v][t][d]) << (BITS * f);
+        for (int i = 0; i < 16; ++i) x[i] = src[i * (KP / 2)];
+        g = 2 * p + h;
+      } else {
+        const int tp = p & 15, j = p >> 4;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(sv + vrow(32 * j + 16 * h) + 2 * tp);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = src[i * (VP / 2)];
+        g = 32 * j + 2 * tp + h;
       }
-      reinterpret_cast<uint32_t*>(et + (is_v ? LT.vc : LT.kc))[lane * CWB + w] = word;
+      float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = __uint_as_float(x[i] << 16), c = __uint_as_float(x[i] & 0xFFFF0000u);
+        mn0 = fminf(mn0, a);
+        mx0 = fmaxf(mx0, a);
+        mn1 = fminf(mn1, c);
+        mx1 = fmaxf(mx1, c);
+      }
+      // lane h = 0 keeps the first group and receives its partner's half of
+      // it; lane h = 1 the second
+      const float smn = __shfl_xor(h ? mn0 : mn1, 32, 64), smx = __shfl_xor(h ? mx0 : mx1, 32, 64);
+      float mn = fminf(h ? mn1 : mn0, smn), mx = fmaxf(h ? mx1 : mx0, smx);
+      mn = mn == 0.f ? 0.f : mn;   // -0 -> +0 (the extremes of the canonical values)
+      mx = mx == 0.f ? 0.f : mx;
+      const float s32 = __fdiv_rn(mx - mn, kTop);
+      const _Float16 hs = (_Float16)s32;
+      const _Float16 hm = (_Float16)mn;
+      const float sc = (float)hs;
+      // the parameters phase 2 reads (see there); s == 0 (all codes 0) is
+      // published as m = 0 and infinite thresholds
+      const bool zero = sc == 0.f;
+      const float m = zero ? 0.f : (float)hm;
+      float4 prm;
+      if (BITS == 2)
+        prm = zero ? make_float4(0.f, INFINITY, INFINITY, INFINITY)
+                   : make_float4(m, 0.5f * sc, 1.5f * sc, 2.5f * sc);
+      else
+        prm = zero ? make_float4(0.f, 0.f, INFINITY, INFINITY)
+                   : make_float4(m, __builtin_amdgcn_rcpf(sc), sc, 0.5f * sc);
+      pp[is_v ? D + g : g] = prm;
+      pend_g = g;   // K: [channel]; V: [j][token]
+      pend_v = is_v;
+      pend_s = __builtin_bit_cast(uint16_t, hs);
+      pend_m = __builtin_bit_cast(uint16_t, hm);
     }
     __syncthreads();
+    // 2. code words, in pairs whose values share their groups (PPT pairs a
+    //    thread); a wave's pairs are all K or all V.  Each chunk position of
+    //    the pair reads its 8 groups' parameters once for both words.
+    //    The code of x in a group (m, s) is decided exactly, without a
+    //    division: with u = x - m (the oracle's float32 difference) and the
+    //    half-way points t_k = (k + 1/2) s, which are exact in float32 (s is
+    //    an fp16 value, k + 1/2 has at most 9 significant bits), u/s lies
+    //    above, at or below k + 1/2 exactly when u lies above, at or below
+    //    t_k, and its float32 rounding never crosses k + 1/2 (k + 1/2 = 1/2,
+    //    where it may land on it from below, rounds to code 0 either way).
+    //    Hence for INT2 c = [u > t_0] + [u >= t_1] + [u > t_2] (a tie at an
+    //    odd k goes up, at an even k down: round half to even).  For 4 and 8
+    //    bits the approximate code c' = rint(clamp(u rcp(s), 0, L)) is within
+    //    one of the true one; the half-way points on either side of c' then
+    //    decide it, a tie going to the even side, and the result is clamped.
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      int lane[2], w[2];
+      const int x = pair_of(i, lane, w);
+      if (NW < 256 && x >= NW) break;   // (head_dim 64, INT2: waves 2 and 3 have no pair)
+      const bool is_v = x >= NW / 2;
+      uint32_t word[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < NCW; ++j) {
+        uint4 vals[2];
+        int pb = 0;   // the parameter index of element 0 (elements e at pb + e)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int cmb = BITS == 2 ? 2 * w[k] + j : (BITS == 4 ? w[k] : w[k] >> 1);
+          int t0, d0;
+          if (!is_v) {
+            layout::k_chunk_elem(cmb, lane[k], 0, D, &t0, &d0);   // 8 channels d0.. of token t0
+            vals[k] = *reinterpret_cast<const uint4*>(&sk[t0 * KP + d0]);
+            pb = d0;
+          } else {
+            layout::v_chunk_elem(cmb, lane[k], 0, &t0, &d0);      // 8 tokens t0.. of channel d0
+            vals[k] = *reinterpret_cast<const uint4*>(&sv[vrow(d0) + t0]);
+            pb = D + 32 * (d0 >> 5) + t0;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (BITS == 8 && (e >> 2) != (w[0] & 1)) continue;   // the other half of the chunk
+          const float4 P = pp[pb + e];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t hw = (&vals[k].x)[e >> 1];
+            const float u = __uint_as_float((e & 1) ? (hw & 0xFFFF0000u) : (hw << 16)) - P.x;
+            uint32_t code;
+            if (BITS == 2) {
+              code = uint32_t(u > P.y) + uint32_t(u >= P.z) + uint32_t(u > P.w);
+            } else {
+              const float c = rintf(__builtin_amdgcn_fmed3f(u * P.y, 0.f, kTop));
+              const int ci = int(c), odd = ci & 1;
+              const float tlo = fmaf(c, P.z, -P.w);   // (c - 1/2) s
+              const float thi = tlo + P.z;            // (c + 1/2) s
+              // a tie moves an odd c to its even neighbour: compare with the
+              // next float above tlo and below thi (both positive for odd c)
+              const int cc = ci - int(u < __int_as_float(__float_as_int(tlo) + odd)) +
+                             int(u > __int_as_float(__float_as_int(thi) - odd));
+              code = uint32_t(cc < 0 ? 0 : (cc > int(kTop) ? int(kTop) : cc));
+            }
+            int wb, bit;
+            const int cmb = BITS == 2 ? 2 * w[k] + j : (BITS == 4 ? w[k] : w[k] >> 1);
+            layout::code_pos(cmb, lane[k], e, D, BITS, &wb, &bit);
+            word[k] |= code << bit;
+          }
+        }
+      }
+      pend_w[2 * i] = word[0];
+      pend_w[2 * i + 1] = word[1];
+    }
+    pend_et = et;
   }
+  flush();
 }
 
 // Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of one tile.
@@ -418,20 +578,26 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (cap <= 0) return hipSuccess;
-  // about 1024 workgroups in all, never more than the largest unit count
+  // three workgroups per compute unit in all (the quantise kernel's
+  // occupancy: one round, no tail of late workgroups), never more than the
+  // largest unit count
   const long max_units = long(cap) * pv.Hkv * (pv.W / 32);
-  long gx = (1024 + pv.B - 1) / pv.B;
+  long gx = (3L * pv.cus + pv.B - 1) / pv.B;
   if (gx > max_units) gx = max_units;
   if (gx < 1) gx = 1;
   const int wi = pv.lbits == 2 ? 0 : (pv.lbits == 4 ? 1 : 2);
   const int di = pv.D == 64 ? 0 : 1;
   typedef void (*Kern)(PoolView, int);
+  typedef void (*QKern)(PoolView, int, const WorkItem*);
   static const Kern kDequant[2][3] = {{dequant_kernel<64, 2>, dequant_kernel<64, 4>, dequant_kernel<64, 8>},
                                       {dequant_kernel<128, 2>, dequant_kernel<128, 4>, dequant_kernel<128, 8>}};
-  static const Kern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
-                                    {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
-  hipLaunchKernelGGL(promote ? kDequant[di][wi] : kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv,
-                     layer);
+  static const QKern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
+                                     {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
+  if (promote)
+    hipLaunchKernelGGL(kDequant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer);
+  else
+    hipLaunchKernelGGL(kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer,
+                       reinterpret_cast<const WorkItem*>(pv.work + pv.work_items));
   return hipGetLastError();
 }
 
