@@ -1,4 +1,5 @@
-"""Demote codes at the codec's edge cases, bit for bit against the oracle.
+"""Demote codes and promoted bf16 at the codec's edge cases, bit for bit
+against the oracle.
 
 The demote kernel decides each code without dividing: it compares x - m with
 the half-way points (k + 1/2) s.  The windows here are built from groups that
@@ -72,8 +73,24 @@ def test_demote_codes_at_edge_cases(bits, D, W):
     pool.prefill(0, K, V, T, dev(np.ones((1, n), np.float32)))
     pool.demote(0, dev(np.arange(n, dtype=np.int32)[None]), dev(np.array([n], np.int32)))
     assert pool.check() == 0
+    entries = []
     for w in range(n):
         got = pool.read_ledger(0, 0, w).cpu().numpy()[0]
-        want = codec.entry_bytes(codec.quantize_window(Kw[w], Vw[w], bits), bits)
-        assert got.tobytes() == want, (bits, D, W, w)
-    log(f"{bits}-bit, head_dim {D}, window {W}: {n} windows of edge-case groups bit-exact")
+        e = codec.quantize_window(Kw[w], Vw[w], bits)
+        entries.append(e)
+        assert got.tobytes() == codec.entry_bytes(e, bits), (bits, D, W, w)
+    # promote every window back: bf16_rne(c s + m), bit for bit; where the
+    # group's scale overflowed fp16 (s = inf) a code 0 gives 0 * inf, NaN on
+    # both sides, whose sign and payload the definition leaves open
+    pool.promote(0, dev(np.arange(n, dtype=np.int32)[None]), dev(np.array([n], np.int32)))
+    assert pool.check() == 0
+    for w in range(n):
+        got = pool.read_window(0, 0, w).cpu().numpy().view(np.uint16)[0]
+        with np.errstate(invalid="ignore", over="ignore"):
+            wk, wv = codec.promote_bits(entries[w])
+        for part, want in ((got[0], wk), (got[1], wv)):
+            nan = (want & 0x7F80 == 0x7F80) & (want & 0x7F != 0)
+            assert np.array_equal(part[~nan], want[~nan]), (bits, D, W, w)
+            assert np.all((part[nan] & 0x7F80 == 0x7F80) & (part[nan] & 0x7F != 0)), (bits, D, W, w)
+    log(f"{bits}-bit, head_dim {D}, window {W}: {n} windows of edge-case groups bit-exact, "
+        "demoted and promoted")

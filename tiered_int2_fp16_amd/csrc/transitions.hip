@@ -487,85 +487,153 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer
 
 // Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of one tile.
 // A ledger chunk (lane, cmb) and the bf16 chunk (cmb, lane) hold the same 8
-// values, so each thread step turns one chunk's codes (one or two code words)
-// into one 16-byte chunk; the tile's scale block is staged in LDS first.
+// values, so each thread turns one chunk's codes (one or two code words) into
+// one 16-byte chunk per step; the tile's scale block (Ks | Km | Vs | Vm, 8 D
+// bytes) is staged in LDS.  The next unit's code words and scale block are
+// loaded into registers while the current unit is decoded (alternate units
+// use alternate LDS blocks, one barrier per unit); a unit's chunks are stored
+// at the start of the next unit, just before the following loads.  The float32 results are
+// never subnormal (c s + m is 0 or at least 2^-24 in magnitude: every term is
+// a multiple of the fp16 quantum 2^-24), and the hardware's packed bf16
+// conversion rounds them to nearest even.
 template <int D, int BITS>
-__global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer) {
-  __shared__ uint4 s_sc[64];   // Ks | Km | Vs | Vm of one tile (8 D bytes, D <= 128)
+__global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, const WorkItem* __restrict__ items) {
+  constexpr int NCH = 8 * D / 256;   // 16-byte chunks per thread (K chunks first, then V)
+  constexpr int NWC = BITS == 8 ? 2 : 1;   // code words per chunk
+  __shared__ uint4 s_sc[2][D / 2];
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
   const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D, BITS);
   constexpr uint32_t kMask = (1u << BITS) - 1u;
-  const WorkItem* work = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(b) * pv.maxw;
-  // the first unit's work item is read together with the count (used only if
-  // the count covers it)
-  const WorkItem first = work[blockIdx.x / (pv.Hkv * TPW)];
+  const WorkItem* work = items + size_t(b) * pv.maxw;   // (not written here: scalar loads)
   const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
-  const _Float16* ks = reinterpret_cast<const _Float16*>(s_sc);
-  const _Float16* km = ks + D;
-  const _Float16* vs = ks + 2 * D;
-  const _Float16* vm = ks + 3 * D;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
-    const int i = u / (pv.Hkv * TPW), r = u % (pv.Hkv * TPW), kvh = r / TPW, tile = r % TPW;
-    const WorkItem it = u == int(blockIdx.x) ? first : work[i];
-    if (it.flag != 1) continue;
-    const uint8_t* et = pv.entry(seg, it.src, kvh) + size_t(tile) * LT.bytes;
-    uint16_t* tb = pv.block(seg, it.dst, kvh) + size_t(tile) * 64 * D;
-    // every load of the tile before the barrier: the scale block and the
-    // code word of each of this thread's chunks
-    if (tid < D / 2) s_sc[tid] = reinterpret_cast<const uint4*>(et + LT.ks)[tid];
-    constexpr int kMaxChunks = 4;   // 8 * D / 256 for D <= 128
-    uint32_t words[kMaxChunks], words_hi[kMaxChunks];   // a chunk's code words (8 bits: two)
+  const int per_item = pv.Hkv * TPW;
+  auto item_of = [&](int u) { return u < units ? work[u / per_item] : WorkItem{0, 0, 0, 0}; };
+  // the unit's code words (NWC per chunk) and, for tid < D/2, 16-byte piece
+  // tid of its scale block; a unit that moves nothing loads nothing
+  auto fetch = [&](int u, const WorkItem& it, uint32_t (&cw)[NCH][NWC], uint4& scp) {
+    const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
+    const uint8_t* et = pv.entry(seg, it.flag == 1 ? it.src : 0, kvh) + size_t(tile) * LT.bytes;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(et), (short)0,
+                                                      it.flag == 1 ? int(LT.bytes) : 0, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
-      const int c = tid + j * 256;
-      if (c < 8 * D) {
-        const bool is_v = c >= 4 * D;
-        const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
-        int wb, bit;
-        layout::code_pos(cmb, lane, 0, D, BITS, &wb, &bit);
-        const uint32_t* cw = reinterpret_cast<const uint32_t*>(et + (is_v ? LT.vc : LT.kc) + wb);
-        words[j] = cw[0];
-        words_hi[j] = BITS == 8 ? cw[1] : 0u;
-      }
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + 256 * j;
+      const bool is_v = 256 * j >= 4 * D;
+      const int cc = is_v ? c - 4 * D : c;
+      int wb, bit;
+      layout::code_pos(cc >> 6, cc & 63, 0, D, BITS, &wb, &bit);
+#pragma unroll
+      for (int q = 0; q < NWC; ++q)
+        cw[j][q] = __builtin_amdgcn_raw_buffer_load_b32(rs, int((is_v ? LT.vc : LT.kc) + wb + 4 * q), 0, 0);
     }
-    __syncthreads();
+    // (threads from D/2 on load piece 0 again and do not use it)
+    scp = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rs, int(LT.ks + 16 * (tid < D / 2 ? tid : 0)), 0, 0));
+  };
+  // a unit's bf16 chunks are stored at the start of the next unit, just
+  // before that unit's successor is loaded (so loads never wait behind fresh
+  // stores); alternate units decode into alternate register sets, so a set's
+  // stores have a whole unit to read their data before it is overwritten.
+  // pend: the tile of a set's chunks (null: none)
+  uint16_t* pend[2] = {nullptr, nullptr};
+  uint4 pout[2][NCH];
+  auto flush = [&](int k) {
+    if (!pend[k]) return;   // (the same for the whole workgroup)
 #pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
-      const int c = tid + j * 256;
-      if (c >= 8 * D) break;
-      const bool is_v = c >= 4 * D;
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + 256 * j;
+      const bool is_v = 256 * j >= 4 * D;
+      reinterpret_cast<uint4*>(pend[k] + (is_v ? 32 * D : 0))[is_v ? c - 4 * D : c] = pout[k][j];
+    }
+    pend[k] = nullptr;
+  };
+  int u = blockIdx.x;
+  WorkItem it = item_of(u);
+  uint32_t cw[NCH][NWC];
+  uint4 nsc;
+  fetch(u, it, cw, nsc);
+  int par = 0;
+  // one unit, decoded into register set k
+  auto step = [&](int k) {
+    const WorkItem itn = item_of(u + gridDim.x);
+    const bool move = it.flag == 1;   // (the same for the whole workgroup)
+    if (move && tid < D / 2) s_sc[par][tid] = nsc;
+    const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
+    uint16_t* tb = pv.block(seg, it.dst, kvh) + size_t(tile) * 64 * D;
+    // this unit's loads are waited for here, before the stores below: the
+    // memory counter is in order, and a wait placed after them would also
+    // wait for the stores
+    uint32_t ccw[NCH][NWC];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int q = 0; q < NWC; ++q) {
+        ccw[j][q] = cw[j][q];
+        asm volatile("" ::"v"(ccw[j][q]));
+      }
+    asm volatile("" ::"v"(nsc.x), "v"(nsc.y), "v"(nsc.z), "v"(nsc.w));
+    flush(k ^ 1);
+    fetch(u + gridDim.x, itn, cw, nsc);   // the next unit's bytes, in flight during this one
+    it = itn;
+    if (!move) return;
+    __syncthreads();
+    const _Float16* ks = reinterpret_cast<const _Float16*>(s_sc[par]);
+    const _Float16* km = ks + D;
+    const _Float16* vs = ks + 2 * D;
+    const _Float16* vm = ks + 3 * D;
+    par ^= 1;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + 256 * j;
+      const bool is_v = 256 * j >= 4 * D;
       const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
+      // the chunk's 8 scales and mins: K channels d0 .. d0 + 7, or V tokens
+      // t0 .. t0 + 7 of channel block d0 / 32
+      int t0, d0;
+      if (is_v) layout::v_chunk_elem(cmb, lane, 0, &t0, &d0);
+      else layout::k_chunk_elem(cmb, lane, 0, D, &t0, &d0);
+      const int pb = is_v ? (d0 >> 5) * 32 + t0 : d0;
+      const uint4 s8 = *reinterpret_cast<const uint4*>(is_v ? vs + pb : ks + pb);
+      const uint4 m8 = *reinterpret_cast<const uint4*>(is_v ? vm + pb : km + pb);
+      const uint32_t sw[4] = {s8.x, s8.y, s8.z, s8.w}, mw[4] = {m8.x, m8.y, m8.z, m8.w};
       uint32_t out[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        uint32_t pair = 0;
+        f32x2 f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e = 2 * e2 + h;
           int wb, bit;
           layout::code_pos(cmb, lane, e, D, BITS, &wb, &bit);
-          const uint32_t word = (BITS == 8 && e >= 4) ? words_hi[j] : words[j];
+          const uint32_t word = (BITS == 8 && e >= 4) ? ccw[j][NWC - 1] : ccw[j][0];
           const float code = float((word >> bit) & kMask);
-          int t, d;
-          float sc, mn;
-          if (is_v) {
-            layout::v_chunk_elem(cmb, lane, e, &t, &d);
-            sc = float(vs[(d >> 5) * 32 + t]);
-            mn = float(vm[(d >> 5) * 32 + t]);
-          } else {
-            layout::k_chunk_elem(cmb, lane, e, D, &t, &d);
-            sc = float(ks[d]);
-            mn = float(km[d]);
-          }
-          pair |= uint32_t(f32_to_bf16_rne(__builtin_fmaf(code, sc, mn))) << (16 * h);
+          const float sc = float(__builtin_bit_cast(_Float16, uint16_t(sw[e2] >> (16 * h))));
+          const float mn = float(__builtin_bit_cast(_Float16, uint16_t(mw[e2] >> (16 * h))));
+          f[h] = __builtin_fmaf(code, sc, mn);
         }
-        out[e2] = pair;
+        out[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
       }
-      reinterpret_cast<uint4*>(tb + (is_v ? 32 * D : 0))[cc] = make_uint4(out[0], out[1], out[2], out[3]);
+      pout[k][j] = make_uint4(out[0], out[1], out[2], out[3]);
     }
-    __syncthreads();
+    pend[k] = tb;
+    // the other set was stored at the top of this unit: keep its registers
+    // (the stores' data) out of the decode's temporaries
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) asm volatile("" ::"v"(pout[k ^ 1][j].x), "v"(pout[k ^ 1][j].y),
+                                               "v"(pout[k ^ 1][j].z), "v"(pout[k ^ 1][j].w));
+  };
+  while (u < units) {
+    step(0);
+    u += gridDim.x;
+    if (u >= units) break;
+    step(1);
+    u += gridDim.x;
   }
+  flush(0);
+  flush(1);
 }
 
 static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t* items, int stride,
@@ -578,26 +646,23 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (cap <= 0) return hipSuccess;
-  // three workgroups per compute unit in all (the quantise kernel's
-  // occupancy: one round, no tail of late workgroups), never more than the
-  // largest unit count
+  // the quantise kernel: three workgroups per compute unit in all (its
+  // occupancy: one round, no tail of late workgroups); the dequantise kernel
+  // (latency-bound, small footprint): eight.  Never more than the largest
+  // unit count.
   const long max_units = long(cap) * pv.Hkv * (pv.W / 32);
-  long gx = (3L * pv.cus + pv.B - 1) / pv.B;
+  long gx = ((promote ? 8L : 3L) * pv.cus + pv.B - 1) / pv.B;
   if (gx > max_units) gx = max_units;
   if (gx < 1) gx = 1;
   const int wi = pv.lbits == 2 ? 0 : (pv.lbits == 4 ? 1 : 2);
   const int di = pv.D == 64 ? 0 : 1;
-  typedef void (*Kern)(PoolView, int);
-  typedef void (*QKern)(PoolView, int, const WorkItem*);
+  typedef void (*Kern)(PoolView, int, const WorkItem*);
   static const Kern kDequant[2][3] = {{dequant_kernel<64, 2>, dequant_kernel<64, 4>, dequant_kernel<64, 8>},
                                       {dequant_kernel<128, 2>, dequant_kernel<128, 4>, dequant_kernel<128, 8>}};
-  static const QKern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
-                                     {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
-  if (promote)
-    hipLaunchKernelGGL(kDequant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer);
-  else
-    hipLaunchKernelGGL(kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv, layer,
-                       reinterpret_cast<const WorkItem*>(pv.work + pv.work_items));
+  static const Kern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
+                                    {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
+  hipLaunchKernelGGL(promote ? kDequant[di][wi] : kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv,
+                     layer, reinterpret_cast<const WorkItem*>(pv.work + pv.work_items));
   return hipGetLastError();
 }
 
