@@ -128,9 +128,29 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
     cnt = cap;
     errs |= KV_ERR_ITEM_RANGE;
   }
-  for (int w = tid; w < maxw; w += blockDim.x) pages[w] = gp[w];
+  // the row and the item list (its first cap entries: no wait for the
+  // count), eight loads per thread in flight at a time; buffer loads read
+  // zeros past the ends without touching memory
+  {
+    const auto rp = __builtin_amdgcn_make_buffer_rsrc(gp, (short)0, maxw * 4, 0x00020000);
+    const auto ri = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(items + size_t(b) * stride), (short)0,
+                                                      cap * 4, 0x00020000);
+    for (int base = 0; base < maxw; base += 8 * 256) {   // (cap <= maxw)
+      uint32_t rw[8], ri8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        rw[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, (base + 256 * j + tid) * 4, 0, 0);
+        ri8[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, (base + 256 * j + tid) * 4, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int x = base + 256 * j + tid;
+        if (x < maxw) pages[x] = rw[j];
+        if (x < cap) item_w[x] = int32_t(ri8[j]);
+      }
+    }
+  }
   for (int i = tid; i < words; i += blockDim.x) used[i] = 0u;
-  for (int i = tid; i < cnt; i += blockDim.x) item_w[i] = items[size_t(b) * stride + i];
   __syncthreads();
   for (int w = tid; w < maxw; w += blockDim.x) {
     const uint32_t e = pages[w];
