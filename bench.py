@@ -85,10 +85,16 @@ def route_bytes(c, n_windows, first_quant, promotions, bits=2):
     return c.batch * n_windows * (4 + 4) + move_bytes(c, first_quant + promotions, bits)
 
 
+# the sources the attention kernel is compiled from (the traffic counters of a
+# launch depend on these alone), and its build flags
+ATTN_SOURCES = ("attn.hip", "device_common.h", "layout.h", "launch.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "tiered_int2_fp16_amd", "csrc"))):
+    for f in ATTN_SOURCES:
         h.update(open(os.path.join(ROOT, "tiered_int2_fp16_amd", "csrc", f), "rb").read())
+    h.update(open(os.path.join(ROOT, "tiered_int2_fp16_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 

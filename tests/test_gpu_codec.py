@@ -89,8 +89,9 @@ def test_demote_codes_at_edge_cases(bits, D, W):
         with np.errstate(invalid="ignore", over="ignore"):
             wk, wv = codec.promote_bits(entries[w])
         for part, want in ((got[0], wk), (got[1], wv)):
-            nan = (want & 0x7F80 == 0x7F80) & (want & 0x7F != 0)
+            nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
             assert np.array_equal(part[~nan], want[~nan]), (bits, D, W, w)
-            assert np.all((part[nan] & 0x7F80 == 0x7F80) & (part[nan] & 0x7F != 0)), (bits, D, W, w)
+            pn = part[nan]
+            assert np.all(((pn & 0x7F80) == 0x7F80) & ((pn & 0x7F) != 0)), (bits, D, W, w)
     log(f"{bits}-bit, head_dim {D}, window {W}: {n} windows of edge-case groups bit-exact, "
         "demoted and promoted")

@@ -533,8 +533,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   auto flush_masses = [&](int nt, const uint32_t* list, bool from_top = false) {
     if (!want_mass) return;
     __builtin_amdgcn_wave_barrier();
+    // heads fastest: the G records of a tile (adjacent in memory) go out from
+    // adjacent lanes, one contiguous piece per tile
     for (int idx = lane; idx < nt * G; idx += 64) {
-      const int h = idx / nt, t = idx - h * nt;
+      const int t = idx / G, h = idx - t * G;
       const uint32_t e = list[t];
       tmass[(size_t(te_win(e)) * TPW + te_tile(e)) * pv.Hq + h] = rec[from_top ? kList - 1 - t : t][h];
     }
@@ -938,11 +940,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     // the query again from memory (the one wave that takes this block): left
     // in qb, its conversions were hoisted ahead of the tile loads
     const auto rq = tile_rsrc(q_arg + (size_t(b) * hq_arg + size_t(kvh) * g_arg) * D, g_arg * D * 2);
+    // the lane's byte offset into the query, formed here from an opaque copy
+    // of the lane index: an offset shared with the first query load would be
+    // kept across the tile loops, where registers run out (it was spilled)
+    const int ln = int(opaque(uint32_t(lane)));
+    const int hq2 = (ln & 15) % GP, g2 = ln >> 4;
     float zp = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 kv = as_bf16x8(*reinterpret_cast<const uint4*>(kn + 32 * kk + 8 * g));
-      const bf16x8 qa = as_bf16x8(load16(rq, boff(hh < g_arg, (hh * D + 32 * kk + 8 * g) * 2)));
+      const bf16x8 kv = as_bf16x8(*reinterpret_cast<const uint4*>(kn + 32 * kk + 8 * g2));
+      const bf16x8 qa = as_bf16x8(load16(rq, boff(hq2 < g_arg, (hq2 * D + 32 * kk + 8 * g2) * 2)));
 #pragma unroll
       for (int e = 0; e < 8; ++e) zp = fmaf(float(qa[e]), float(kv[e]), zp);
     }
