@@ -1,0 +1,112 @@
+"""Transition plans with repeated items, bad items and too few slots.
+
+The plan's outcome is defined as taking the items one by one in list order:
+an item outside the window range is an error; a window in the wrong tier is a
+state error; a valid item takes a free slot, and when none is left fails with
+a no-slot error (kvtier.h, kv_demote_quantize / kv_promote_dequantize).  The
+kernel computes all items at once; these lists mix every case, repeat
+windows (a repeat after a success sees the moved window, after a failure
+fails the same way), and run past 256 items (more than one round of the
+workgroup).  The expected tiers and error bits come from walking the list in
+order here; the moved windows' bytes are compared with the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+
+from oracle import codec
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from tests.gpu_harness import dev, log  # noqa: E402
+
+F, Q = 2, 1
+ITEM_RANGE, DEMOTE_STATE, PROMOTE_STATE, NO_BF16, NO_LEDGER = 32, 1, 2, 4, 8
+
+
+def _walk(tier, has_ledger, items, n, promote, free_slots):
+    """The list taken in order: new tiers, error bits, the moved windows."""
+    tier = list(tier)
+    errs, moved = 0, []
+    for w in items:
+        if w < 0 or w >= n:
+            errs |= ITEM_RANGE
+        elif not promote:
+            if tier[w] != F:
+                errs |= DEMOTE_STATE
+            elif has_ledger[w]:
+                tier[w] = Q
+            elif free_slots > 0:
+                free_slots -= 1
+                tier[w] = Q
+                moved.append(w)
+            else:
+                errs |= NO_LEDGER
+        else:
+            if tier[w] != Q or not has_ledger[w]:
+                errs |= PROMOTE_STATE
+            elif free_slots > 0:
+                free_slots -= 1
+                tier[w] = F
+                moved.append(w)
+            else:
+                errs |= NO_BF16
+    return tier, errs, moved
+
+
+def _pool(n, ledger_slots, bf16_slots, rng):
+    from tiered_int2_fp16_amd import binding as B
+    W, D = 32, 64
+    cfg = B.make_config(1, 1, 1, 1, D, W, n, 1, bf16_slots, ledger_slots, 2)
+    pool = B.Pool(cfg)
+    kv = rng.standard_normal((2, n * W, D)).astype(np.float32)
+    bits = (kv.view(np.uint32) >> 16).astype(np.uint16)
+    pool.prefill(0, dev(bits[0].reshape(1, 1, n * W, D)), dev(bits[1].reshape(1, 1, n * W, D)), n * W,
+                 dev(np.ones((1, n), np.float32)))
+    return pool, bits.reshape(2, n, W, D)
+
+
+def _state(pool, n):
+    pages = pool.pages(0).cpu().numpy().view(np.uint32)[0][:n]
+    return (pages & 3).tolist(), ((pages >> 2) & 1).astype(bool).tolist()
+
+
+@pytest.mark.parametrize("n,ledger_slots,extra", [(16, 3, 0), (512, 280, 40)])
+def test_plan_repeats_bad_items_and_exhaustion(n, ledger_slots, extra):
+    rng = np.random.default_rng(n)
+    pool, bits = _pool(n, ledger_slots, n, rng)
+    if n == 16:
+        dem = [2, 5, 2, 7, 100, 9, 5, 11, -1, 7]
+    else:   # 300 distinct windows, 40 repeats and a few out of range, shuffled
+        base = rng.permutation(n - 1)[:300].tolist()
+        dem = base + rng.choice(base, extra).tolist() + [n + 3, -7, n - 1 + 100]
+        dem = [dem[i] for i in rng.permutation(len(dem))]
+    tier0, led0 = _state(pool, n)
+    want_tier, want_err, moved = _walk(tier0, led0, dem, n, False, ledger_slots)
+    pool.demote(0, dev(np.array([dem], np.int32)), dev(np.array([len(dem)], np.int32)))
+    tier, led = _state(pool, n)
+    assert tier == want_tier
+    assert pool.check() == want_err
+    for w in moved[:12] + moved[-4:]:
+        got = pool.read_ledger(0, 0, w).cpu().numpy()[0]
+        want = codec.entry_bytes(codec.quantize_window(bits[0, w], bits[1, w], 2), 2)
+        assert got.tobytes() == want, w
+    # promotions: repeats, windows in the wrong tier, and more than the free bf16 slots
+    q = [w for w in range(n) if tier[w] == Q]
+    free_bf16 = n - sum(1 for w in range(n) if tier[w] == F)
+    pro = q[:3] + q[:2] + [0 if tier[0] == F else 1, n + 5] + q[3:]
+    want_tier2, want_err2, moved2 = _walk(tier, led, pro, n, True, free_bf16)
+    pool.promote(0, dev(np.array([pro], np.int32)), dev(np.array([len(pro)], np.int32)))
+    tier2, _ = _state(pool, n)
+    assert tier2 == want_tier2
+    assert pool.check() == want_err2
+    for w in moved2[:8]:
+        got = pool.read_window(0, 0, w).cpu().numpy().view(np.uint16)[0]
+        e = codec.quantize_window(bits[0, w], bits[1, w], 2)
+        wk, wv = codec.promote_bits(e)
+        assert np.array_equal(got[0], wk) and np.array_equal(got[1], wv), w
+    log(f"{n} windows: {len(dem)} demote items ({len(moved)} moved, errors {want_err:#x}), "
+        f"{len(pro)} promote items ({len(moved2)} moved, errors {want_err2:#x})")

@@ -85,48 +85,48 @@ struct WorkItem {
   int w, src, dst, flag;  // flag 1: move bytes; 2: tier flip only; 0: invalid
 };
 
-// Lowest free slot at or after word *cursor (slots are taken in ascending
-// order, so the words before the cursor are full); marks it used.
-__device__ inline int take_free(uint32_t* bits, int nbits, int* cursor) {
-  for (int word = *cursor; word * 32 < nbits; ++word) {
-    const uint32_t x = ~bits[word];
-    if (x) {
-      const int j = word * 32 + __builtin_ctz(x);
-      if (j >= nbits) return -1;
-      bits[word] |= 1u << (j & 31);
-      *cursor = word;
-      return j;
-    }
-  }
-  *cursor = (nbits + 31) / 32;
-  return -1;
-}
-
 // promote == false: demote plan (ledger slots); true: promote plan (bf16 slots).
-// One workgroup per sequence.  The page table, the occupied-slot bitmap and
-// the item list are staged in LDS; items are then validated and given slots
-// in list order (the lowest free slot each), and the page table is written
-// back.
+// One workgroup per sequence.  The page-table row, the free-slot bitmap and
+// the item list are staged in LDS.  The outcome is that of taking the items
+// one by one in list order, each valid item the lowest free slot, computed
+// for all items at once:
+//  - an item is checked against the pre-transition row; a window listed
+//    again after its first occurrence has the outcome of that occurrence's
+//    state: after a success it has moved (a state error), after a failure
+//    it fails the same way;
+//  - the k-th item (in list order) that needs a slot takes the k-th free
+//    slot in ascending order, and every such item from the free count on
+//    finds none (no slot is freed during a plan).
+// Then the work list and the updated row are written back.
 __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const int32_t* items, int stride,
                                                    const int32_t* counts, int promote) {
   extern __shared__ uint32_t smem[];
+  __shared__ int s_wsum[4];
+  __shared__ int s_errs;
   const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int maxw = pv.maxw, W = pv.W;
   const int nslots = promote ? pv.nb : pv.nl;
   const int words = (nslots + 31) / 32;
   const int cap = stride < maxw ? stride : maxw;
-  uint32_t* pages = smem;                                         // [maxw]
-  uint32_t* used = smem + maxw;                                   // [words]
-  int32_t* item_w = reinterpret_cast<int32_t*>(used + words);    // [cap]
+  uint32_t* pages = smem;                                             // [maxw]
+  uint32_t* freew = pages + maxw;                                     // [words] free slots
+  int32_t* fpc = reinterpret_cast<int32_t*>(freew + words);          // [words + 1] free slots before a word
+  // [cap] the items: their windows, then each item's outcome packed as
+  // window | flag << 12 | error kind << 14 | slot << 16 (flag 1: move bytes,
+  // 2: tier flip only; error kind 1: window out of range, 2: state, 3: no
+  // free slot)
+  int32_t* item_w = fpc + words + 1;
+  int32_t* first = item_w + cap;                                      // [maxw] first list position
   const int len = pv.tokens[seg];
   const int n = windows_of(len, W);
   uint32_t* gp = pv.pages + size_t(seg) * maxw;
   int cnt = counts[b];
-  int errs = 0;
+  if (tid == 0) s_errs = 0;
   if (cnt < 0) cnt = 0;
   if (cnt > cap) {
     cnt = cap;
-    errs |= KV_ERR_ITEM_RANGE;
+    if (tid == 0) s_errs = KV_ERR_ITEM_RANGE;
   }
   // the row and the item list (its first cap entries: no wait for the
   // count), eight loads per thread in flight at a time; buffer loads read
@@ -145,71 +145,147 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int x = base + 256 * j + tid;
-        if (x < maxw) pages[x] = rw[j];
+        if (x < maxw) {
+          pages[x] = rw[j];
+          first[x] = 0x7FFFFFFF;
+        }
         if (x < cap) item_w[x] = int32_t(ri8[j]);
       }
     }
   }
-  for (int i = tid; i < words; i += blockDim.x) used[i] = 0u;
+  for (int i = tid; i < words; i += blockDim.x) {
+    const int rest = nslots - 32 * i;
+    freew[i] = rest >= 32 ? 0xFFFFFFFFu : ((1u << rest) - 1u);
+  }
   __syncthreads();
+  // occupied slots out of the free map; each window's first list position
   for (int w = tid; w < maxw; w += blockDim.x) {
     const uint32_t e = pages[w];
+    int sl = -1;
     if (promote) {
-      if (pe_tier(e) == TIER_F && w < n) {
-        const int sl = pe_bslot(e);
-        if (sl < nslots) atomicOr(&used[sl >> 5], 1u << (sl & 31));
-      }
+      if (pe_tier(e) == TIER_F && w < n) sl = pe_bslot(e);
     } else if (pe_tier(e) != TIER_E && pe_has_ledger(e)) {
-      const int sl = pe_lslot(e);
-      if (sl < nslots) atomicOr(&used[sl >> 5], 1u << (sl & 31));
+      sl = pe_lslot(e);
     }
+    if (sl >= 0 && sl < nslots) atomicAnd(&freew[sl >> 5], ~(1u << (sl & 31)));
+  }
+  for (int i = tid; i < cnt; i += blockDim.x) {
+    const int w = item_w[i];
+    if (w >= 0 && w < n) atomicMin(&first[w], i);
   }
   __syncthreads();
-  WorkItem* work = reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + size_t(b) * maxw;
-  if (tid == 0) {
-    int cursor = 0;
-    for (int i = 0; i < cnt; ++i) {
+  // free slots before each word: one wave, 64 words a pass
+  if (wv == 0) {
+    int run = 0;
+    for (int w0 = 0; w0 < words; w0 += 64) {
+      const int wd = w0 + lane;
+      const int c = wd < words ? __popc(freew[wd]) : 0;
+      int incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (wd < words) fpc[wd] = run + incl - c;
+      run += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) fpc[words] = run;
+  }
+  __syncthreads();
+  const int nfree = fpc[words];
+  // items in rounds of 256: validation against the pre-transition row, rank
+  // among the items that need a slot, slot
+  int base = 0;
+  for (int r0 = 0; r0 < cnt; r0 += 256) {
+    const int i = r0 + tid;
+    int need = 0, flag = 0, err = 0, slot = 0;
+    if (i < cnt) {
       const int w = item_w[i];
-      WorkItem it{w, -1, -1, 0};
       if (w < 0 || w >= n) {
-        errs |= KV_ERR_ITEM_RANGE;
-      } else {
+        err = KV_ERR_ITEM_RANGE;
+      } else if (first[w] == i) {
         const uint32_t e = pages[w];
         if (!promote) {
-          if (pe_tier(e) != TIER_F || (w + 1) * W > len) {
-            errs |= KV_ERR_DEMOTE_STATE;
-          } else if (pe_has_ledger(e)) {
-            pages[w] = pe_make(TIER_Q, true, 0, pe_lslot(e));
-            it.flag = 2;
-          } else {
-            const int j = take_free(used, nslots, &cursor);
-            if (j < 0) {
-              errs |= KV_ERR_NO_LEDGER_SLOT;
-            } else {
-              pages[w] = pe_make(TIER_Q, true, 0, j);
-              it = WorkItem{w, pe_bslot(e), j, 1};
-            }
-          }
+          if (pe_tier(e) != TIER_F || (w + 1) * W > len) err = KV_ERR_DEMOTE_STATE;
+          else if (pe_has_ledger(e)) flag = 2;
+          else need = 1;
         } else {
-          if (pe_tier(e) != TIER_Q || !pe_has_ledger(e)) {
-            errs |= KV_ERR_PROMOTE_STATE;
-          } else {
-            const int j = take_free(used, nslots, &cursor);
-            if (j < 0) {
-              errs |= KV_ERR_NO_BF16_SLOT;
-            } else {
-              pages[w] = pe_make(TIER_F, true, j, pe_lslot(e));
-              it = WorkItem{w, pe_lslot(e), j, 1};
-            }
-          }
+          if (pe_tier(e) != TIER_Q || !pe_has_ledger(e)) err = KV_ERR_PROMOTE_STATE;
+          else need = 1;
         }
       }
-      work[i] = it;
     }
-    pv.work[pv.work_counts + b] = cnt;
-    if (errs) set_err(pv.err, errs);
+    const uint64_t bal = __ballot(need);
+    if (lane == 0) s_wsum[wv] = __popcll(bal);
+    __syncthreads();
+    int rank = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
+    for (int v = 0; v < wv; ++v) rank += s_wsum[v];
+    base += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+    if (need) {
+      if (rank < nfree) {
+        // the word holding free slot number `rank`, then that slot within it
+        int lo = 0, hi = words;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (fpc[mid] <= rank) lo = mid;
+          else hi = mid;
+        }
+        uint32_t x = freew[lo];
+        for (int k = rank - fpc[lo]; k > 0; --k) x &= x - 1u;
+        slot = 32 * lo + __builtin_ctz(x);
+        flag = 1;
+      } else {
+        err = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
+      }
+    }
+    const int kind = err == KV_ERR_ITEM_RANGE ? 1 : (err == 0 ? 0 : (need ? 3 : 2));
+    __syncthreads();   // (every thread has read its item's window above)
+    if (i < cnt)
+      item_w[i] = int32_t(uint32_t(kind == 1 ? 0 : item_w[i]) | (uint32_t(flag) << 12) | (uint32_t(kind) << 14) |
+                          (uint32_t(slot) << 16));
   }
   __syncthreads();
+  // the work list; first occurrences update the row, later ones take their
+  // first occurrence's state
+  WorkItem* work = reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + size_t(b) * maxw;
+  const int err_state = promote ? KV_ERR_PROMOTE_STATE : KV_ERR_DEMOTE_STATE;
+  const int err_slot = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
+  int errs = 0;
+  for (int i = tid; i < cnt; i += blockDim.x) {
+    const uint32_t o = uint32_t(item_w[i]);
+    const int w = int(o & 0xFFFu), flag = int((o >> 12) & 3u), slot = int(o >> 16);
+    int kind = int((o >> 14) & 3u);
+    WorkItem it{w, -1, -1, 0};
+    if (kind != 1 && first[w] != i) {
+      // a later listing of the window: its first occurrence moved it (a
+      // state error now), or failed, and this one fails the same way
+      const uint32_t of = uint32_t(item_w[first[w]]);
+      kind = ((of >> 12) & 3u) ? 2 : int((of >> 14) & 3u);
+    } else if (flag) {
+      const uint32_t e = pages[w];
+      if (!promote) {
+        if (flag == 2) {
+          pages[w] = pe_make(TIER_Q, true, 0, pe_lslot(e));
+          it.flag = 2;
+        } else {
+          pages[w] = pe_make(TIER_Q, true, 0, slot);
+          it = WorkItem{w, pe_bslot(e), slot, 1};
+        }
+      } else {
+        pages[w] = pe_make(TIER_F, true, slot, pe_lslot(e));
+        it = WorkItem{w, pe_lslot(e), slot, 1};
+      }
+    }
+    errs |= kind == 1 ? KV_ERR_ITEM_RANGE : (kind == 2 ? err_state : (kind == 3 ? err_slot : 0));
+    work[i] = it;
+  }
+  if (errs) atomicOr(&s_errs, errs);
+  __syncthreads();
+  if (tid == 0) {
+    pv.work[pv.work_counts + b] = cnt;
+    if (s_errs) set_err(pv.err, s_errs);
+  }
   for (int w = tid; w < maxw; w += blockDim.x) gp[w] = pages[w];
 }
 
@@ -660,7 +736,9 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
                                     const int32_t* counts, bool promote, hipStream_t s) {
   const int nslots = promote ? pv.nb : pv.nl;
   const int cap = stride < pv.maxw ? stride : pv.maxw;
-  const size_t shm = (size_t(pv.maxw) + size_t((nslots + 31) / 32) + size_t(cap > 0 ? cap : 0)) * 4;
+  const int words = (nslots + 31) / 32, capw = cap > 0 ? cap : 0;
+  // plan LDS: row, free map and its word prefix, items, first positions
+  const size_t shm = (2 * size_t(pv.maxw) + 2 * size_t(words) + 1 + size_t(capw)) * 4;
   hipLaunchKernelGGL(plan_kernel, dim3(pv.B), dim3(256), shm, s, pv, layer, items, stride, counts,
                      int(promote));
   hipError_t e = hipGetLastError();
