@@ -610,6 +610,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   // decode constants (mask of a code pair's fields, exponent of 1.0), held in
   // VGPRs for the bit selects
   const uint32_t kMaskR = opaque(BITS == 2 ? 0x03000300u : 0x03C003C0u), kOneR = opaque(0x3C003C00u);
+  const float kNegOne = __int_as_float(uniform(int(opaque(0xBF800000u))));   // -1.0f in an SGPR
   // 2^b q in fp16 (4q for INT2) and this lane's slices of the tile constant
   // (q4[jc + i * NREP], zero past KK); formed once the wave's first tile loads
   // are out, so the wait for the query never holds them back
@@ -721,12 +722,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     softmax_tile<NB, BITS>(st, z, qscale, bias0 * qscale, p, &rs);   // p = 2^b x probability
     // 2^b p as fp16 high + low parts, then 2^b p s' = high*s' + (exact
     // residual of that product + low*s'), all in packed fp16
+    // (the residual x - p4 is exact in fp32; taken as a fused multiply-add
+    // by -1 held in a register, it is one mixed-precision FMA that reads its
+    // fp16 half of p4's packed register, instead of a conversion back to fp32
+    // and a subtraction; the empty asm keeps the compiler from converting p
+    // to fp16 a second time for those reads)
     f16x8 p4, p4l;
 #pragma unroll
-    for (int e2 = 0; e2 < 8; ++e2) {
-      const float x = p[e2];
-      p4[e2] = (_Float16)x;
-      p4l[e2] = (_Float16)(x - float(p4[e2]));
+    for (int r = 0; r < 4; ++r) {
+      const f16x2 h2 = __builtin_bit_cast(
+          f16x2, opaque(__builtin_bit_cast(uint32_t, f16x2{(_Float16)p[2 * r], (_Float16)p[2 * r + 1]})));
+      p4[2 * r] = h2[0];
+      p4[2 * r + 1] = h2[1];
+      p4l[2 * r] = (_Float16)__builtin_fmaf(float(h2[0]), kNegOne, p[2 * r]);
+      p4l[2 * r + 1] = (_Float16)__builtin_fmaf(float(h2[1]), kNegOne, p[2 * r + 1]);
     }
     // v = (m' - 2^b s') + (1 + c/2^b) 2^b s'.  The min term, 2^b times over:
     // sum_t 2^b p m' + sum_t 2^b p (-2^b s'), straight from the fp16 scales
