@@ -827,13 +827,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     }
   };
   // Both tiers in one loop: a wave with a long INT2 list and some bf16 tiles
-  // takes one bf16 tile after every four INT2 tiles, so that the bf16 bytes
+  // takes one bf16 tile after every eight INT2 tiles, so that the bf16 bytes
   // stream in while INT2 tiles are decoded (an INT2 tile costs far more
-  // instructions per byte than a bf16 tile).  Two INT2 tiles and one bf16
-  // tile are in flight; every load is unconditional (empty resources past the
-  // ends), so each tile waits only for its own loads.  INT2 tiles record
-  // their masses from the top rows of the record block, bf16 tiles from the
-  // bottom (both lists fit one chunk).
+  // instructions per byte than a bf16 tile); the bf16 tiles left over run in
+  // the bf16 loop after it.  A wave's loads complete in the order they were
+  // issued, so an INT2 tile requested behind a bf16 tile's 16 KB waits for
+  // all of it: one bf16 tile per eight INT2 tiles was measured faster than
+  // one per four, six, twelve or sixteen (128K loop and Mistral step).  Two
+  // INT2 tiles and one bf16 tile are in flight; every load is unconditional
+  // (empty resources past the ends), so each tile waits only for its own
+  // loads.  INT2 tiles record their masses from the top rows of the record
+  // block, bf16 tiles from the bottom (both lists fit one chunk).
   int f_done = 0;   // bf16 tiles of the first chunk taken in the mixed loop
   auto mixed_tiles = [&]() {
     const int nq = q_end - q_beg, nf = f_end - f_beg;
@@ -845,11 +849,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     load_f(FA, 0, nf);
     __builtin_amdgcn_sched_barrier(0);
     make_q4();
-    // whole groups of four (the tiles past the end load nothing and are not
+    // whole groups of eight (the tiles past the end load nothing and are not
     // computed): the loop has no early exit, so every path into its head has
     // the same loads in flight in the same order
     int jf = 0;
-    for (int i = 0; i < nq; i += 4) {
+    for (int i = 0; i < nq; i += 8) {
       compute_q(A, i, kList - 1 - i);
       load_q(A, i + 2, nq);
       __builtin_amdgcn_sched_barrier(0);
@@ -861,6 +865,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
       __builtin_amdgcn_sched_barrier(0);
       if (i + 3 < nq) compute_q(Bq, i + 3, kList - 4 - i);
       load_q(Bq, i + 5, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 4 < nq) compute_q(A, i + 4, kList - 5 - i);
+      load_q(A, i + 6, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 5 < nq) compute_q(Bq, i + 5, kList - 6 - i);
+      load_q(Bq, i + 7, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 6 < nq) compute_q(A, i + 6, kList - 7 - i);
+      load_q(A, i + 8, nq);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 7 < nq) compute_q(Bq, i + 7, kList - 8 - i);
+      load_q(Bq, i + 9, nq);
       __builtin_amdgcn_sched_barrier(0);
       if (jf < nf) compute_f(FA, jf);
       ++jf;
