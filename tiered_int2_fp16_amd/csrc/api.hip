@@ -66,8 +66,6 @@ PoolView view(const kv_pool* p) {
   v.lbits = g.cfg.ledger_bits;
   v.work_items = int(g.work_items);
   v.work_counts = int(g.work_counts);
-  v.attn_counters = int(g.attn_counters);
-  v.seg_counters = int(g.seg_counters);
   v.cus = p->cus;
   return v;
 }

@@ -32,7 +32,7 @@ struct PoolView {
   int32_t* err;       // device error word
   int B, L, Hq, Hkv, D, W, maxw, R, nb, nl, G;
   int lbits;          // ledger code width: 2, 4 or 8
-  int work_items, work_counts, attn_counters, seg_counters;  // int32 offsets into work
+  int work_items, work_counts;  // int32 offsets into work
   int cus;            // compute units of the pool's device (launch sizing)
 
   __device__ uint16_t* block(int seg, int slot, int kvh) const {

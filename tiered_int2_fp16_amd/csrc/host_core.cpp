@@ -54,8 +54,6 @@ bool geometry_init(const kv_pool_config& c, Geometry* g, std::string* err) {
   size_t w = 0;
   r.work_items = w;    w += size_t(c.batch) * c.max_windows * 4;
   r.work_counts = w;   w += size_t(c.batch);
-  r.attn_counters = w; w += size_t(c.batch) * c.kv_heads;
-  r.seg_counters = w;  w += size_t(c.batch);
   r.size[KV_REGION_WORK] = w * 4;
   r.size[KV_REGION_ERR] = 4;
   size_t off = 0;

@@ -30,8 +30,6 @@ struct Geometry {
   // KV_REGION_WORK sub-layout (int32 offsets into the region)
   size_t work_items = 0;      // int4 [batch][max_windows]: window, src, dst, flag
   size_t work_counts = 0;     // int  [batch]
-  size_t attn_counters = 0;   // int  [batch][kv_heads], zero at rest
-  size_t seg_counters = 0;    // int  [batch], zero at rest
 };
 
 // Validate `cfg` and fill `g`.  On failure returns false with a message.
