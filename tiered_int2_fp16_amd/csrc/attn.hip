@@ -1179,6 +1179,11 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       }
     }
     if (act) s_acc[tid] = acc;
+    // the append decision is read here, ahead of the output store: the memory
+    // counter is in order, so a read of it after the store would wait for the
+    // store's completion
+    const int app = uniform(int(inf4.x)), slot = uniform(int(inf4.y)), row = uniform(int(inf4.z));
+    const int newwin = uniform(int(inf4.w)), len_old = uniform(int(i4));
     __syncthreads();
     if (tid < items) {
       float4 t4 = s_acc[tid];
@@ -1190,8 +1195,6 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       *reinterpret_cast<float4*>(out_p + (size_t(b) * Hq + size_t(kvh) * G + h) * D + d) =
           make_float4(t4.x * iz, t4.y * iz, t4.z * iz, t4.w * iz);
     }
-    const int app = uniform(int(inf4.x)), slot = uniform(int(inf4.y)), row = uniform(int(inf4.z));
-    const int newwin = uniform(int(inf4.w)), len_old = uniform(int(i4));
     if (app && sl == 0) {
       // the appended token joins its window (no kernel of this step reads it)
       const int len = len_old + 1;
@@ -1331,6 +1334,10 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
     tile_masses(p0, t2);
     masses(p0, t2);
   }
+  // the old score is taken into its register here, ahead of the mass stores:
+  // the memory counter is in order, so waiting for it after the stores would
+  // wait for their completion (an empty asm statement that reads the register)
+  asm volatile("" ::"v"(s_old));
   __syncthreads();
   // masses out in window order (16 consecutive windows per head)
   if (mass_p) {
