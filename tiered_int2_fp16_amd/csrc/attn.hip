@@ -1201,8 +1201,12 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
       const int n_old = windows_of(len_old, W);
       uint16_t* dst = bf16_p + ((size_t(seg) * nb + slot) * Hkv + kvh) * size_t(2 * W * D);
       for (int dd = tid; dd < D; dd += 256) {
-        dst[layout::bf16_window_k(row, dd, D)] = kn_p[(size_t(b) * Hkv + kvh) * D + dd];
-        dst[layout::bf16_window_v(row, dd, D)] = vn_p[(size_t(b) * Hkv + kvh) * D + dd];
+        // both values loaded before either store (a load after a store would
+        // wait for the store's completion)
+        const uint16_t kv = kn_p[(size_t(b) * Hkv + kvh) * D + dd];
+        const uint16_t vv = vn_p[(size_t(b) * Hkv + kvh) * D + dd];
+        dst[layout::bf16_window_k(row, dd, D)] = kv;
+        dst[layout::bf16_window_v(row, dd, D)] = vv;
       }
       if (kvh == 0 && tid == 0) {
         if (newwin) pages_p[size_t(seg) * maxw + n_old] = pe_make(TIER_F, false, slot, 0);
