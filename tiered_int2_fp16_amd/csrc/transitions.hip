@@ -552,10 +552,21 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer
           for (int k = 0; k < 2; ++k) {
             const uint32_t hw = (&vals[k].x)[e >> 1];
             const float u = __uint_as_float((e & 1) ? (hw & 0xFFFF0000u) : (hw << 16)) - P.x;
-            uint32_t code;
+            int wb, bit;
+            const int cmb = BITS == 2 ? 2 * w[k] + j : (BITS == 4 ? w[k] : w[k] >> 1);
+            layout::code_pos(cmb, lane[k], e, D, BITS, &wb, &bit);
             if (BITS == 2) {
-              code = uint32_t(u > P.y) + uint32_t(u >= P.z) + uint32_t(u > P.w);
+              // With t0 < t1 < t2 (finite s > 0), u >= t1 implies u > t0
+              // and u < t1 implies u <= t2: one comparison picks the half, a
+              // second the code within it; the two bits go in as constants
+              // at the field's position.  (s = 0 or inf: the thresholds are
+              // all inf and a finite u gets 0 either way; u = +inf there
+              // means the defining quotient u/s is inf/inf, which has no
+              // code.)
+              const bool up = u >= P.z;
+              word[k] |= (up ? (2u << bit) : 0u) | (u > (up ? P.w : P.y) ? (1u << bit) : 0u);
             } else {
+              uint32_t code;
               const float c = rintf(__builtin_amdgcn_fmed3f(u * P.y, 0.f, kTop));
               const int ci = int(c), odd = ci & 1;
               const float tlo = fmaf(c, P.z, -P.w);   // (c - 1/2) s
@@ -565,11 +576,8 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer
               const int cc = ci - int(u < __int_as_float(__float_as_int(tlo) + odd)) +
                              int(u > __int_as_float(__float_as_int(thi) - odd));
               code = uint32_t(cc < 0 ? 0 : (cc > int(kTop) ? int(kTop) : cc));
+              word[k] |= code << bit;
             }
-            int wb, bit;
-            const int cmb = BITS == 2 ? 2 * w[k] + j : (BITS == 4 ? w[k] : w[k] >> 1);
-            layout::code_pos(cmb, lane[k], e, D, BITS, &wb, &bit);
-            word[k] |= code << bit;
           }
         }
       }
