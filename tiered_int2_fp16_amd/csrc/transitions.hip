@@ -301,8 +301,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 // the chunk and field index arithmetic below then reduces to shifts, masks and
 // constants)
 //
-// Per unit (one 32-token tile of one kv head), three phases, two barriers
-// (alternate units use alternate LDS buffers):
+// Per unit (one 32-token tile of one kv head), three phases and three
+// barriers, one LDS buffer (so that four workgroups fit a CU at head_dim 128;
+// two buffers for alternate units, one barrier fewer, held it to three):
 //  0. every thread writes its 16-byte chunks of the tile (loaded into
 //     registers while the previous unit was processed) to LDS with one store
 //     each: K as [token][channel], V as [channel][token];
@@ -317,8 +318,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 // they are then stored, just before the loads of the unit after it are
 // issued, so those loads never wait behind freshly issued stores.
 template <int D, int BITS>
-__global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer,
-                                                         const WorkItem* __restrict__ items) {
+__global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolView pv, int layer,
+                                                                        const WorkItem* __restrict__ items) {
   constexpr int KP = D + 8;    // K rows [token][channel] (bf16), padded
   constexpr int VP = 40;       // V rows [channel][token] (bf16), padded; 8 more per 32 rows
   constexpr int CWB = BITS * D / 64;          // code words per lane per part
@@ -327,14 +328,11 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer
   constexpr int NCH = 8 * D / 256;            // 16-byte chunks per thread (K and V)
   constexpr int NCW = BITS == 2 ? 2 : 1;      // chunks per code word
   constexpr float kTop = float((1 << BITS) - 1);
-  // two buffers, used by alternate units: a unit's first phase may then begin
-  // while slower threads still read the previous unit's data (two barriers
-  // per unit)
-  __shared__ __attribute__((aligned(16))) uint16_t sk2[2][32 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sv2[2][D * VP + (D / 32) * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sk[32 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[D * VP + (D / 32) * 8];
   // group parameters (phase 1 to phase 2): K group of channel d at d, V group
   // (token t, block j) at D + 32 j + t
-  __shared__ float4 pp2[2][2 * D];
+  __shared__ float4 pp[2 * D];
   auto vrow = [](int d) { return d * VP + (d >> 5) * 8; };   // (a wave's two 32-row blocks hit other banks)
   const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
   const bool has_group = 2 * D >= 256 || tid < 2 * D;   // phase 1 threads (whole waves)
@@ -412,13 +410,10 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer
   WorkItem it = item_of(u);
   uint4 qv[NCH];
   fetch(u, it, qv);
-  int par = 0;
   for (; u < units; u += gridDim.x) {
     const WorkItem itn = item_of(u + gridDim.x);
     const bool move = it.flag == 1;   // (the same for the whole workgroup)
-    uint16_t* sk = sk2[par];
-    uint16_t* sv = sv2[par];
-    float4* pp = pp2[par];
+    __syncthreads();   // every thread is done with the previous unit's LDS data
     const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
     uint8_t* et = pv.entry(seg, it.dst, kvh) + size_t(tile) * LT.bytes;
     // 0. chunks to LDS: chunk c < 4 D is K chunk (cmb, lane) = (c / 64, c % 64),
@@ -441,7 +436,6 @@ __global__ __launch_bounds__(256, 3) void quantize_kernel(PoolView pv, int layer
     fetch(u + gridDim.x, itn, qv);   // the next unit's bytes, in flight during the rest of this one
     it = itn;
     if (!move) continue;
-    par ^= 1;
     __syncthreads();
     // 1. group parameters.  The first D threads take the K groups, the next D
     //    the V groups (whole waves each).  A thread reads 16 bf16 pairs: half
@@ -752,12 +746,12 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (cap <= 0) return hipSuccess;
-  // the quantise kernel: three workgroups per compute unit in all (its
-  // occupancy: one round, no tail of late workgroups); the dequantise kernel
-  // (latency-bound, small footprint): eight.  Never more than the largest
-  // unit count.
+  // the quantise kernel: its occupancy in workgroups per compute unit (four
+  // at head_dim 128, three at 64: one round, no tail of late workgroups); the
+  // dequantise kernel (latency-bound, small footprint): eight.  Never more
+  // than the largest unit count.
   const long max_units = long(cap) * pv.Hkv * (pv.W / 32);
-  long gx = ((promote ? 8L : 3L) * pv.cus + pv.B - 1) / pv.B;
+  long gx = ((promote ? 8L : (pv.D == 128 ? 4L : 3L)) * pv.cus + pv.B - 1) / pv.B;
   if (gx > max_units) gx = max_units;
   if (gx < 1) gx = 1;
   const int wi = pv.lbits == 2 ? 0 : (pv.lbits == 4 ? 1 : 2);
