@@ -68,7 +68,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGMax = 8;     // query heads per kv head supported
 constexpr int kMaxSplits = 64;
-constexpr int kMassWindows = 16;   // windows per mass block of the combine kernel
+constexpr int kMassWindows = 16;   // windows per mass block of the combine kernel, at most
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -1095,13 +1095,13 @@ __device__ inline float oct_reduce(float x, Op op) {
 
 
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, int acc_scores) {
+__global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, int acc_scores, int mass_lg) {
   constexpr int kSlice = 32, NO = D / kSlice;
   __shared__ float s_m[kMaxSplits * kGMax];
   __shared__ float s_hm[kGMax], s_hz[kGMax];
   __shared__ float4 s_acc[256];
   __shared__ int s_win[kMassWindows];
-  extern __shared__ float s_dynf[];   // mass blocks: M, 1/Z [Hq], masses [kMassWindows][Hq], appended [Hq]
+  extern __shared__ float s_dynf[];   // mass blocks: M, 1/Z [Hq], masses [mw][Hq], appended [Hq]
   const int b = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
   // Every kernel argument that either kind of block reads is fetched in one
   // batch here: left to itself, the compiler requests a branch's arguments
@@ -1218,17 +1218,18 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
 
   // ---------------------------------------------------------- window masses
   if (!mass_p && !acc_scores) return;
-  const int w0 = (x - Hkv * NO) * kMassWindows;
+  const int mw = 1 << mass_lg;   // windows per mass block: 8 or 16
+  const int w0 = (x - Hkv * NO) * mw;
   if (w0 >= maxw) return;
   float* s_M = s_dynf;             // [Hq]
   float* s_Zh = s_dynf + Hq;       // [Hq] 1 / normaliser
-  float* s_mv = s_dynf + 2 * Hq;   // [kMassWindows][Hq]
-  float2* s_app = reinterpret_cast<float2*>(s_dynf + (2 + kMassWindows) * Hq);   // [Hq]
+  float* s_mv = s_dynf + 2 * Hq;   // [mw][Hq]
+  float2* s_app = reinterpret_cast<float2*>(s_dynf + (2 + mw) * Hq);   // [Hq]
   // thread pairs (head h, window wl), heads fastest: pair p = tid + 256 i has
   // h = p % Hq, wl = p / Hq, and the records of one tile of all heads are
   // contiguous
   constexpr int kPairs = 4, kTiles = 8;   // pairs per batch; tiles per window at most
-  const int npairs = Hq * kMassWindows;
+  const int npairs = Hq * mw;
   const int bpairs = min(kPairs, (npairs + 255) / 256);   // pairs of a thread in one batch
   const auto rtm = tile_rsrc(tm_p + size_t(b) * maxw * TPW * Hq, maxw * TPW * Hq * 8);
   const auto rml = tile_rsrc(ml_p + size_t(b) * Hq * S, Hq * S * 8);
@@ -1255,8 +1256,8 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   const uint32_t i4 = load4(rinfo, 16);
   float2 t1[kPairs][kTiles];
   tile_masses(0, t1);
-  const int wt = w0 + tid;   // thread tid < kMassWindows: its window's page entry and score
-  const bool tw = tid < kMassWindows && wt < maxw;
+  const int wt = w0 + tid;   // thread tid < mw: its window's page entry and score
+  const bool tw = tid < mw && wt < maxw;
   const uint32_t pe = load4(rpg, boff(tw, wt * 4));
   const float s_old = __uint_as_float(load4(rsc, boff(acc_scores && tw, wt * 4)));
   const auto rap = tile_rsrc(am_p + size_t(b) * Hq, Hq * 8);
@@ -1293,13 +1294,13 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   const int app = uniform(int(inf4.x)), len_old = uniform(int(i4));
   const int len = len_old + (app ? 1 : 0);
   const int n_old = windows_of(len_old, W), n_win = windows_of(len, W);
-  const bool tin = tid < kMassWindows && wt < n_win;
+  const bool tin = tid < mw && wt < n_win;
   if (app) {
     if (tid < Hq) s_app[tid] = appm;
     for (int h = tid + 256; h < Hq; h += 256) s_app[h] = as_f2(load8(rap, h * 8));
   }
   // liveness and valid tiles of the block's windows
-  if (tid < kMassWindows) {
+  if (tid < mw) {
     bool live = false;
     int vt = 0;
     if (tin) {
@@ -1343,10 +1344,10 @@ __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, i
   // wait for their completion (an empty asm statement that reads the register)
   asm volatile("" ::"v"(s_old));
   __syncthreads();
-  // masses out in window order (16 consecutive windows per head)
+  // masses out in window order (the block's mw consecutive windows per head)
   if (mass_p) {
     for (int idx = tid; idx < npairs; idx += 256) {
-      const int h = idx / kMassWindows, ww = idx % kMassWindows;
+      const int h = idx >> mass_lg, ww = idx & (mw - 1);
       if (w0 + ww < n_win) mass_p[(size_t(b) * Hq + h) * maxw + w0 + ww] = s_mv[ww * Hq + h];
     }
   }
@@ -1382,9 +1383,16 @@ static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream
   else
     e = pv.G <= 4 ? launch_attn_kernel<D, 4, 8>(pv, a, shm, s) : launch_attn_kernel<D, 8, 8>(pv, a, shm, s);
   if (e != hipSuccess) return e;
-  const int mass_blocks = (a.mass || a.acc_scores) ? (pv.maxw + kMassWindows - 1) / kMassWindows : 0;
+  // Mass blocks of 16 windows; of 8 when that makes at most 64 blocks in all
+  // (a short launch, where more blocks with half the pairs each end sooner:
+  // 32K step 18.2 -> 17.8 us; with more blocks the redundant per-block head
+  // reductions cost more than they save).
+  const int mb16 = (pv.maxw + kMassWindows - 1) / kMassWindows;
+  const int mass_lg = pv.B * mb16 <= 64 ? 3 : 4;
+  const int mw = 1 << mass_lg;
+  const int mass_blocks = (a.mass || a.acc_scores) ? (pv.maxw + mw - 1) / mw : 0;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(pv.Hkv * (D / 32) + mass_blocks, pv.B), dim3(256),
-                     size_t(4 + kMassWindows) * pv.Hq * 4, s, pv, a, a.acc_scores);
+                     size_t(4 + mw) * pv.Hq * 4, s, pv, a, a.acc_scores, mass_lg);
   return hipGetLastError();
 }
 
