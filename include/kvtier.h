@@ -110,7 +110,7 @@ typedef struct {
  *                    bits 17-31 ledger slot.
  *  KV_REGION_SCORES  float [segment][max_windows] cumulative scores.
  *  KV_REGION_TOKENS  int32 [segment] tokens cached.
- *  KV_REGION_WORK    library scratch (transition work lists, counters).
+ *  KV_REGION_WORK    library scratch (transition work lists and their item counts).
  *  KV_REGION_ERR     int32 device error word. */
 enum {
   KV_REGION_BF16 = 0, KV_REGION_LEDGER = 1, KV_REGION_PAGES = 2, KV_REGION_SCORES = 3,
