@@ -1094,9 +1094,12 @@ __device__ inline float oct_reduce(float x, Op op) {
 
 
 
-template <int D>
+// SL: channels of one output block (32, or the whole head when the splits
+// are few: a thread then reduces at most kMaxSplits / 4 = 16 splits of its
+// item, which covers them).
+template <int D, int SL>
 __global__ __launch_bounds__(256) void combine_kernel(PoolView pv, AttnArgs a, int acc_scores, int mass_lg) {
-  constexpr int kSlice = 32, NO = D / kSlice;
+  constexpr int kSlice = SL, NO = D / kSlice;
   __shared__ float s_m[kMaxSplits * kGMax];
   __shared__ float s_hm[kGMax], s_hz[kGMax];
   __shared__ float4 s_acc[256];
@@ -1391,8 +1394,17 @@ static hipError_t launch_attn_t(const PoolView& pv, const AttnArgs& a, hipStream
   const int mass_lg = pv.B * mb16 <= 64 ? 3 : 4;
   const int mw = 1 << mass_lg;
   const int mass_blocks = (a.mass || a.acc_scores) ? (pv.maxw + mw - 1) / mw : 0;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(pv.Hkv * (D / 32) + mass_blocks, pv.B), dim3(256),
-                     size_t(4 + mw) * pv.Hq * 4, s, pv, a, a.acc_scores, mass_lg);
+  // Output blocks: one per kv head when there are at most 8 splits (the
+  // Mistral-7B step, 2 splits: the combine 8.5 -> 6.1 us; at 16 splits the
+  // Qwen2.5-7B step gained nothing), else one per 32-channel slice, so a
+  // thread's share of a many-split reduction stays short.
+  const size_t cshm = size_t(4 + mw) * pv.Hq * 4;
+  if (a.splits <= 8)
+    hipLaunchKernelGGL((combine_kernel<D, D>), dim3(pv.Hkv + mass_blocks, pv.B), dim3(256), cshm, s, pv, a,
+                       a.acc_scores, mass_lg);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, 32>), dim3(pv.Hkv * (D / 32) + mass_blocks, pv.B), dim3(256), cshm, s,
+                       pv, a, a.acc_scores, mass_lg);
   return hipGetLastError();
 }
 
