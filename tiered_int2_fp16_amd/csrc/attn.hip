@@ -827,19 +827,21 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     }
   };
   // Both tiers in one loop: a wave with a long INT2 list and some bf16 tiles
-  // takes one bf16 tile after every eight INT2 tiles, so that the bf16 bytes
+  // takes one bf16 tile after every K INT2 tiles, so that the bf16 bytes
   // stream in while INT2 tiles are decoded (an INT2 tile costs far more
   // instructions per byte than a bf16 tile); the bf16 tiles left over run in
   // the bf16 loop after it.  A wave's loads complete in the order they were
   // issued, so an INT2 tile requested behind a bf16 tile's 16 KB waits for
-  // all of it: one bf16 tile per eight INT2 tiles was measured faster than
-  // one per four, six, twelve or sixteen (128K loop and Mistral step).  Two
+  // all of it: K = 8 was measured fastest at the 128K loop (against 4, 6, 12
+  // and 16), K = 4 at the Mistral step, whose shares hold fewer INT2 tiles
+  // per bf16 tile.  Two
   // INT2 tiles and one bf16 tile are in flight; every load is unconditional
   // (empty resources past the ends), so each tile waits only for its own
   // loads.  INT2 tiles record their masses from the top rows of the record
   // block, bf16 tiles from the bottom (both lists fit one chunk).
   int f_done = 0;   // bf16 tiles of the first chunk taken in the mixed loop
-  auto mixed_tiles = [&]() {
+  auto mixed_tiles = [&](auto group) {
+    constexpr int K = decltype(group)::value;   // INT2 tiles per bf16 tile
     const int nq = q_end - q_beg, nf = f_end - f_beg;
     QB A, Bq;
     load_q(A, 0, nq);
@@ -849,35 +851,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
     load_f(FA, 0, nf);
     __builtin_amdgcn_sched_barrier(0);
     make_q4();
-    // whole groups of eight (the tiles past the end load nothing and are not
+    // whole groups of K (the tiles past the end load nothing and are not
     // computed): the loop has no early exit, so every path into its head has
     // the same loads in flight in the same order
     int jf = 0;
-    for (int i = 0; i < nq; i += 8) {
-      compute_q(A, i, kList - 1 - i);
-      load_q(A, i + 2, nq);
+    auto slot = [&](QB& qq, int i, int k) {
+      if (k == 0 || i + k < nq) compute_q(qq, i + k, kList - 1 - k - i);
+      load_q(qq, i + k + 2, nq);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < nq) compute_q(Bq, i + 1, kList - 2 - i);
-      load_q(Bq, i + 3, nq);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 2 < nq) compute_q(A, i + 2, kList - 3 - i);
-      load_q(A, i + 4, nq);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 3 < nq) compute_q(Bq, i + 3, kList - 4 - i);
-      load_q(Bq, i + 5, nq);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 4 < nq) compute_q(A, i + 4, kList - 5 - i);
-      load_q(A, i + 6, nq);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 5 < nq) compute_q(Bq, i + 5, kList - 6 - i);
-      load_q(Bq, i + 7, nq);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 6 < nq) compute_q(A, i + 6, kList - 7 - i);
-      load_q(A, i + 8, nq);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 7 < nq) compute_q(Bq, i + 7, kList - 8 - i);
-      load_q(Bq, i + 9, nq);
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int i = 0; i < nq; i += K) {
+      slot(A, i, 0);
+      slot(Bq, i, 1);
+      slot(A, i, 2);
+      slot(Bq, i, 3);
+      if constexpr (K == 8) {
+        slot(A, i, 4);
+        slot(Bq, i, 5);
+        slot(A, i, 6);
+        slot(Bq, i, 7);
+      }
       if (jf < nf) compute_f(FA, jf);
       ++jf;
       load_f(FA, jf, nf);   // (empty past the end)
@@ -924,7 +917,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   if constexpr (GP == 4 && BITS == 2) {
     const int nq_all = q_end - q_beg, nf_all = f_end - f_beg;
     mixed = !short_share && nq_all >= kMixedList && nq_all + nf_all <= kList;
-    if (mixed) mixed_tiles();
+    // one bf16 tile per eight INT2 tiles for INT2-heavy shares (the 128K loop,
+    // about five INT2 tiles per bf16 tile), per four otherwise (the Mistral
+    // step, about three: attention 48.3 -> 45.6 us by kernel trace)
+    if (mixed) {
+      if (nq_all > 4 * nf_all)
+        mixed_tiles(std::integral_constant<int, 8>{});
+      else
+        mixed_tiles(std::integral_constant<int, 4>{});
+    }
   }
   if (!mixed && !short_share) {
     if (f_beg < f_end && kEarlyF)
