@@ -748,10 +748,12 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   if (cap <= 0) return hipSuccess;
   // the quantise kernel: its occupancy in workgroups per compute unit (four
   // at head_dim 128, three at 64: one round, no tail of late workgroups); the
-  // dequantise kernel (latency-bound, small footprint): eight.  Never more
-  // than the largest unit count.
+  // dequantise kernel: four, so each workgroup takes several units and its
+  // prefetch of the next unit pays (measured at the Mistral-7B step against
+  // two, three, six and eight: eight, two units each, needed a second round
+  // at its 78 VGPRs).  Never more than the largest unit count.
   const long max_units = long(cap) * pv.Hkv * (pv.W / 32);
-  long gx = ((promote ? 8L : (pv.D == 128 ? 4L : 3L)) * pv.cus + pv.B - 1) / pv.B;
+  long gx = ((promote ? 4L : (pv.D == 128 ? 4L : 3L)) * pv.cus + pv.B - 1) / pv.B;
   if (gx > max_units) gx = max_units;
   if (gx < 1) gx = 1;
   const int wi = pv.lbits == 2 ? 0 : (pv.lbits == 4 ? 1 : 2);
