@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolVie
     //    and l ^ 32 hold the two halves; after one exchange lane l finishes
     //    the pair's first group and lane l ^ 32 its second.
     if (has_group) {
-      const bool is_v = tid >= D;
+      const bool is_v = __builtin_amdgcn_readfirstlane(int(tid >= D)) != 0;   // (whole waves: scalar branches)
       const int idx = is_v ? tid - D : tid, l = idx & 63, h = l >> 5;
       const int p = (idx >> 6) * 32 + (l & 31);   // the pair, 0 .. D/2 - 1
       uint32_t x[16];
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolVie
       int lane[2], w[2];
       const int x = pair_of(i, lane, w);
       if (NW < 256 && x >= NW) break;   // (head_dim 64, INT2: waves 2 and 3 have no pair)
-      const bool is_v = x >= NW / 2;
+      const bool is_v = __builtin_amdgcn_readfirstlane(int(x >= NW / 2)) != 0;   // (whole waves)
       uint32_t word[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < NCW; ++j) {
@@ -586,19 +586,18 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolVie
 // Promote data kernel: bf16_rne(fmaf(c, s, m)) for every value of one tile.
 // A ledger chunk (lane, cmb) and the bf16 chunk (cmb, lane) hold the same 8
 // values, so each thread turns one chunk's codes (one or two code words) into
-// one 16-byte chunk per step; the tile's scale block (Ks | Km | Vs | Vm, 8 D
-// bytes) is staged in LDS.  The next unit's code words and scale block are
-// loaded into registers while the current unit is decoded (alternate units
-// use alternate LDS blocks, one barrier per unit); a unit's chunks are stored
-// at the start of the next unit, just before the following loads.  The float32 results are
-// never subnormal (c s + m is 0 or at least 2^-24 in magnitude: every term is
-// a multiple of the fp16 quantum 2^-24), and the hardware's packed bf16
-// conversion rounds them to nearest even.
+// one 16-byte chunk; the tile's scale block (Ks | Km | Vs | Vm, 8 D bytes) is
+// staged in LDS.  A workgroup loads the code words and scale blocks of a
+// batch of four units at once, then decodes and stores them one after the
+// other.  The float32 results are never subnormal (c s + m is 0 or at least
+// 2^-24 in magnitude: every term is a multiple of the fp16 quantum 2^-24),
+// and the hardware's packed bf16 conversion rounds them to nearest even.
 template <int D, int BITS>
 __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, const WorkItem* __restrict__ items) {
   constexpr int NCH = 8 * D / 256;   // 16-byte chunks per thread (K chunks first, then V)
   constexpr int NWC = BITS == 8 ? 2 : 1;   // code words per chunk
-  __shared__ uint4 s_sc[2][D / 2];
+  constexpr int NBU = 4;             // units whose loads go out together (a batch)
+  __shared__ uint4 s_sc[NBU][D / 2];
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int b = blockIdx.y, tid = threadIdx.x, W = pv.W, TPW = W / 32;
@@ -608,7 +607,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, co
   const WorkItem* work = items + size_t(b) * pv.maxw;   // (not written here: scalar loads)
   const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
   const int per_item = pv.Hkv * TPW;
-  auto item_of = [&](int u) { return u < units ? work[u / per_item] : WorkItem{0, 0, 0, 0}; };
   // the unit's code words (NWC per chunk) and, for tid < D/2, 16-byte piece
   // tid of its scale block; a unit that moves nothing loads nothing
   auto fetch = [&](int u, const WorkItem& it, uint32_t (&cw)[NCH][NWC], uint4& scp) {
@@ -631,107 +629,77 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, co
     scp = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                         rs, int(LT.ks + 16 * (tid < D / 2 ? tid : 0)), 0, 0));
   };
-  // a unit's bf16 chunks are stored at the start of the next unit, just
-  // before that unit's successor is loaded (so loads never wait behind fresh
-  // stores); alternate units decode into alternate register sets, so a set's
-  // stores have a whole unit to read their data before it is overwritten.
-  // pend: the tile of a set's chunks (null: none)
-  uint16_t* pend[2] = {nullptr, nullptr};
-  uint4 pout[2][NCH];
-  auto flush = [&](int k) {
-    if (!pend[k]) return;   // (the same for the whole workgroup)
+  // Batches of NBU units (u0, u0 + gridDim.x, ...): every load of a batch goes
+  // out before its first store, so no wait for a unit's data also waits for
+  // stores (a wave's memory counter is in order); each unit's 16 KB of bf16
+  // is stored as soon as it is decoded.
+  for (int u0 = blockIdx.x; u0 < units; u0 += NBU * gridDim.x) {
+    WorkItem its[NBU];
+    uint32_t cw[NBU][NCH][NWC];
+    uint4 scp[NBU];
+    // every item of the batch first (no branch: a unit past the list takes
+    // the last item's entry with its flag cleared), then every load
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + 256 * j;
-      const bool is_v = 256 * j >= 4 * D;
-      reinterpret_cast<uint4*>(pend[k] + (is_v ? 32 * D : 0))[is_v ? c - 4 * D : c] = pout[k][j];
+    for (int k = 0; k < NBU; ++k) {
+      const int u = u0 + k * gridDim.x;
+      its[k] = work[min(u, units - 1) / per_item];
+      if (u >= units) its[k].flag = 0;
     }
-    pend[k] = nullptr;
-  };
-  int u = blockIdx.x;
-  WorkItem it = item_of(u);
-  uint32_t cw[NCH][NWC];
-  uint4 nsc;
-  fetch(u, it, cw, nsc);
-  int par = 0;
-  // one unit, decoded into register set k
-  auto step = [&](int k) {
-    const WorkItem itn = item_of(u + gridDim.x);
-    const bool move = it.flag == 1;   // (the same for the whole workgroup)
-    if (move && tid < D / 2) s_sc[par][tid] = nsc;
-    const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
-    uint16_t* tb = pv.block(seg, it.dst, kvh) + size_t(tile) * 64 * D;
-    // this unit's loads are waited for here, before the stores below: the
-    // memory counter is in order, and a wait placed after them would also
-    // wait for the stores
-    uint32_t ccw[NCH][NWC];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
+    for (int k = 0; k < NBU; ++k) fetch(u0 + k * gridDim.x, its[k], cw[k], scp[k]);
+    if (u0 != blockIdx.x) __syncthreads();   // the previous batch's scale reads are done
+    if (tid < D / 2) {
 #pragma unroll
-      for (int q = 0; q < NWC; ++q) {
-        ccw[j][q] = cw[j][q];
-        asm volatile("" ::"v"(ccw[j][q]));
-      }
-    asm volatile("" ::"v"(nsc.x), "v"(nsc.y), "v"(nsc.z), "v"(nsc.w));
-    flush(k ^ 1);
-    fetch(u + gridDim.x, itn, cw, nsc);   // the next unit's bytes, in flight during this one
-    it = itn;
-    if (!move) return;
+      for (int k = 0; k < NBU; ++k) s_sc[k][tid] = scp[k];
+    }
     __syncthreads();
-    const _Float16* ks = reinterpret_cast<const _Float16*>(s_sc[par]);
-    const _Float16* km = ks + D;
-    const _Float16* vs = ks + 2 * D;
-    const _Float16* vm = ks + 3 * D;
-    par ^= 1;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = tid + 256 * j;
-      const bool is_v = 256 * j >= 4 * D;
-      const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
-      // the chunk's 8 scales and mins: K channels d0 .. d0 + 7, or V tokens
-      // t0 .. t0 + 7 of channel block d0 / 32
-      int t0, d0;
-      if (is_v) layout::v_chunk_elem(cmb, lane, 0, &t0, &d0);
-      else layout::k_chunk_elem(cmb, lane, 0, D, &t0, &d0);
-      const int pb = is_v ? (d0 >> 5) * 32 + t0 : d0;
-      const uint4 s8 = *reinterpret_cast<const uint4*>(is_v ? vs + pb : ks + pb);
-      const uint4 m8 = *reinterpret_cast<const uint4*>(is_v ? vm + pb : km + pb);
-      const uint32_t sw[4] = {s8.x, s8.y, s8.z, s8.w}, mw[4] = {m8.x, m8.y, m8.z, m8.w};
-      uint32_t out[4];
+    for (int k = 0; k < NBU; ++k) {
+      const WorkItem& it = its[k];
+      if (it.flag != 1) continue;   // (the same for the whole workgroup)
+      const int u = u0 + k * gridDim.x;
+      const int r = u % per_item, kvh = r / TPW, tile = r % TPW;
+      uint16_t* tb = pv.block(seg, it.dst, kvh) + size_t(tile) * 64 * D;
+      const _Float16* ks = reinterpret_cast<const _Float16*>(s_sc[k]);
+      const _Float16* km = ks + D;
+      const _Float16* vs = ks + 2 * D;
+      const _Float16* vm = ks + 3 * D;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        f32x2 f;
+      for (int j = 0; j < NCH; ++j) {
+        const int c = tid + 256 * j;
+        const bool is_v = 256 * j >= 4 * D;
+        const int cc = is_v ? c - 4 * D : c, cmb = cc >> 6, lane = cc & 63;
+        // the chunk's 8 scales and mins: K channels d0 .. d0 + 7, or V tokens
+        // t0 .. t0 + 7 of channel block d0 / 32
+        int t0, d0;
+        if (is_v) layout::v_chunk_elem(cmb, lane, 0, &t0, &d0);
+        else layout::k_chunk_elem(cmb, lane, 0, D, &t0, &d0);
+        const int pb = is_v ? (d0 >> 5) * 32 + t0 : d0;
+        const uint4 s8 = *reinterpret_cast<const uint4*>(is_v ? vs + pb : ks + pb);
+        const uint4 m8 = *reinterpret_cast<const uint4*>(is_v ? vm + pb : km + pb);
+        const uint32_t sw[4] = {s8.x, s8.y, s8.z, s8.w}, mw[4] = {m8.x, m8.y, m8.z, m8.w};
+        uint32_t out[4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * e2 + h;
-          int wb, bit;
-          layout::code_pos(cmb, lane, e, D, BITS, &wb, &bit);
-          const uint32_t word = (BITS == 8 && e >= 4) ? ccw[j][NWC - 1] : ccw[j][0];
-          const float code = float((word >> bit) & kMask);
-          const float sc = float(__builtin_bit_cast(_Float16, uint16_t(sw[e2] >> (16 * h))));
-          const float mn = float(__builtin_bit_cast(_Float16, uint16_t(mw[e2] >> (16 * h))));
-          f[h] = __builtin_fmaf(code, sc, mn);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          f32x2 f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int e = 2 * e2 + h;
+            int wb, bit;
+            layout::code_pos(cmb, lane, e, D, BITS, &wb, &bit);
+            const uint32_t word = (BITS == 8 && e >= 4) ? cw[k][j][NWC - 1] : cw[k][j][0];
+            const float code = float((word >> bit) & kMask);
+            const float sc = float(__builtin_bit_cast(_Float16, uint16_t(sw[e2] >> (16 * h))));
+            const float mn = float(__builtin_bit_cast(_Float16, uint16_t(mw[e2] >> (16 * h))));
+            f[h] = __builtin_fmaf(code, sc, mn);
+          }
+          out[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
         }
-        out[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+        reinterpret_cast<uint4*>(tb + (is_v ? 32 * D : 0))[is_v ? c - 4 * D : c] =
+            make_uint4(out[0], out[1], out[2], out[3]);
       }
-      pout[k][j] = make_uint4(out[0], out[1], out[2], out[3]);
     }
-    pend[k] = tb;
-    // the other set was stored at the top of this unit: keep its registers
-    // (the stores' data) out of the decode's temporaries
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) asm volatile("" ::"v"(pout[k ^ 1][j].x), "v"(pout[k ^ 1][j].y),
-                                               "v"(pout[k ^ 1][j].z), "v"(pout[k ^ 1][j].w));
-  };
-  while (u < units) {
-    step(0);
-    u += gridDim.x;
-    if (u >= units) break;
-    step(1);
-    u += gridDim.x;
   }
-  flush(0);
-  flush(1);
 }
 
 static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t* items, int stride,
@@ -748,10 +716,11 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   if (cap <= 0) return hipSuccess;
   // the quantise kernel: its occupancy in workgroups per compute unit (four
   // at head_dim 128, three at 64: one round, no tail of late workgroups); the
-  // dequantise kernel: four, so each workgroup takes several units and its
-  // prefetch of the next unit pays (measured at the Mistral-7B step against
-  // two, three, six and eight: eight, two units each, needed a second round
-  // at its 78 VGPRs).  Never more than the largest unit count.
+  // dequantise kernel: four, each taking its units in batches of four (at
+  // the Mistral-7B step, 4096 units, one batch per workgroup; measured
+  // against two units per batch at eight workgroups per CU, and four or eight
+  // units per batch at four or eight per CU).  Never more than the largest
+  // unit count.
   const long max_units = long(cap) * pv.Hkv * (pv.W / 32);
   long gx = ((promote ? 4L : (pv.D == 128 ? 4L : 3L)) * pv.cus + pv.B - 1) / pv.B;
   if (gx > max_units) gx = max_units;
