@@ -489,8 +489,7 @@ def full_step_workload(c, B, torch, dev, steps, warmup, bits=2):
     def step():
         restore()
         for layer in range(c.layers):
-            pool.demote(layer, dem_l[layer], cnt_d)
-            pool.promote(layer, pro_l[layer], cnt_p)
+            pool.transitions(layer, dem_l[layer], cnt_d, pro_l[layer], cnt_p)   # one plan launch for both
             pool.attn(layer, Q_l[layer], out=out, mass=mass, scores=True)
 
     for _ in range(warmup):
@@ -510,8 +509,19 @@ def full_step_workload(c, B, torch, dev, steps, warmup, bits=2):
     torch.cuda.synchronize()
     t_timed = time.perf_counter() - t0
     assert pool.check() == 0
-    # the parts of one layer's step, eagerly with stream events (one more step)
+    # the parts of one layer's step, eagerly with stream events (two more
+    # steps: the moves as one call, then as a demote and a promote call)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * c.layers)]
+    restore()
+    for layer in range(c.layers):
+        ev[4 * layer].record()
+        pool.transitions(layer, dem_l[layer], cnt_d, pro_l[layer], cnt_p)
+        ev[4 * layer + 1].record()
+        pool.attn(layer, Q_l[layer], out=out, mass=mass, scores=True)
+        ev[4 * layer + 2].record()
+    torch.cuda.synchronize()
+    part = lambda k: float(np.mean([ev[4 * l + k].elapsed_time(ev[4 * l + k + 1]) for l in range(c.layers)])) * 1e3
+    mov_us, att_us = part(0), part(1)
     restore()
     for layer in range(c.layers):
         ev[4 * layer].record()
@@ -522,8 +532,8 @@ def full_step_workload(c, B, torch, dev, steps, warmup, bits=2):
         pool.attn(layer, Q_l[layer], out=out, mass=mass, scores=True)
         ev[4 * layer + 3].record()
     torch.cuda.synchronize()
-    part = lambda k: float(np.mean([ev[4 * l + k].elapsed_time(ev[4 * l + k + 1]) for l in range(c.layers)])) * 1e3
-    dem_us, pro_us, att_us = part(0), part(1), part(2)
+    assert pool.check() == 0
+    dem_us, pro_us = part(0), part(1)
     n_f, n_q = 12 - c.demote_per_seg + c.promote_per_seg, 21 + c.demote_per_seg - c.promote_per_seg
     lay = type("lay", (), {})()
     for f in ("window", "head_dim", "kv_heads", "q_heads", "batch"):
@@ -538,9 +548,10 @@ def full_step_workload(c, B, torch, dev, steps, warmup, bits=2):
     res = {"value": round(value, 2), "unit": "GB/s", "steps": steps, "warmup": warmup,
            "ms_per_step": round(1e3 * t_timed / steps, 4), "full_steps_per_s": round(steps / t_timed, 2),
            "bytes_per_step": per_step, "percent_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-           "per_layer_us": {"demote": round(dem_us, 2), "promote": round(pro_us, 2), "decode_step": round(att_us, 2)},
-           "per_layer_bytes": {"demote": d_b, "promote": p_b, "decode_step": a_b},
-           "roofline": pk(a_b, att_us),
+           "per_layer_us": {"transitions": round(mov_us, 2), "decode_step": round(att_us, 2),
+                            "demote": round(dem_us, 2), "promote": round(pro_us, 2)},
+           "per_layer_bytes": {"transitions": d_b + p_b, "decode_step": a_b, "demote": d_b, "promote": p_b},
+           "roofline": pk(a_b, att_us), "roofline_transitions": pk(d_b + p_b, mov_us),
            "roofline_demote": pk(d_b, dem_us), "roofline_promote": pk(p_b, pro_us),
            "tiers_after_moves": {"bf16": n_f, "ledger": n_q, "evicted": n - n_f - n_q}}
     del g, pool

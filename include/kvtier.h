@@ -194,6 +194,19 @@ kv_status kv_demote_quantize(kv_pool* pool, int32_t layer, const int32_t* items,
 kv_status kv_promote_dequantize(kv_pool* pool, int32_t layer, const int32_t* items,
                                 int32_t stride, const int32_t* counts, void* stream);
 
+/* A routing event's moves in one call ("Kernmechanismen": demotion,
+ * promotion, window-level routing): exactly
+ * kv_demote_quantize(demote lists) followed by kv_promote_dequantize(promote
+ * lists) on the same stream - the same pages, ledger entries, bf16 slots and
+ * error bits - with one plan launch for both lists instead of two.  The
+ * lists have the format of those calls (kv_score_route writes such a pair).
+ * KV_EINVAL for NULL lists or counts, a stride < 1 or a pool without ledger
+ * slots. */
+kv_status kv_apply_transitions(kv_pool* pool, int32_t layer, const int32_t* demote_items,
+                               int32_t demote_stride, const int32_t* demote_counts,
+                               const int32_t* promote_items, int32_t promote_stride,
+                               const int32_t* promote_counts, void* stream);
+
 /* Workspace bytes kv_tiered_decode_attn needs for this pool. [host] */
 size_t kv_attn_workspace_bytes(const kv_pool* pool);
 

@@ -260,8 +260,8 @@ def test_mistral_full_step_sampled():
             pro[b, : len(top)] = sorted(top)
         cnt_d = np.full(c.batch, c.demote_per_seg, np.int32)
         cnt_p = np.full(c.batch, c.promote_per_seg, np.int32)
-        p.pool.demote(layer, dev(dem), dev(cnt_d))
-        p.pool.promote(layer, dev(pro), dev(cnt_p))
+        # both lists in one call, as the bench's step makes them (one plan launch)
+        p.pool.transitions(layer, dev(dem), dev(cnt_d), dev(pro), dev(cnt_p))
         for b in p.seqs:
             seg = p.oracle[(layer, b)]
             for w in dem[b][: c.demote_per_seg]:

@@ -57,10 +57,10 @@ def _walk(tier, has_ledger, items, n, promote, free_slots):
     return tier, errs, moved
 
 
-def _pool(n, ledger_slots, bf16_slots, rng):
+def _pool(n, ledger_slots, bf16_slots, rng, bits=2):
     from tiered_int2_fp16_amd import binding as B
     W, D = 32, 64
-    cfg = B.make_config(1, 1, 1, 1, D, W, n, 1, bf16_slots, ledger_slots, 2)
+    cfg = B.make_config(1, 1, 1, 1, D, W, n, 1, bf16_slots, ledger_slots, bits)
     pool = B.Pool(cfg)
     kv = rng.standard_normal((2, n * W, D)).astype(np.float32)
     bits = (kv.view(np.uint32) >> 16).astype(np.uint16)
@@ -110,3 +110,59 @@ def test_plan_repeats_bad_items_and_exhaustion(n, ledger_slots, extra):
         assert np.array_equal(got[0], wk) and np.array_equal(got[1], wv), w
     log(f"{n} windows: {len(dem)} demote items ({len(moved)} moved, errors {want_err:#x}), "
         f"{len(pro)} promote items ({len(moved2)} moved, errors {want_err2:#x})")
+
+
+@pytest.mark.parametrize("n,ledger_slots,bf16_slots,bits", [(16, 3, 12, 2), (512, 280, 400, 2), (64, 40, 48, 4)])
+def test_one_launch_for_both_lists_matches_two_calls(n, ledger_slots, bf16_slots, bits):
+    """kv_apply_transitions against kv_demote_quantize then kv_promote_dequantize
+    on twin pools: the same rows, error bits, ledger entries and bf16 windows.
+    The promote list names windows the demote list moves in the same call (so
+    a promotion reads the entry the quantise kernel has just written and may
+    take the bf16 slot a demotion has just freed), older ledger windows,
+    repeats, wrong-tier and out-of-range items, and more windows than slots."""
+    rng = np.random.default_rng(1000 + n)
+    n_live = min(n, bf16_slots)          # prefill puts window w in bf16 slot w
+    pools = []
+    for _ in range(2):
+        pool, bits_kv = _pool(n_live, ledger_slots, bf16_slots, np.random.default_rng(7 + n), bits)
+        pools.append(pool)
+    n = n_live
+    # a first demotion so that some windows already have ledger entries
+    first = rng.permutation(n - 1)[: n // 4].tolist()
+    for pool in pools:
+        pool.demote(0, dev(np.array([first], np.int32)), dev(np.array([len(first)], np.int32)))
+    tier0, led0 = _state(pools[0], n)
+    assert pools[0].check() == pools[1].check()
+    f_now = [w for w in range(n - 1) if tier0[w] == F]
+    q_now = [w for w in range(n) if tier0[w] == Q]
+    dem = rng.permutation(f_now)[: max(1, 2 * len(f_now) // 3)].tolist()
+    dem = dem + dem[:2] + [n + 1, -3] + q_now[:1]
+    pro = dem[:3] + q_now[:5] + q_now[:1] + [n + 9] + rng.permutation(q_now)[5:].tolist() + dem[3:]
+    d_items, d_cnt = dev(np.array([dem], np.int32)), dev(np.array([len(dem)], np.int32))
+    p_items, p_cnt = dev(np.array([pro], np.int32)), dev(np.array([len(pro)], np.int32))
+    pools[0].demote(0, d_items, d_cnt)
+    pools[0].promote(0, p_items, p_cnt)
+    pools[1].transitions(0, d_items, d_cnt, p_items, p_cnt)
+    rows = [p.pages(0).cpu().numpy().copy() for p in pools]
+    assert np.array_equal(rows[0], rows[1])
+    errs = [p.check() for p in pools]
+    assert errs[0] == errs[1]
+    tier, led = _state(pools[0], n)
+    # and both against the lists taken in order
+    t1, e1, moved_d = _walk(tier0, led0, dem, n, False, ledger_slots - sum(led0))
+    led1 = [led0[w] or w in moved_d for w in range(n)]
+    t2, e2, moved_p = _walk(t1, led1, pro, n, True, bf16_slots - sum(1 for t in t1 if t == F))
+    assert tier == t2 and errs[0] == e1 | e2
+    if n > 16:   # windows demoted and promoted back in the same call
+        assert set(moved_d) & set(moved_p)
+    for w in range(n):
+        if tier[w] != 0 and led[w]:
+            a = pools[0].read_ledger(0, 0, w).cpu().numpy()
+            b = pools[1].read_ledger(0, 0, w).cpu().numpy()
+            assert a.tobytes() == b.tobytes(), ("ledger", w)
+        if tier[w] == F:
+            a = pools[0].read_window(0, 0, w).cpu().numpy()
+            b = pools[1].read_window(0, 0, w).cpu().numpy()
+            assert a.tobytes() == b.tobytes(), ("bf16", w)
+    log(f"{n} windows, {bits}-bit ledger: {len(dem)} demote and {len(pro)} promote items in one call, "
+        f"errors {errs[0]:#x}, {sum(1 for t in tier if t == F)} bf16 / {sum(1 for t in tier if t == Q)} ledger after")

@@ -30,6 +30,7 @@ EXPORTS = [
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
     "kv_attn_profile", "kv_attn_timings", "kv_decode_step", "kv_route_diagnostics",
     "kv_prefill_scores_workspace_bytes", "kv_prefill_scores", "kv_decode_step_noalloc",
+    "kv_apply_transitions",
     "kv_stream_probe",
 ]
 
@@ -64,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "kv_prefill": (I32, [P, I32, P, P, I32, P, P]),
         "kv_demote_quantize": (I32, [P, I32, P, I32, P, P]),
         "kv_promote_dequantize": (I32, [P, I32, P, I32, P, P]),
+        "kv_apply_transitions": (I32, [P, I32, P, I32, P, P, I32, P, P]),
         "kv_attn_workspace_bytes": (SZ, [P]),
         "kv_tiered_decode_attn": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
@@ -162,6 +164,11 @@ def kv_demote_quantize(h, layer, items, counts, stream=None):
 
 def kv_promote_dequantize(h, layer, items, counts, stream=None):
     _ck(LIB.kv_promote_dequantize(h, layer, _ptr(items), items.shape[-1], _ptr(counts), _stream(stream)))
+
+
+def kv_apply_transitions(h, layer, d_items, d_counts, p_items, p_counts, stream=None):
+    _ck(LIB.kv_apply_transitions(h, layer, _ptr(d_items), d_items.shape[-1], _ptr(d_counts),
+                                 _ptr(p_items), p_items.shape[-1], _ptr(p_counts), _stream(stream)))
 
 
 def kv_attn_workspace_bytes(h) -> int:
@@ -317,6 +324,12 @@ class Pool:
         self._items(items, counts)
         kv_promote_dequantize(self.h, layer, items, counts)
 
+    def transitions(self, layer, d_items, d_counts, p_items, p_counts):
+        """kv_apply_transitions: the demotions, then the promotions, one plan launch."""
+        self._items(d_items, d_counts)
+        self._items(p_items, p_counts)
+        kv_apply_transitions(self.h, layer, d_items, d_counts, p_items, p_counts)
+
     def attn(self, layer, q, k_new=None, v_new=None, out=None, mass=None, want_mass=True, scores=False):
         """kv_tiered_decode_attn, or kv_decode_step when `scores` (fused score update)."""
         c = self.cfg
@@ -348,8 +361,7 @@ class Pool:
 
     def apply_route(self, layer, transitions, counts):
         """Demotions then promotions of a routing event, straight from device lists."""
-        self.demote(layer, transitions[0], counts[0])
-        self.promote(layer, transitions[1], counts[1])
+        self.transitions(layer, transitions[0], counts[0], transitions[1], counts[1])
 
     def diagnostics(self, layer, diag, counts=None, shadow_mass=None):
         """kv_route_diagnostics into diag float [batch][5] (churn, promotions,

@@ -14,6 +14,9 @@ hipError_t launch_demote(const PoolView& pv, int layer, const int32_t* items, in
                          const int32_t* counts, hipStream_t s);
 hipError_t launch_promote(const PoolView& pv, int layer, const int32_t* items, int stride,
                           const int32_t* counts, hipStream_t s);
+hipError_t launch_transitions(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
+                              const int32_t* d_counts, const int32_t* p_items, int p_stride,
+                              const int32_t* p_counts, hipStream_t s);
 hipError_t launch_read(const PoolView& pv, int layer, int b, int window, bool ledger, void* dst,
                        hipStream_t s);
 

@@ -10,7 +10,9 @@
 //
 // Each transition is two launches: a plan kernel (one workgroup per sequence)
 // validates the items in order, assigns the lowest free slot and rewrites the
-// page table; a data kernel then moves the bytes of every planned item.
+// page table; a data kernel then moves the bytes of every planned item.  A
+// routing event's demotions and promotions together take three: one plan
+// launch for both lists, then the two data kernels.
 #include "launch.h"
 #include "layout.h"
 
@@ -85,207 +87,229 @@ struct WorkItem {
   int w, src, dst, flag;  // flag 1: move bytes; 2: tier flip only; 0: invalid
 };
 
-// promote == false: demote plan (ledger slots); true: promote plan (bf16 slots).
-// One workgroup per sequence.  The page-table row, the free-slot bitmap and
-// the item list are staged in LDS.  The outcome is that of taking the items
-// one by one in list order, each valid item the lowest free slot, computed
-// for all items at once:
-//  - an item is checked against the pre-transition row; a window listed
-//    again after its first occurrence has the outcome of that occurrence's
-//    state: after a success it has moved (a state error), after a failure
-//    it fails the same way;
+// A plan's item list: items int32 [batch][stride] of window indices, counts
+// int32 [batch]; items == nullptr: no such list in this launch.
+struct PlanList {
+  const int32_t* items;
+  const int32_t* counts;
+  int stride;
+};
+
+// The demote plan (ledger slots), the promote plan (bf16 slots), or both in
+// one launch, the demotions first: the promote plan then starts from the row
+// the demote plan left, exactly as when the two are launched one after the
+// other.  One workgroup per sequence.  The page-table row and the item lists
+// are staged in LDS with one batch of loads; for each plan, the free-slot
+// bitmap too.  A plan's outcome is that of taking its items one by one in
+// list order, each valid item the lowest free slot, computed for all items
+// at once:
+//  - an item is checked against the row as the plan found it; a window
+//    listed again after its first occurrence has the outcome of that
+//    occurrence's state: after a success it has moved (a state error), after
+//    a failure it fails the same way;
 //  - the k-th item (in list order) that needs a slot takes the k-th free
 //    slot in ascending order, and every such item from the free count on
 //    finds none (no slot is freed during a plan).
-// Then the work list and the updated row are written back.
-__global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const int32_t* items, int stride,
-                                                   const int32_t* counts, int promote) {
+// Each plan writes its work list (list 0: demotions, list 1: promotions) and
+// item count; the updated row is written back at the end.
+__global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, PlanList dl, PlanList pl) {
   extern __shared__ uint32_t smem[];
   __shared__ int s_wsum[4];
   __shared__ int s_errs;
   const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int maxw = pv.maxw, W = pv.W;
-  const int nslots = promote ? pv.nb : pv.nl;
-  const int words = (nslots + 31) / 32;
-  const int cap = stride < maxw ? stride : maxw;
+  const int cap_d = dl.items ? min(dl.stride, maxw) : 0;
+  const int cap_p = pl.items ? min(pl.stride, maxw) : 0;
+  const int words_max = (max(dl.items ? pv.nl : 0, pl.items ? pv.nb : 0) + 31) / 32;
   uint32_t* pages = smem;                                             // [maxw]
-  uint32_t* freew = pages + maxw;                                     // [words] free slots
-  int32_t* fpc = reinterpret_cast<int32_t*>(freew + words);          // [words + 1] free slots before a word
-  // [cap] the items: their windows, then each item's outcome packed as
-  // window | flag << 12 | error kind << 14 | slot << 16 (flag 1: move bytes,
-  // 2: tier flip only; error kind 1: window out of range, 2: state, 3: no
-  // free slot)
-  int32_t* item_w = fpc + words + 1;
-  int32_t* first = item_w + cap;                                      // [maxw] first list position
+  int32_t* first = reinterpret_cast<int32_t*>(pages + maxw);         // [maxw] first list position
+  uint32_t* freew = reinterpret_cast<uint32_t*>(first + maxw);       // [words] free slots
+  int32_t* fpc = reinterpret_cast<int32_t*>(freew + words_max);      // [words + 1] free slots before a word
+  // [cap] each list's items: their windows, then each item's outcome packed
+  // as window | flag << 12 | error kind << 14 | slot << 16 (flag 1: move
+  // bytes, 2: tier flip only; error kind 1: window out of range, 2: state,
+  // 3: no free slot)
+  int32_t* item_d = fpc + words_max + 1;
+  int32_t* item_p = item_d + cap_d;
   const int len = pv.tokens[seg];
   const int n = windows_of(len, W);
+  const int cnt_d = dl.items ? dl.counts[b] : 0, cnt_p = pl.items ? pl.counts[b] : 0;
   uint32_t* gp = pv.pages + size_t(seg) * maxw;
-  int cnt = counts[b];
   if (tid == 0) s_errs = 0;
-  if (cnt < 0) cnt = 0;
-  if (cnt > cap) {
-    cnt = cap;
-    if (tid == 0) s_errs = KV_ERR_ITEM_RANGE;
-  }
-  // the row and the item list (its first cap entries: no wait for the
-  // count), eight loads per thread in flight at a time; buffer loads read
-  // zeros past the ends without touching memory
+  // the row and the item lists (their first cap entries: no wait for the
+  // counts), eight entries of each per thread in flight at a time; buffer
+  // loads read zeros past the ends without touching memory
   {
     const auto rp = __builtin_amdgcn_make_buffer_rsrc(gp, (short)0, maxw * 4, 0x00020000);
-    const auto ri = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(items + size_t(b) * stride), (short)0,
-                                                      cap * 4, 0x00020000);
-    for (int base = 0; base < maxw; base += 8 * 256) {   // (cap <= maxw)
-      uint32_t rw[8], ri8[8];
+    const auto rd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(dl.items ? dl.items + size_t(b) * dl.stride : nullptr), (short)0, cap_d * 4,
+        0x00020000);
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(pl.items ? pl.items + size_t(b) * pl.stride : nullptr), (short)0, cap_p * 4,
+        0x00020000);
+    for (int base = 0; base < maxw; base += 8 * 256) {   // (caps <= maxw)
+      uint32_t rw[8], id8[8], ip8[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         rw[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, (base + 256 * j + tid) * 4, 0, 0);
-        ri8[j] = __builtin_amdgcn_raw_buffer_load_b32(ri, (base + 256 * j + tid) * 4, 0, 0);
+        id8[j] = __builtin_amdgcn_raw_buffer_load_b32(rd, (base + 256 * j + tid) * 4, 0, 0);
+        ip8[j] = __builtin_amdgcn_raw_buffer_load_b32(rq, (base + 256 * j + tid) * 4, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int x = base + 256 * j + tid;
-        if (x < maxw) {
-          pages[x] = rw[j];
-          first[x] = 0x7FFFFFFF;
-        }
-        if (x < cap) item_w[x] = int32_t(ri8[j]);
+        if (x < maxw) pages[x] = rw[j];
+        if (x < cap_d) item_d[x] = int32_t(id8[j]);
+        if (x < cap_p) item_p[x] = int32_t(ip8[j]);
       }
     }
   }
-  for (int i = tid; i < words; i += blockDim.x) {
-    const int rest = nslots - 32 * i;
-    freew[i] = rest >= 32 ? 0xFFFFFFFFu : ((1u << rest) - 1u);
-  }
-  __syncthreads();
-  // occupied slots out of the free map; each window's first list position
-  for (int w = tid; w < maxw; w += blockDim.x) {
-    const uint32_t e = pages[w];
-    int sl = -1;
-    if (promote) {
-      if (pe_tier(e) == TIER_F && w < n) sl = pe_bslot(e);
-    } else if (pe_tier(e) != TIER_E && pe_has_ledger(e)) {
-      sl = pe_lslot(e);
+  // one plan over the staged row
+  auto plan = [&](int cnt, int32_t* item_w, int cap, bool promote) {
+    const int nslots = promote ? pv.nb : pv.nl;
+    const int words = (nslots + 31) / 32;
+    if (cnt < 0) cnt = 0;
+    if (cnt > cap) {
+      cnt = cap;
+      if (tid == 0) atomicOr(&s_errs, KV_ERR_ITEM_RANGE);
     }
-    if (sl >= 0 && sl < nslots) atomicAnd(&freew[sl >> 5], ~(1u << (sl & 31)));
-  }
-  for (int i = tid; i < cnt; i += blockDim.x) {
-    const int w = item_w[i];
-    if (w >= 0 && w < n) atomicMin(&first[w], i);
-  }
-  __syncthreads();
-  // free slots before each word: one wave, 64 words a pass
-  if (wv == 0) {
-    int run = 0;
-    for (int w0 = 0; w0 < words; w0 += 64) {
-      const int wd = w0 + lane;
-      const int c = wd < words ? __popc(freew[wd]) : 0;
-      int incl = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
+    for (int i = tid; i < words; i += blockDim.x) {
+      const int rest = nslots - 32 * i;
+      freew[i] = rest >= 32 ? 0xFFFFFFFFu : ((1u << rest) - 1u);
+    }
+    for (int w = tid; w < maxw; w += blockDim.x) first[w] = 0x7FFFFFFF;
+    __syncthreads();
+    // occupied slots out of the free map; each window's first list position
+    for (int w = tid; w < maxw; w += blockDim.x) {
+      const uint32_t e = pages[w];
+      int sl = -1;
+      if (promote) {
+        if (pe_tier(e) == TIER_F && w < n) sl = pe_bslot(e);
+      } else if (pe_tier(e) != TIER_E && pe_has_ledger(e)) {
+        sl = pe_lslot(e);
       }
-      if (wd < words) fpc[wd] = run + incl - c;
-      run += __shfl(incl, 63, 64);
+      if (sl >= 0 && sl < nslots) atomicAnd(&freew[sl >> 5], ~(1u << (sl & 31)));
     }
-    if (lane == 0) fpc[words] = run;
-  }
-  __syncthreads();
-  const int nfree = fpc[words];
-  // items in rounds of 256: validation against the pre-transition row, rank
-  // among the items that need a slot, slot
-  int base = 0;
-  for (int r0 = 0; r0 < cnt; r0 += 256) {
-    const int i = r0 + tid;
-    int need = 0, flag = 0, err = 0, slot = 0;
-    if (i < cnt) {
+    for (int i = tid; i < cnt; i += blockDim.x) {
       const int w = item_w[i];
-      if (w < 0 || w >= n) {
-        err = KV_ERR_ITEM_RANGE;
-      } else if (first[w] == i) {
+      if (w >= 0 && w < n) atomicMin(&first[w], i);
+    }
+    __syncthreads();
+    // free slots before each word: one wave, 64 words a pass
+    if (wv == 0) {
+      int run = 0;
+      for (int w0 = 0; w0 < words; w0 += 64) {
+        const int wd = w0 + lane;
+        const int c = wd < words ? __popc(freew[wd]) : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        if (wd < words) fpc[wd] = run + incl - c;
+        run += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) fpc[words] = run;
+    }
+    __syncthreads();
+    const int nfree = fpc[words];
+    // items in rounds of 256: validation against the row as found, rank
+    // among the items that need a slot, slot
+    int base = 0;
+    for (int r0 = 0; r0 < cnt; r0 += 256) {
+      const int i = r0 + tid;
+      int need = 0, flag = 0, err = 0, slot = 0;
+      if (i < cnt) {
+        const int w = item_w[i];
+        if (w < 0 || w >= n) {
+          err = KV_ERR_ITEM_RANGE;
+        } else if (first[w] == i) {
+          const uint32_t e = pages[w];
+          if (!promote) {
+            if (pe_tier(e) != TIER_F || (w + 1) * W > len) err = KV_ERR_DEMOTE_STATE;
+            else if (pe_has_ledger(e)) flag = 2;
+            else need = 1;
+          } else {
+            if (pe_tier(e) != TIER_Q || !pe_has_ledger(e)) err = KV_ERR_PROMOTE_STATE;
+            else need = 1;
+          }
+        }
+      }
+      const uint64_t bal = __ballot(need);
+      if (lane == 0) s_wsum[wv] = __popcll(bal);
+      __syncthreads();
+      int rank = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
+      for (int v = 0; v < wv; ++v) rank += s_wsum[v];
+      base += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+      __syncthreads();
+      if (need) {
+        if (rank < nfree) {
+          // the word holding free slot number `rank`, then that slot within it
+          int lo = 0, hi = words;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (fpc[mid] <= rank) lo = mid;
+            else hi = mid;
+          }
+          uint32_t x = freew[lo];
+          for (int k = rank - fpc[lo]; k > 0; --k) x &= x - 1u;
+          slot = 32 * lo + __builtin_ctz(x);
+          flag = 1;
+        } else {
+          err = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
+        }
+      }
+      const int kind = err == KV_ERR_ITEM_RANGE ? 1 : (err == 0 ? 0 : (need ? 3 : 2));
+      __syncthreads();   // (every thread has read its item's window above)
+      if (i < cnt)
+        item_w[i] = int32_t(uint32_t(kind == 1 ? 0 : item_w[i]) | (uint32_t(flag) << 12) |
+                            (uint32_t(kind) << 14) | (uint32_t(slot) << 16));
+    }
+    __syncthreads();
+    // the work list; first occurrences update the row, later ones take their
+    // first occurrence's state
+    const int list = promote ? 1 : 0;
+    WorkItem* work = reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + (size_t(list) * pv.B + b) * maxw;
+    const int err_state = promote ? KV_ERR_PROMOTE_STATE : KV_ERR_DEMOTE_STATE;
+    const int err_slot = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
+    int errs = 0;
+    for (int i = tid; i < cnt; i += blockDim.x) {
+      const uint32_t o = uint32_t(item_w[i]);
+      const int w = int(o & 0xFFFu), flag = int((o >> 12) & 3u), slot = int(o >> 16);
+      int kind = int((o >> 14) & 3u);
+      WorkItem it{w, -1, -1, 0};
+      if (kind != 1 && first[w] != i) {
+        // a later listing of the window: its first occurrence moved it (a
+        // state error now), or failed, and this one fails the same way
+        const uint32_t of = uint32_t(item_w[first[w]]);
+        kind = ((of >> 12) & 3u) ? 2 : int((of >> 14) & 3u);
+      } else if (flag) {
         const uint32_t e = pages[w];
         if (!promote) {
-          if (pe_tier(e) != TIER_F || (w + 1) * W > len) err = KV_ERR_DEMOTE_STATE;
-          else if (pe_has_ledger(e)) flag = 2;
-          else need = 1;
+          if (flag == 2) {
+            pages[w] = pe_make(TIER_Q, true, 0, pe_lslot(e));
+            it.flag = 2;
+          } else {
+            pages[w] = pe_make(TIER_Q, true, 0, slot);
+            it = WorkItem{w, pe_bslot(e), slot, 1};
+          }
         } else {
-          if (pe_tier(e) != TIER_Q || !pe_has_ledger(e)) err = KV_ERR_PROMOTE_STATE;
-          else need = 1;
+          pages[w] = pe_make(TIER_F, true, slot, pe_lslot(e));
+          it = WorkItem{w, pe_lslot(e), slot, 1};
         }
       }
+      errs |= kind == 1 ? KV_ERR_ITEM_RANGE : (kind == 2 ? err_state : (kind == 3 ? err_slot : 0));
+      work[i] = it;
     }
-    const uint64_t bal = __ballot(need);
-    if (lane == 0) s_wsum[wv] = __popcll(bal);
-    __syncthreads();
-    int rank = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
-    for (int v = 0; v < wv; ++v) rank += s_wsum[v];
-    base += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    __syncthreads();
-    if (need) {
-      if (rank < nfree) {
-        // the word holding free slot number `rank`, then that slot within it
-        int lo = 0, hi = words;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (fpc[mid] <= rank) lo = mid;
-          else hi = mid;
-        }
-        uint32_t x = freew[lo];
-        for (int k = rank - fpc[lo]; k > 0; --k) x &= x - 1u;
-        slot = 32 * lo + __builtin_ctz(x);
-        flag = 1;
-      } else {
-        err = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
-      }
-    }
-    const int kind = err == KV_ERR_ITEM_RANGE ? 1 : (err == 0 ? 0 : (need ? 3 : 2));
-    __syncthreads();   // (every thread has read its item's window above)
-    if (i < cnt)
-      item_w[i] = int32_t(uint32_t(kind == 1 ? 0 : item_w[i]) | (uint32_t(flag) << 12) | (uint32_t(kind) << 14) |
-                          (uint32_t(slot) << 16));
-  }
-  __syncthreads();
-  // the work list; first occurrences update the row, later ones take their
-  // first occurrence's state
-  WorkItem* work = reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + size_t(b) * maxw;
-  const int err_state = promote ? KV_ERR_PROMOTE_STATE : KV_ERR_DEMOTE_STATE;
-  const int err_slot = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
-  int errs = 0;
-  for (int i = tid; i < cnt; i += blockDim.x) {
-    const uint32_t o = uint32_t(item_w[i]);
-    const int w = int(o & 0xFFFu), flag = int((o >> 12) & 3u), slot = int(o >> 16);
-    int kind = int((o >> 14) & 3u);
-    WorkItem it{w, -1, -1, 0};
-    if (kind != 1 && first[w] != i) {
-      // a later listing of the window: its first occurrence moved it (a
-      // state error now), or failed, and this one fails the same way
-      const uint32_t of = uint32_t(item_w[first[w]]);
-      kind = ((of >> 12) & 3u) ? 2 : int((of >> 14) & 3u);
-    } else if (flag) {
-      const uint32_t e = pages[w];
-      if (!promote) {
-        if (flag == 2) {
-          pages[w] = pe_make(TIER_Q, true, 0, pe_lslot(e));
-          it.flag = 2;
-        } else {
-          pages[w] = pe_make(TIER_Q, true, 0, slot);
-          it = WorkItem{w, pe_bslot(e), slot, 1};
-        }
-      } else {
-        pages[w] = pe_make(TIER_F, true, slot, pe_lslot(e));
-        it = WorkItem{w, pe_lslot(e), slot, 1};
-      }
-    }
-    errs |= kind == 1 ? KV_ERR_ITEM_RANGE : (kind == 2 ? err_state : (kind == 3 ? err_slot : 0));
-    work[i] = it;
-  }
-  if (errs) atomicOr(&s_errs, errs);
-  __syncthreads();
-  if (tid == 0) {
-    pv.work[pv.work_counts + b] = cnt;
-    if (s_errs) set_err(pv.err, s_errs);
-  }
+    if (errs) atomicOr(&s_errs, errs);
+    if (tid == 0) pv.work[pv.work_counts + list * pv.B + b] = cnt;
+    __syncthreads();   // the row's updates are in before anything reads it again
+  };
+  if (dl.items) plan(cnt_d, item_d, cap_d, false);
+  if (pl.items) plan(cnt_p, item_p, cap_p, true);
+  if (tid == 0 && s_errs) set_err(pv.err, s_errs);
   for (int w = tid; w < maxw; w += blockDim.x) gp[w] = pages[w];
 }
 
@@ -319,7 +343,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, const
 // issued, so those loads never wait behind freshly issued stores.
 template <int D, int BITS>
 __global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolView pv, int layer,
-                                                                        const WorkItem* __restrict__ items) {
+                                                                        const WorkItem* __restrict__ items,
+                                                                        const int32_t* __restrict__ counts) {
   constexpr int KP = D + 8;    // K rows [token][channel] (bf16), padded
   constexpr int VP = 40;       // V rows [channel][token] (bf16), padded; 8 more per 32 rows
   constexpr int CWB = BITS * D / 64;          // code words per lane per part
@@ -339,7 +364,7 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolVie
   const int seg = layer * pv.B + b;
   const layout::LedgerTile LT(D, BITS);
   const WorkItem* work = items + size_t(b) * pv.maxw;   // (not written here: scalar loads)
-  const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
+  const int units = counts[b] * pv.Hkv * TPW;
   const int per_item = pv.Hkv * TPW;
   // the unit's item (flag 1: move bytes; flag 0 past the list)
   auto item_of = [&](int u) { return u < units ? work[u / per_item] : WorkItem{0, 0, 0, 0}; };
@@ -593,7 +618,8 @@ __global__ __launch_bounds__(256, D == 128 ? 4 : 3) void quantize_kernel(PoolVie
 // 2^-24 in magnitude: every term is a multiple of the fp16 quantum 2^-24),
 // and the hardware's packed bf16 conversion rounds them to nearest even.
 template <int D, int BITS>
-__global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, const WorkItem* __restrict__ items) {
+__global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, const WorkItem* __restrict__ items,
+                                                     const int32_t* __restrict__ counts) {
   constexpr int NCH = 8 * D / 256;   // 16-byte chunks per thread (K chunks first, then V)
   constexpr int NWC = BITS == 8 ? 2 : 1;   // code words per chunk
   constexpr int NBU = 4;             // units whose loads go out together (a batch)
@@ -605,7 +631,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, co
   const layout::LedgerTile LT(D, BITS);
   constexpr uint32_t kMask = (1u << BITS) - 1u;
   const WorkItem* work = items + size_t(b) * pv.maxw;   // (not written here: scalar loads)
-  const int units = pv.work[pv.work_counts + b] * pv.Hkv * TPW;
+  const int units = counts[b] * pv.Hkv * TPW;
   const int per_item = pv.Hkv * TPW;
   // the unit's code words (NWC per chunk) and, for tid < D/2, 16-byte piece
   // tid of its scale block; a unit that moves nothing loads nothing
@@ -702,18 +728,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, co
   }
 }
 
-static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t* items, int stride,
-                                    const int32_t* counts, bool promote, hipStream_t s) {
-  const int nslots = promote ? pv.nb : pv.nl;
-  const int cap = stride < pv.maxw ? stride : pv.maxw;
-  const int words = (nslots + 31) / 32, capw = cap > 0 ? cap : 0;
-  // plan LDS: row, free map and its word prefix, items, first positions
-  const size_t shm = (2 * size_t(pv.maxw) + 2 * size_t(words) + 1 + size_t(capw)) * 4;
-  hipLaunchKernelGGL(plan_kernel, dim3(pv.B), dim3(256), shm, s, pv, layer, items, stride, counts,
-                     int(promote));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (cap <= 0) return hipSuccess;
+// The data kernel of one planned list (list 0: demotions, 1: promotions) of
+// at most cap items per sequence.
+static hipError_t launch_data(const PoolView& pv, int layer, int cap, bool promote, hipStream_t s) {
   // the quantise kernel: its occupancy in workgroups per compute unit (four
   // at head_dim 128, three at 64: one round, no tail of late workgroups); the
   // dequantise kernel: four, each taking its units in batches of four (at
@@ -727,24 +744,57 @@ static hipError_t launch_transition(const PoolView& pv, int layer, const int32_t
   if (gx < 1) gx = 1;
   const int wi = pv.lbits == 2 ? 0 : (pv.lbits == 4 ? 1 : 2);
   const int di = pv.D == 64 ? 0 : 1;
-  typedef void (*Kern)(PoolView, int, const WorkItem*);
+  typedef void (*Kern)(PoolView, int, const WorkItem*, const int32_t*);
   static const Kern kDequant[2][3] = {{dequant_kernel<64, 2>, dequant_kernel<64, 4>, dequant_kernel<64, 8>},
                                       {dequant_kernel<128, 2>, dequant_kernel<128, 4>, dequant_kernel<128, 8>}};
   static const Kern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
                                     {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
+  const int list = promote ? 1 : 0;
+  const WorkItem* items = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(list) * pv.B * pv.maxw;
+  const int32_t* counts = pv.work + pv.work_counts + list * pv.B;
   hipLaunchKernelGGL(promote ? kDequant[di][wi] : kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv,
-                     layer, reinterpret_cast<const WorkItem*>(pv.work + pv.work_items));
+                     layer, items, counts);
   return hipGetLastError();
+}
+
+// Either list may be absent (items == nullptr): one plan launch for both
+// lists, then the quantise and the dequantise kernel.  The quantise kernel
+// reads every demoted window's bf16 slot before the dequantise kernel can
+// write a promoted window into it (stream order).
+hipError_t launch_transitions(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
+                              const int32_t* d_counts, const int32_t* p_items, int p_stride,
+                              const int32_t* p_counts, hipStream_t s) {
+  const int cap_d = d_items ? (d_stride < pv.maxw ? d_stride : pv.maxw) : 0;
+  const int cap_p = p_items ? (p_stride < pv.maxw ? p_stride : pv.maxw) : 0;
+  const int slots = max(d_items ? pv.nl : 0, p_items ? pv.nb : 0);
+  const int words = (slots + 31) / 32;
+  // plan LDS: row, first positions, free map and its word prefix, items
+  const size_t shm = (2 * size_t(pv.maxw) + 2 * size_t(words) + 1 + size_t(cap_d) + size_t(cap_p)) * 4;
+  if (d_items && p_items && shm > 64 * 1024) {
+    // both lists do not fit one workgroup's 64 KB (long rows and item lists,
+    // many slots): the two plans launch one after the other (each alone
+    // stays within 58 KB at the largest configuration)
+    hipError_t e = launch_transitions(pv, layer, d_items, d_stride, d_counts, nullptr, 0, nullptr, s);
+    if (e != hipSuccess) return e;
+    return launch_transitions(pv, layer, nullptr, 0, nullptr, p_items, p_stride, p_counts, s);
+  }
+  hipLaunchKernelGGL(plan_kernel, dim3(pv.B), dim3(256), shm, s, pv, layer,
+                     PlanList{d_items, d_counts, d_stride}, PlanList{p_items, p_counts, p_stride});
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (cap_d > 0 && (e = launch_data(pv, layer, cap_d, false, s)) != hipSuccess) return e;
+  if (cap_p > 0 && (e = launch_data(pv, layer, cap_p, true, s)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 hipError_t launch_demote(const PoolView& pv, int layer, const int32_t* items, int stride,
                          const int32_t* counts, hipStream_t s) {
-  return launch_transition(pv, layer, items, stride, counts, false, s);
+  return launch_transitions(pv, layer, items, stride, counts, nullptr, 0, nullptr, s);
 }
 
 hipError_t launch_promote(const PoolView& pv, int layer, const int32_t* items, int stride,
                           const int32_t* counts, hipStream_t s) {
-  return launch_transition(pv, layer, items, stride, counts, true, s);
+  return launch_transitions(pv, layer, nullptr, 0, nullptr, items, stride, counts, s);
 }
 
 // ---------------------------------------------------------------- read-back
