@@ -465,8 +465,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const uint32_t* __restrict
   // INT2 tiles, so HBM bytes (mostly bf16) and decode work (mostly INT2) are
   // spread alike over all waves - and so over all SIMDs and CUs.
   const int nwaves = S * kAttnWaves, widx = split * kAttnWaves + wid;
-  const int f_beg = widx * NF / nwaves, f_end = (widx + 1) * NF / nwaves;
   const int q_beg = widx * NQ / nwaves, q_end = (widx + 1) * NQ / nwaves;
+  // INT2 shares of k or k + 1 tiles: when the bf16 tiles fit on the waves
+  // with k, only those take them (evenly), so no wave holds both an extra
+  // INT2 tile and a bf16 tile.  Waves with k + 1 before wave x:
+  // floor(x NQ / nwaves) - k x.
+  int f_beg, f_end;
+  {
+    const int k = NQ / nwaves, n_lo = (k + 1) * nwaves - NQ;
+    if (NQ % nwaves != 0 && NF <= n_lo) {
+      const int r = widx - (q_beg - k * widx);   // rank among the k-tile waves
+      const bool lo = q_end - q_beg == k;
+      f_beg = r * NF / n_lo;
+      f_end = lo ? (r + 1) * NF / n_lo : f_beg;
+    } else {
+      f_beg = widx * NF / nwaves;
+      f_end = (widx + 1) * NF / nwaves;
+    }
+  }
   // the wave's current chunk of each list (at most kList tiles of a tier)
   const uint32_t* listf = s_tiles + f_beg;
   const uint32_t* listq = s_tiles + NF + q_beg;
