@@ -486,11 +486,26 @@ def full_step_workload(c, B, torch, dev, steps, warmup, bits=2):
     def restore():
         torch.add(saved, 0, out=pages_all)   # a copy kernel (no memset or memcpy node in the graph)
 
+    # Every layer's moves are known at the start of the step, so their plans
+    # (latency-bound single launches) run ahead on a second stream; each
+    # layer's data kernels wait only for its own plan.
+    side = torch.cuda.Stream(device=dev)
+    ev_restored = torch.cuda.Event()
+    ev_plan = [torch.cuda.Event() for _ in range(c.layers)]
+
     def step():
         restore()
+        main = torch.cuda.current_stream()
+        ev_restored.record(main)
+        side.wait_event(ev_restored)
         for layer in range(c.layers):
-            pool.transitions(layer, dem_l[layer], cnt_d, pro_l[layer], cnt_p)   # one plan launch for both
+            pool.plan_transitions(layer, dem_l[layer], cnt_d, pro_l[layer], cnt_p, stream=side)
+            ev_plan[layer].record(side)
+        for layer in range(c.layers):
+            main.wait_event(ev_plan[layer])
+            pool.move_planned(layer)
             pool.attn(layer, Q_l[layer], out=out, mass=mass, scores=True)
+        main.wait_stream(side)
 
     for _ in range(warmup):
         step()
@@ -510,7 +525,8 @@ def full_step_workload(c, B, torch, dev, steps, warmup, bits=2):
     t_timed = time.perf_counter() - t0
     assert pool.check() == 0
     # the parts of one layer's step, eagerly with stream events (two more
-    # steps: the moves as one call, then as a demote and a promote call)
+    # steps, on one stream: the moves as one call, then as a demote and a
+    # promote call)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * c.layers)]
     restore()
     for layer in range(c.layers):

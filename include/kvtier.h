@@ -110,7 +110,7 @@ typedef struct {
  *                    bits 17-31 ledger slot.
  *  KV_REGION_SCORES  float [segment][max_windows] cumulative scores.
  *  KV_REGION_TOKENS  int32 [segment] tokens cached.
- *  KV_REGION_WORK    library scratch (transition work lists and their item counts).
+ *  KV_REGION_WORK    library scratch (each layer's transition work lists and their item counts).
  *  KV_REGION_ERR     int32 device error word. */
 enum {
   KV_REGION_BF16 = 0, KV_REGION_LEDGER = 1, KV_REGION_PAGES = 2, KV_REGION_SCORES = 3,
@@ -206,6 +206,26 @@ kv_status kv_apply_transitions(kv_pool* pool, int32_t layer, const int32_t* demo
                                int32_t demote_stride, const int32_t* demote_counts,
                                const int32_t* promote_items, int32_t promote_stride,
                                const int32_t* promote_counts, void* stream);
+
+/* kv_apply_transitions in two calls, so that a caller can plan a layer's
+ * moves ahead of time, on another stream, while other layers' kernels run
+ * ("Kernmechanismen": the moves of a routing event are known before the
+ * layers are visited).  kv_plan_transitions validates both lists, assigns
+ * the slots and rewrites the layer's page table at once, exactly as
+ * kv_apply_transitions does, and leaves the layer's work lists in the pool;
+ * kv_move_planned then moves the bytes those lists name (quantise, then
+ * dequantise).  Between the two calls nothing may read or write the layer's
+ * windows (no attention, append, read-back or other move of that layer):
+ * the page table already shows the moves while the bytes are not yet there.
+ * Each layer has its own work lists, so plans of different layers can run
+ * ahead of each other's moves; a second plan of the same layer replaces the
+ * first.  Arguments and errors of kv_plan_transitions as kv_apply_transitions;
+ * kv_move_planned: KV_EINVAL for a pool without ledger slots. */
+kv_status kv_plan_transitions(kv_pool* pool, int32_t layer, const int32_t* demote_items,
+                              int32_t demote_stride, const int32_t* demote_counts,
+                              const int32_t* promote_items, int32_t promote_stride,
+                              const int32_t* promote_counts, void* stream);
+kv_status kv_move_planned(kv_pool* pool, int32_t layer, void* stream);
 
 /* Workspace bytes kv_tiered_decode_attn needs for this pool. [host] */
 size_t kv_attn_workspace_bytes(const kv_pool* pool);

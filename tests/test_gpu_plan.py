@@ -166,3 +166,82 @@ def test_one_launch_for_both_lists_matches_two_calls(n, ledger_slots, bf16_slots
             assert a.tobytes() == b.tobytes(), ("bf16", w)
     log(f"{n} windows, {bits}-bit ledger: {len(dem)} demote and {len(pro)} promote items in one call, "
         f"errors {errs[0]:#x}, {sum(1 for t in tier if t == F)} bf16 / {sum(1 for t in tier if t == Q)} ledger after")
+
+
+def test_moves_planned_ahead_on_a_second_stream_match_one_call():
+    """kv_plan_transitions for every layer on a second stream, then per layer
+    kv_move_planned and a decode step on the first (waiting only for that
+    layer's plan), against kv_apply_transitions and the same decode step per
+    layer on one stream: pages, scores, ledger entries, bf16 windows, outputs
+    and masses bit for bit (three layers, so that later plans run ahead of
+    earlier layers' moves and each layer keeps its own work lists)."""
+    from tiered_int2_fp16_amd import binding as B
+    L, Bsz, Hq, Hkv, D, W, n = 3, 2, 8, 2, 64, 64, 24
+    rng = np.random.default_rng(77)
+    kv = [rng.standard_normal((2, Bsz, Hkv, n * W, D)).astype(np.float32) for _ in range(L)]
+    kvb = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in kv]
+    prior = [rng.lognormal(0.0, 1.0, (Bsz, n)).astype(np.float32) for _ in range(L)]
+    q = [dev(((rng.standard_normal((Bsz, Hq, D)).astype(np.float32)).view(np.uint32) >> 16)
+             .astype(np.uint16).view(np.int16)) for _ in range(L)]
+    pools = []
+    for _ in range(2):
+        pool = B.Pool(B.make_config(Bsz, L, Hq, Hkv, D, W, n, 2, n, 20, 2))
+        for l in range(L):
+            pool.prefill(l, dev(kvb[l][0].view(np.int16)), dev(kvb[l][1].view(np.int16)), n * W, dev(prior[l]))
+            tr, cn = pool.score_route(l, None, 1, 0.4, 0.25)
+            pool.transitions(l, tr[0], cn[0], tr[1], cn[1])
+        pools.append(pool)
+    torch.cuda.synchronize()
+    assert pools[0].check() == 0 and pools[1].check() == 0
+    # per layer: demote half of the non-recent bf16 windows, promote the ledger
+    # windows of highest prior (repeats and a wrong-tier item included)
+    dems, pros = [], []
+    for l in range(L):
+        pg = pools[0].pages(l).cpu().numpy().view(np.uint32)[:, :n] & 3
+        d = np.zeros((Bsz, n), np.int32)
+        p = np.zeros((Bsz, n), np.int32)
+        cd, cp = np.zeros(Bsz, np.int32), np.zeros(Bsz, np.int32)
+        for b in range(Bsz):
+            f = [w for w in range(n - 2) if pg[b][w] == F][::2]
+            qq = sorted([w for w in range(n) if pg[b][w] == Q], key=lambda w: -prior[l][b][w])[:3]
+            lst_d = f + f[:1]
+            lst_p = qq + f[1:2] + qq[:1]
+            d[b, :len(lst_d)], p[b, :len(lst_p)] = lst_d, lst_p
+            cd[b], cp[b] = len(lst_d), len(lst_p)
+        dems.append((dev(d), dev(cd)))
+        pros.append((dev(p), dev(cp)))
+    outs = [[torch.empty(Bsz, Hq, D, dtype=torch.float32, device="cuda") for _ in range(L)] for _ in range(2)]
+    masses = [[torch.zeros(Bsz, Hq, n, dtype=torch.float32, device="cuda") for _ in range(L)] for _ in range(2)]
+    for l in range(L):
+        pools[0].transitions(l, dems[l][0], dems[l][1], pros[l][0], pros[l][1])
+        pools[0].attn(l, q[l], out=outs[0][l], mass=masses[0][l], scores=True)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ev0 = torch.cuda.Event()
+    ev0.record(main)
+    side.wait_event(ev0)
+    evs = []
+    for l in range(L):
+        pools[1].plan_transitions(l, dems[l][0], dems[l][1], pros[l][0], pros[l][1], stream=side)
+        evs.append(torch.cuda.Event())
+        evs[-1].record(side)
+    for l in range(L):
+        main.wait_event(evs[l])
+        pools[1].move_planned(l)
+        pools[1].attn(l, q[l], out=outs[1][l], mass=masses[1][l], scores=True)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    errs = [p.check() for p in pools]
+    assert errs[0] == errs[1] == DEMOTE_STATE | PROMOTE_STATE
+    for l in range(L):
+        assert torch.equal(outs[0][l], outs[1][l]) and torch.equal(masses[0][l], masses[1][l]), l
+        assert torch.equal(pools[0].pages(l), pools[1].pages(l)), l
+        assert torch.equal(pools[0].scores(l), pools[1].scores(l)), l
+        pg = pools[0].pages(l).cpu().numpy().view(np.uint32)[:, :n]
+        for b in range(Bsz):
+            for w in range(n):
+                if (pg[b][w] & 3) == F:
+                    assert torch.equal(pools[0].read_window(l, b, w), pools[1].read_window(l, b, w)), (l, b, w)
+                if (pg[b][w] & 3) != 0 and (pg[b][w] >> 2) & 1:
+                    assert torch.equal(pools[0].read_ledger(l, b, w), pools[1].read_ledger(l, b, w)), (l, b, w)
+    log(f"{L} layers planned ahead on a second stream: identical to one call per layer")

@@ -30,7 +30,7 @@ EXPORTS = [
     "kv_read_window", "kv_tier_counts", "kv_pool_check", "kv_last_error",
     "kv_attn_profile", "kv_attn_timings", "kv_decode_step", "kv_route_diagnostics",
     "kv_prefill_scores_workspace_bytes", "kv_prefill_scores", "kv_decode_step_noalloc",
-    "kv_apply_transitions",
+    "kv_apply_transitions", "kv_plan_transitions", "kv_move_planned",
     "kv_stream_probe",
 ]
 
@@ -66,6 +66,8 @@ def _load() -> ctypes.CDLL:
         "kv_demote_quantize": (I32, [P, I32, P, I32, P, P]),
         "kv_promote_dequantize": (I32, [P, I32, P, I32, P, P]),
         "kv_apply_transitions": (I32, [P, I32, P, I32, P, P, I32, P, P]),
+        "kv_plan_transitions": (I32, [P, I32, P, I32, P, P, I32, P, P]),
+        "kv_move_planned": (I32, [P, I32, P]),
         "kv_attn_workspace_bytes": (SZ, [P]),
         "kv_tiered_decode_attn": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
         "kv_decode_step": (I32, [P, I32, P, P, P, P, P, P, SZ, P]),
@@ -169,6 +171,15 @@ def kv_promote_dequantize(h, layer, items, counts, stream=None):
 def kv_apply_transitions(h, layer, d_items, d_counts, p_items, p_counts, stream=None):
     _ck(LIB.kv_apply_transitions(h, layer, _ptr(d_items), d_items.shape[-1], _ptr(d_counts),
                                  _ptr(p_items), p_items.shape[-1], _ptr(p_counts), _stream(stream)))
+
+
+def kv_plan_transitions(h, layer, d_items, d_counts, p_items, p_counts, stream=None):
+    _ck(LIB.kv_plan_transitions(h, layer, _ptr(d_items), d_items.shape[-1], _ptr(d_counts),
+                                _ptr(p_items), p_items.shape[-1], _ptr(p_counts), _stream(stream)))
+
+
+def kv_move_planned(h, layer, stream=None):
+    _ck(LIB.kv_move_planned(h, layer, _stream(stream)))
 
 
 def kv_attn_workspace_bytes(h) -> int:
@@ -329,6 +340,16 @@ class Pool:
         self._items(d_items, d_counts)
         self._items(p_items, p_counts)
         kv_apply_transitions(self.h, layer, d_items, d_counts, p_items, p_counts)
+
+    def plan_transitions(self, layer, d_items, d_counts, p_items, p_counts, stream=None):
+        """kv_plan_transitions on `stream` (default: the current stream)."""
+        self._items(d_items, d_counts)
+        self._items(p_items, p_counts)
+        kv_plan_transitions(self.h, layer, d_items, d_counts, p_items, p_counts, stream)
+
+    def move_planned(self, layer, stream=None):
+        """kv_move_planned on `stream` (default: the current stream)."""
+        kv_move_planned(self.h, layer, stream)
 
     def attn(self, layer, q, k_new=None, v_new=None, out=None, mass=None, want_mass=True, scores=False):
         """kv_tiered_decode_attn, or kv_decode_step when `scores` (fused score update)."""

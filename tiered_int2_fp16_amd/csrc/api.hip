@@ -285,6 +285,32 @@ kv_status kv_apply_transitions(kv_pool* pool, int32_t layer, const int32_t* demo
   return e == hipSuccess ? KV_OK : hip_fail(e, "transitions launch");
 }
 
+kv_status kv_plan_transitions(kv_pool* pool, int32_t layer, const int32_t* demote_items,
+                              int32_t demote_stride, const int32_t* demote_counts,
+                              const int32_t* promote_items, int32_t promote_stride,
+                              const int32_t* promote_counts, void* stream) {
+  kv_status st = check_pool_layer(pool, layer);
+  if (st) return st;
+  if (!demote_items || !demote_counts || !promote_items || !promote_counts)
+    return fail(KV_EINVAL, "item lists and counts must not be NULL");
+  if (demote_stride < 1 || promote_stride < 1) return fail(KV_EINVAL, "strides must be >= 1");
+  if (pool->g.cfg.ledger_slots == 0) return fail(KV_EINVAL, "pool has no ledger slots");
+  if ((st = set_device(pool))) return st;
+  hipError_t e = launch_plan(view(pool), layer, demote_items, demote_stride, demote_counts, promote_items,
+                             promote_stride, promote_counts, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV_OK : hip_fail(e, "plan launch");
+}
+
+kv_status kv_move_planned(kv_pool* pool, int32_t layer, void* stream) {
+  kv_status st = check_pool_layer(pool, layer);
+  if (st) return st;
+  if (pool->g.cfg.ledger_slots == 0) return fail(KV_EINVAL, "pool has no ledger slots");
+  if ((st = set_device(pool))) return st;
+  const int m = pool->g.cfg.max_windows;
+  hipError_t e = launch_moves(view(pool), layer, m, m, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KV_OK : hip_fail(e, "move launch");
+}
+
 size_t kv_attn_workspace_bytes(const kv_pool* pool) {
   if (!pool) return 0;
   return attn_workspace(pool->g, pool->splits).total;

@@ -52,8 +52,10 @@ bool geometry_init(const kv_pool_config& c, Geometry* g, std::string* err) {
   r.size[KV_REGION_TOKENS] = size_t(r.segments) * 4;
   // work region, in int32 units
   size_t w = 0;
-  r.work_items = w;    w += 2 * size_t(c.batch) * c.max_windows * 4;   // list 0: demotions, 1: promotions
-  r.work_counts = w;   w += 2 * size_t(c.batch);
+  // per layer, list 0: demotions, 1: promotions (a layer's moves can be
+  // planned ahead of another layer's data kernels)
+  r.work_items = w;    w += size_t(c.layers) * 2 * size_t(c.batch) * c.max_windows * 4;
+  r.work_counts = w;   w += size_t(c.layers) * 2 * size_t(c.batch);
   r.size[KV_REGION_WORK] = w * 4;
   r.size[KV_REGION_ERR] = 4;
   size_t off = 0;

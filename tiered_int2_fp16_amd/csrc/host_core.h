@@ -28,9 +28,9 @@ struct Geometry {
   size_t size[KV_REGION_COUNT]{};
   size_t total = 0;
   // KV_REGION_WORK sub-layout (int32 offsets into the region)
-  size_t work_items = 0;      // int4 [2][batch][max_windows]: window, src, dst, flag (list 0
-                              // demotions, list 1 promotions)
-  size_t work_counts = 0;     // int  [2][batch]
+  size_t work_items = 0;      // int4 [layers][2][batch][max_windows]: window, src, dst, flag
+                              // (list 0 demotions, list 1 promotions)
+  size_t work_counts = 0;     // int  [layers][2][batch]
 };
 
 // Validate `cfg` and fill `g`.  On failure returns false with a message.

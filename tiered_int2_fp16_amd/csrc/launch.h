@@ -17,6 +17,10 @@ hipError_t launch_promote(const PoolView& pv, int layer, const int32_t* items, i
 hipError_t launch_transitions(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
                               const int32_t* d_counts, const int32_t* p_items, int p_stride,
                               const int32_t* p_counts, hipStream_t s);
+hipError_t launch_plan(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
+                       const int32_t* d_counts, const int32_t* p_items, int p_stride,
+                       const int32_t* p_counts, hipStream_t s);
+hipError_t launch_moves(const PoolView& pv, int layer, int cap_d, int cap_p, hipStream_t s);
 hipError_t launch_read(const PoolView& pv, int layer, int b, int window, bool ledger, void* dst,
                        hipStream_t s);
 

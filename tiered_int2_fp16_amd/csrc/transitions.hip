@@ -12,7 +12,9 @@
 // validates the items in order, assigns the lowest free slot and rewrites the
 // page table; a data kernel then moves the bytes of every planned item.  A
 // routing event's demotions and promotions together take three: one plan
-// launch for both lists, then the two data kernels.
+// launch for both lists, then the two data kernels (a caller may also plan
+// a layer's moves ahead, on another stream, and launch its data kernels
+// later).
 #include "launch.h"
 #include "layout.h"
 
@@ -110,8 +112,8 @@ struct PlanList {
 //  - the k-th item (in list order) that needs a slot takes the k-th free
 //    slot in ascending order, and every such item from the free count on
 //    finds none (no slot is freed during a plan).
-// Each plan writes its work list (list 0: demotions, list 1: promotions) and
-// item count; the updated row is written back at the end.
+// Each plan writes its work list (list 0: demotions, list 1: promotions, of
+// this layer) and item count; the updated row is written back at the end.
 __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, PlanList dl, PlanList pl) {
   extern __shared__ uint32_t smem[];
   __shared__ int s_wsum[4];
@@ -271,7 +273,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, PlanL
     // the work list; first occurrences update the row, later ones take their
     // first occurrence's state
     const int list = promote ? 1 : 0;
-    WorkItem* work = reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + (size_t(list) * pv.B + b) * maxw;
+    WorkItem* work =
+        reinterpret_cast<WorkItem*>(pv.work + pv.work_items) + ((size_t(layer) * 2 + list) * pv.B + b) * maxw;
     const int err_state = promote ? KV_ERR_PROMOTE_STATE : KV_ERR_DEMOTE_STATE;
     const int err_slot = promote ? KV_ERR_NO_BF16_SLOT : KV_ERR_NO_LEDGER_SLOT;
     int errs = 0;
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PoolView pv, int layer, PlanL
       work[i] = it;
     }
     if (errs) atomicOr(&s_errs, errs);
-    if (tid == 0) pv.work[pv.work_counts + list * pv.B + b] = cnt;
+    if (tid == 0) pv.work[pv.work_counts + (size_t(layer) * 2 + list) * pv.B + b] = cnt;
     __syncthreads();   // the row's updates are in before anything reads it again
   };
   if (dl.items) plan(cnt_d, item_d, cap_d, false);
@@ -735,8 +738,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(PoolView pv, int layer, co
   }
 }
 
-// The data kernel of one planned list (list 0: demotions, 1: promotions) of
-// at most cap items per sequence.
+// The data kernel of one planned list of `layer` (list 0: demotions, 1:
+// promotions) of at most cap items per sequence.
 static hipError_t launch_data(const PoolView& pv, int layer, int cap, bool promote, hipStream_t s) {
   // the quantise kernel: its occupancy in workgroups per compute unit (four
   // at head_dim 128, three at 64: one round, no tail of late workgroups); the
@@ -757,20 +760,20 @@ static hipError_t launch_data(const PoolView& pv, int layer, int cap, bool promo
   static const Kern kQuant[2][3] = {{quantize_kernel<64, 2>, quantize_kernel<64, 4>, quantize_kernel<64, 8>},
                                     {quantize_kernel<128, 2>, quantize_kernel<128, 4>, quantize_kernel<128, 8>}};
   const int list = promote ? 1 : 0;
-  const WorkItem* items = reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + size_t(list) * pv.B * pv.maxw;
-  const int32_t* counts = pv.work + pv.work_counts + list * pv.B;
+  const WorkItem* items =
+      reinterpret_cast<const WorkItem*>(pv.work + pv.work_items) + (size_t(layer) * 2 + list) * pv.B * pv.maxw;
+  const int32_t* counts = pv.work + pv.work_counts + (size_t(layer) * 2 + list) * pv.B;
   hipLaunchKernelGGL(promote ? kDequant[di][wi] : kQuant[di][wi], dim3(unsigned(gx), pv.B), dim3(256), 0, s, pv,
                      layer, items, counts);
   return hipGetLastError();
 }
 
-// Either list may be absent (items == nullptr): one plan launch for both
-// lists, then the quantise and the dequantise kernel.  The quantise kernel
-// reads every demoted window's bf16 slot before the dequantise kernel can
-// write a promoted window into it (stream order).
-hipError_t launch_transitions(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
-                              const int32_t* d_counts, const int32_t* p_items, int p_stride,
-                              const int32_t* p_counts, hipStream_t s) {
+// The plan of a layer's moves: one launch for both lists (either may be
+// absent, items == nullptr).  When the two lists and the row would need more
+// than 64 KB of LDS, the two plans launch one after the other.
+hipError_t launch_plan(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
+                       const int32_t* d_counts, const int32_t* p_items, int p_stride,
+                       const int32_t* p_counts, hipStream_t s) {
   const int cap_d = d_items ? (d_stride < pv.maxw ? d_stride : pv.maxw) : 0;
   const int cap_p = p_items ? (p_stride < pv.maxw ? p_stride : pv.maxw) : 0;
   const int slots = max(d_items ? pv.nl : 0, p_items ? pv.nb : 0);
@@ -778,20 +781,35 @@ hipError_t launch_transitions(const PoolView& pv, int layer, const int32_t* d_it
   // plan LDS: row, first positions, free map and its word prefix, items
   const size_t shm = (2 * size_t(pv.maxw) + 2 * size_t(words) + 1 + size_t(cap_d) + size_t(cap_p)) * 4;
   if (d_items && p_items && shm > 64 * 1024) {
-    // both lists do not fit one workgroup's 64 KB (long rows and item lists,
-    // many slots): the two plans launch one after the other (each alone
-    // stays within 58 KB at the largest configuration)
-    hipError_t e = launch_transitions(pv, layer, d_items, d_stride, d_counts, nullptr, 0, nullptr, s);
+    // (each plan alone stays within 58 KB at the largest configuration)
+    hipError_t e = launch_plan(pv, layer, d_items, d_stride, d_counts, nullptr, 0, nullptr, s);
     if (e != hipSuccess) return e;
-    return launch_transitions(pv, layer, nullptr, 0, nullptr, p_items, p_stride, p_counts, s);
+    return launch_plan(pv, layer, nullptr, 0, nullptr, p_items, p_stride, p_counts, s);
   }
   hipLaunchKernelGGL(plan_kernel, dim3(pv.B), dim3(256), shm, s, pv, layer,
                      PlanList{d_items, d_counts, d_stride}, PlanList{p_items, p_counts, p_stride});
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+// The data kernels of the lists planned for `layer`: the quantise kernel,
+// then the dequantise kernel, which may write a promoted window into a bf16
+// slot whose demoted window the quantise kernel reads (stream order).
+// cap_d, cap_p: the lists' largest item counts (grid sizing only).
+hipError_t launch_moves(const PoolView& pv, int layer, int cap_d, int cap_p, hipStream_t s) {
+  hipError_t e;
   if (cap_d > 0 && (e = launch_data(pv, layer, cap_d, false, s)) != hipSuccess) return e;
   if (cap_p > 0 && (e = launch_data(pv, layer, cap_p, true, s)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+hipError_t launch_transitions(const PoolView& pv, int layer, const int32_t* d_items, int d_stride,
+                              const int32_t* d_counts, const int32_t* p_items, int p_stride,
+                              const int32_t* p_counts, hipStream_t s) {
+  hipError_t e = launch_plan(pv, layer, d_items, d_stride, d_counts, p_items, p_stride, p_counts, s);
+  if (e != hipSuccess) return e;
+  const int cap_d = d_items ? (d_stride < pv.maxw ? d_stride : pv.maxw) : 0;
+  const int cap_p = p_items ? (p_stride < pv.maxw ? p_stride : pv.maxw) : 0;
+  return launch_moves(pv, layer, cap_d, cap_p, s);
 }
 
 hipError_t launch_demote(const PoolView& pv, int layer, const int32_t* items, int stride,
