@@ -219,7 +219,10 @@ kv_status kv_apply_transitions(kv_pool* pool, int32_t layer, const int32_t* demo
  * the page table already shows the moves while the bytes are not yet there.
  * Each layer has its own work lists, so plans of different layers can run
  * ahead of each other's moves; a second plan of the same layer replaces the
- * first.  Arguments and errors of kv_plan_transitions as kv_apply_transitions;
+ * first.  Each plan is moved once: a second kv_move_planned of the same plan
+ * would quantise slots the first one may already have refilled (a pool's
+ * lists are empty until its first plan, so a move before any plan does
+ * nothing).  Arguments and errors of kv_plan_transitions as kv_apply_transitions;
  * kv_move_planned: KV_EINVAL for a pool without ledger slots. */
 kv_status kv_plan_transitions(kv_pool* pool, int32_t layer, const int32_t* demote_items,
                               int32_t demote_stride, const int32_t* demote_counts,
