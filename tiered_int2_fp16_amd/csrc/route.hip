@@ -96,17 +96,42 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
   uint32_t* pages = smem + 2 * kpad + maxw;                  // [maxw]
   uint8_t* newt = reinterpret_cast<uint8_t*>(smem + 2 * kpad + 2 * maxw);  // [maxw]
   __shared__ int wave_tot[16][4];
+  uint32_t* gp = pv.pages + size_t(seg) * maxw;
+  const float* gs = pv.scores + size_t(seg) * maxw;
+  // the token count, the page entries and the scores in one round of loads
+  // (none of them waits for another; entries past the row read 0)
   const int len = pv.tokens[seg];
+  constexpr int kPer = 4;   // windows per thread in the first round (1024 threads: 4096 windows)
+  uint32_t e4[kPer];
+  float s4[kPer];
+  {
+    const auto rp = __builtin_amdgcn_make_buffer_rsrc(gp, (short)0, maxw * 4, 0x00020000);
+    const auto rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(gs), (short)0, maxw * 4, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int w = tid + int(blockDim.x) * j;
+      e4[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, w * 4, 0, 0);
+      s4[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsc, w * 4, 0, 0));
+    }
+  }
   const int n = windows_of(len, pv.W);
   const int fr = n - pv.R > 0 ? n - pv.R : 0;  // first recent window
   int n_hi, n_lo;
   device_tier_counts(n, pv.R, pv.lbits, beta, phi, &n_hi, &n_lo);
   int nf = n_hi - (n - fr);
   nf = nf > 0 ? nf : 0;
-  uint32_t* gp = pv.pages + size_t(seg) * maxw;
-  const float* gs = pv.scores + size_t(seg) * maxw;
   const int fpad = (fr + 7) & ~7;
-  for (int w = tid; w < fpad; w += blockDim.x) {
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int w = tid + int(blockDim.x) * j;
+    if (w < fpad) key[w] = (w < fr && pe_tier(e4[j]) != TIER_E) ? rank_key(s4[j], w) : 0;
+    if (w < n) {
+      pages[w] = e4[j];
+      rank[w] = 0;
+    }
+  }
+  // (rows longer than kPer x 1024 windows: the rest, as before)
+  for (int w = tid + kPer * int(blockDim.x); w < fpad; w += blockDim.x) {
     uint64_t k = 0;
     if (w < fr) {
       const uint32_t e = gp[w];
@@ -114,7 +139,7 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
     }
     key[w] = k;
   }
-  for (int w = tid; w < n; w += blockDim.x) {
+  for (int w = tid + kPer * int(blockDim.x); w < n; w += blockDim.x) {
     pages[w] = gp[w];
     rank[w] = 0;
   }
