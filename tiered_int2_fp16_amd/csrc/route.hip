@@ -86,11 +86,24 @@ __device__ inline uint64_t rank_key(float score, int w) {
 
 // One workgroup per sequence: rank the eligible windows by counting, assign
 // tiers, emit the transition lists in ascending window order, apply evictions.
+// Rows with more rankable windows than this are ranked by a sort (the pair
+// counts grow with the square of the row: 1021 windows took about 25 us on
+// the one workgroup of a sequence).
+constexpr int kSortFrom = 512;
+
+// Key slots of the router's LDS: the row rounded up to 8, and to a power of
+// two for the sort of long rows.
+__host__ __device__ inline int key_slots(int maxw) {
+  int n = 8;
+  while (n < maxw) n <<= 1;
+  return maxw > kSortFrom ? n : (maxw + 7) & ~7;
+}
+
 __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, double beta, double phi,
                                                      int32_t* transitions, int32_t* counts) {
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const int b = blockIdx.x, seg = layer * pv.B + b, tid = threadIdx.x;
-  const int maxw = pv.maxw, kpad = (maxw + 7) & ~7;
+  const int maxw = pv.maxw, kpad = key_slots(maxw);
   uint64_t* key = reinterpret_cast<uint64_t*>(smem);         // [kpad] rank_key, 0 if not eligible
   int* rank = reinterpret_cast<int*>(smem + 2 * kpad);       // [maxw]
   uint32_t* pages = smem + 2 * kpad + maxw;                  // [maxw]
@@ -144,10 +157,37 @@ __global__ __launch_bounds__(1024) void route_kernel(PoolView pv, int layer, dou
     rank[w] = 0;
   }
   __syncthreads();
-  // rank[w] = number of x with key[x] > key[w] (one unsigned compare per
-  // key).  Thread jobs (w, part): each part counts one slice of x, eight keys
-  // per step.
-  {
+  // rank[w] = number of x with key[x] > key[w].  Long rows: the keys are
+  // sorted in LDS (bitonic, descending; keys are distinct but for the zeros
+  // of windows that take no part, which sort last), and a key's position is
+  // its rank.  Short rows: one unsigned compare per key pair; thread jobs (w,
+  // part), each part counting one slice of x, eight keys per step.
+  if (fr > kSortFrom) {
+    int N = 8;
+    while (N < fpad) N <<= 1;   // (N <= kpad)
+    for (int w = fpad + tid; w < N; w += blockDim.x) key[w] = 0;
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < N; i += blockDim.x) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint64_t x = key[i], y = key[ixj];
+            const bool desc = (i & k) == 0;
+            if (desc ? x < y : x > y) {
+              key[i] = y;
+              key[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int p = tid; p < N; p += blockDim.x) {
+      const uint64_t x = key[p];
+      if (x) rank[int(0xFFFFFFFFu - uint32_t(x))] = p;
+    }
+  } else {
     const int parts = fr > 0 ? max(1, min(8, int(blockDim.x) / fr)) : 1;
     const int chunk = ((fpad / 8 + parts - 1) / parts) * 8;
     for (int job = tid; job < fr * parts; job += blockDim.x) {
@@ -300,7 +340,7 @@ hipError_t launch_score_route(const PoolView& pv, int layer, const float* mass, 
     if (e != hipSuccess) return e;
   }
   if (do_route) {
-    const size_t shm = size_t((pv.maxw + 7) & ~7) * 8 + size_t(pv.maxw) * 9;
+    const size_t shm = size_t(key_slots(pv.maxw)) * 8 + size_t(pv.maxw) * 9;
     hipLaunchKernelGGL(route_kernel, dim3(pv.B), dim3(1024), shm, s, pv, layer, beta, phi, transitions,
                        counts);
     return hipGetLastError();
